@@ -1,0 +1,261 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 batch-1 decode library.
+ *
+ * The operations follow the "annotated-llm-runtime" pages:
+ *   [TS] "Building a Custom LLM Inference Runtime for Qwen2.5-Coder-7B on
+ *        NVIDIA H100 Hopper Architecture" (techsurvey.info),
+ *   [SP] "The Architecture of Modern Inference: A Deep Dive into the
+ *        Development of the Annotated LLM Runtime for NVIDIA Hopper GPUs"
+ *        (snapost.net),
+ *   [AI] "How To Build Your Own LLM Runtime From Scratch" (aissential.tech).
+ *
+ * Conventions for every call:
+ *   - No exceptions cross this boundary.  Each call returns a w4_status; on a
+ *     failure w4_last_error() (thread-local) holds a readable message.
+ *   - "device" pointers are HIP device memory (e.g. a torch CUDA tensor's
+ *     data_ptr()), owned by the caller, 16-byte aligned unless stated.
+ *     "host" pointers are ordinary CPU memory owned by the caller.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     GPU calls only enqueue work and return; they never allocate.
+ *   - fp16 values travel as uint16_t bit patterns (IEEE binary16).
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     outputs are then left untouched.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t w4_status;
+#define W4_OK       0
+#define W4_EINVAL  (-1) /* bad shape or argument                               */
+#define W4_EALIGN  (-2) /* a pointer is NULL or not 16-byte aligned            */
+#define W4_ERANGE  (-3) /* a code outside [-8, 7] or a non-finite scale        */
+#define W4_ESTATE  (-4) /* call out of sequence (position mismatch, no model)  */
+#define W4_ENOSPC  (-5) /* the KV page pool or token history is full           */
+#define W4_EHIP    (-6) /* the HIP runtime reported an error                   */
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *w4_last_error(void);
+
+/* Library build identifier (static string). */
+const char *w4_version(void);
+
+/* ------------------------------------------------------------------------
+ * Packed int4 weights  ([TS] "Technical Specifications and Hardware
+ * Alignment": symmetric group-wise INT4, group 128, one fp16 scale per
+ * group; [TS] ".nanoqwen File Format": nibbles pre-arranged for the
+ * unpacking datapath, here gfx950's 128-bit loads).
+ *
+ * Logical weights: codes q[N][K] (int8 holding values in [-8, 7]) and scales
+ * s[N][K/128] (fp16), W[n][k] = q[n][k] * s[n][k / 128].  K must be a
+ * positive multiple of 128.
+ *
+ * Packed layout (private to the kernels, documented for tests): rows are
+ * grouped in blocks of 64 (N is padded up; pad rows have code 0 and scale 0).
+ * For row block b, 32-element K chunk c and row r = 64 b + l, the 16 bytes at
+ * offset ((b * K/32 + c) * 64 + l) * 16 hold elements k = 32 c .. 32 c + 31 of
+ * packed row r as four little-endian 32-bit words; word d holds elements
+ * 32 c + 8 d + e, e = 0..7, as nibbles u = q + 8: element 2j in bits
+ * [4j, 4j+4), element 2j+1 in bits [16+4j, 16+4j+4).  Scales are stored as
+ * packed_s[(b * K/128 + g) * 64 + l] = s[row][g].
+ * Packed row r holds logical row row_perm[r] (identity when row_perm is NULL).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of packed codes / packed scales for an N x K matrix (0 if invalid). */
+size_t w4_packed_qbytes(int64_t N, int64_t K);
+size_t w4_packed_sbytes(int64_t N, int64_t K);
+
+/* Host-side packer.  q, scales, row_perm: host, read-only.  packed_q
+ * (w4_packed_qbytes bytes) and packed_s (w4_packed_sbytes bytes): host,
+ * written.  group must be 128.  row_perm, if not NULL, is a permutation of
+ * [0, N).  Errors: W4_EINVAL (shape, group, bad permutation), W4_ERANGE (a
+ * code outside [-8, 7] or a non-finite scale), W4_EALIGN (NULL pointer). */
+w4_status pack_int4_weights(const int8_t *q, const uint16_t *scales, int64_t N,
+                            int64_t K, int32_t group, const int32_t *row_perm,
+                            uint8_t *packed_q, uint16_t *packed_s);
+
+/* Exact inverse of pack_int4_weights (same arguments, data flowing back). */
+w4_status unpack_int4_weights(const uint8_t *packed_q, const uint16_t *packed_s,
+                              int64_t N, int64_t K, int32_t group,
+                              const int32_t *row_perm, int8_t *q,
+                              uint16_t *scales);
+
+/* fp16 matrices (the lm_head, [TS] "Technical Specifications…": kept in raw
+ * fp16).  Same row blocks of 64; the 16 bytes at ((b * K/8 + c) * 64 + l) * 16
+ * hold elements 8c .. 8c+7 of row 64 b + l.  K must be a multiple of 8. */
+size_t w4_packed_f16_bytes(int64_t N, int64_t K);
+w4_status w4_pack_f16_matrix(const uint16_t *w, int64_t N, int64_t K,
+                             uint16_t *packed);
+
+/* ------------------------------------------------------------------------
+ * W4A16 GEMV  ([TS] "Engineering Challenges" item 3, the fp16-activation
+ * path: int4 weights unpacked on the fly, fp16 activations, no activation
+ * quantisation).  y[r] = fp16( sum_k W[r][k] * x[k] ) for packed rows
+ * r < N, accumulated in fp32 within a group and fp64 across groups.
+ *
+ *   packed_q, packed_s : device, from pack_int4_weights (any row_perm; y is
+ *                        in packed row order)
+ *   x                  : device, fp16 [K]
+ *   y                  : device, fp16 [N] (written)
+ *   workspace          : device, w4_gemv_ws_bytes(N, K) bytes of scratch
+ *                        (split-K partials and arrival counters); no
+ *                        initialisation needed, the call clears its counters
+ *                        first.  Calls that share a workspace must be ordered
+ *                        on one stream.
+ * Errors: W4_EINVAL (N < 1, K not a positive multiple of 128, workspace too
+ * small), W4_EALIGN, W4_EHIP (launch failure). */
+size_t w4_gemv_ws_bytes(int64_t N, int64_t K);
+w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_s,
+                     const uint16_t *x, uint16_t *y, int64_t N, int64_t K,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* The MLP decode block of one token on the same kernels the decode step
+ * uses: the fused gate+up GEMV with its SwiGLU epilogue, then the down GEMV
+ * (SwiGLU MLP of the Qwen2.5-7B decode workload; int4 projections as above).
+ *   h = fp16( silu(Wg x) * (Wu x) ),   y = fp16( Wd h )
+ *   gu_q, gu_s     : device, the [gate ; up] matrix (2F rows, K = D) packed
+ *                    with the W4_PERM_GATE_UP row order (see below)
+ *   down_q, down_s : device, Wd (D rows, K = F) packed in identity order
+ *   x              : device, fp16 [D];  h : fp16 [F] and y : fp16 [D] (written)
+ *   workspace      : device, w4_mlp_ws_bytes(D, F) bytes of scratch (as for
+ *                    w4a16_gemv)
+ * D and F must be positive multiples of 128.  Errors as for w4a16_gemv. */
+size_t w4_mlp_ws_bytes(int64_t D, int64_t F);
+w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *down_q,
+                    const uint16_t *down_s, const uint16_t *x, uint16_t *h, uint16_t *y,
+                    int64_t D, int64_t F, void *workspace, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention  ([TS] "Technical Specifications…": 16-token pages,
+ * one kv-head slice of a page is 4 KiB; [SP] "Three Critical Engineering
+ * Challenges" item 1: softmax and weighted-V accumulation over KV pages).
+ *
+ * out[h] = sum_t softmax_t(scale * q[h] . K[t, h / (n_qh/n_kvh)]) V[t, ...]
+ * over the ctx_len cached tokens t; token t lives in physical page
+ * page_table[t / 16], slot t % 16.
+ *
+ *   q           : device, fp16 [n_qh][head_dim]
+ *   k_pool,
+ *   v_pool      : device, fp16 [n_phys][n_kvh][16][head_dim]
+ *   page_table  : device, int32 [n_pages_max]; entries are trusted to be
+ *                 valid physical pages of the pools
+ *   out         : device, fp16 [n_qh][head_dim] (written)
+ *   workspace   : device, w4_attn_ws_bytes(n_qh, n_kvh, n_pages_max) bytes of
+ *                 scratch (per-split partials and arrival counters); no
+ *                 initialisation needed; calls sharing it must be ordered
+ * head_dim must be 128; n_qh a multiple of n_kvh with n_qh / n_kvh in
+ * {1, 2, 4, 7, 8}; 1 <= ctx_len <= 16 * n_pages_max.  Otherwise W4_EINVAL. */
+size_t w4_attn_ws_bytes(int32_t n_qh, int32_t n_kvh, int32_t n_pages_max);
+w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool,
+                            const uint16_t *v_pool, const int32_t *page_table,
+                            int32_t ctx_len, int32_t n_qh, int32_t n_kvh,
+                            int32_t head_dim, int32_t n_pages_max, float scale,
+                            uint16_t *out, void *workspace, size_t ws_bytes,
+                            void *stream);
+
+/* ------------------------------------------------------------------------
+ * Decoder model and the graph-captured decode step
+ * ([TS] "Engineering Challenges" item 2 and [SP] "Eliminating Host Overhead
+ * with CUDA Graphs": the whole step captured once, in a page-boundary and a
+ * no-boundary variant picked per step by position modulo 16; [SP]
+ * ".nanoqwen Format": no allocation while generating).
+ * ------------------------------------------------------------------------ */
+
+typedef struct w4_model w4_model;
+
+typedef struct {
+    int32_t d_model;     /* hidden size, multiple of 128                   */
+    int32_t d_ff;        /* MLP size, multiple of 128                      */
+    int32_t n_layers;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;  /* n_q_heads / n_kv_heads in {1, 2, 4, 7, 8}      */
+    int32_t head_dim;    /* must be 128                                    */
+    int32_t vocab;
+    int32_t max_pages;   /* KV pool pages per layer; positions < 16*max_pages */
+    float eps;           /* RMSNorm epsilon                                */
+    double theta;        /* RoPE base                                      */
+} w4_model_config;
+
+/* Row orders the model expects its packed projections in (pass the result
+ * as row_perm to pack_int4_weights):
+ *   W4_PERM_QKV     : N = (n_q_heads + 2 n_kv_heads) * head_dim rows of the
+ *                     [q heads | k heads | v heads] matrix; within each head
+ *                     packed row 2i holds dim i and 2i+1 holds dim i + 64, so
+ *                     the two halves of a rotary pair sit in adjacent lanes.
+ *   W4_PERM_GATE_UP : N = 2 d_ff rows of [gate ; up]; packed row 2i holds
+ *                     gate row i and 2i+1 holds up row i. */
+#define W4_PERM_QKV     0
+#define W4_PERM_GATE_UP 1
+w4_status w4_model_row_perm(int32_t kind, const w4_model_config *cfg,
+                            int32_t *perm /* host, N entries */);
+
+/* Device buffers of a model; all caller-owned and outliving the model.
+ * Per-layer entries are host arrays of n_layers device pointers. */
+typedef struct {
+    const uint8_t *const *qkv_q;      /* packed, W4_PERM_QKV order          */
+    const uint16_t *const *qkv_s;
+    const uint16_t *const *qkv_bias;  /* fp16 [qkv rows], logical order     */
+    const uint8_t *const *o_q;        /* packed, identity order             */
+    const uint16_t *const *o_s;
+    const uint8_t *const *gu_q;       /* packed, W4_PERM_GATE_UP order      */
+    const uint16_t *const *gu_s;
+    const uint8_t *const *down_q;     /* packed, identity order             */
+    const uint16_t *const *down_s;
+    const uint16_t *const *ln1;       /* fp16 [d_model]                     */
+    const uint16_t *const *ln2;       /* fp16 [d_model]                     */
+    const uint16_t *embed;            /* fp16 [vocab][d_model], row-major   */
+    const uint16_t *lnf;              /* fp16 [d_model]                     */
+    const uint16_t *lm_head;          /* w4_pack_f16_matrix of [vocab][d]   */
+    uint16_t *k_cache;                /* fp16 [n_layers][max_pages][n_kv][16][128] */
+    uint16_t *v_cache;                /* same shape                         */
+    int32_t *page_table;              /* int32 [max_pages], written by steps */
+    const int32_t *free_list;         /* int32 [max_pages]: physical page for
+                                         each successive logical page       */
+    int32_t *tokens;                  /* int32 [16*max_pages + 1]: prompt in
+                                         [0, n_prompt), generated after     */
+    float *logits;                    /* fp32 [vocab], last step's logits   */
+} w4_model_buffers;
+
+/* Creates a model: validates cfg and buffers, allocates the library's own
+ * workspace (activations, split-K partials, counters, RoPE table) and
+ * captures the two step graphs.  This is the only call that allocates. */
+w4_status w4_model_create(const w4_model_config *cfg,
+                          const w4_model_buffers *buf, w4_model **out);
+void w4_model_destroy(w4_model *m);
+
+/* Starts a sequence: position 0, the first n_prompt entries of tokens are
+ * the prompt (teacher-forced).  Enqueued on stream. */
+w4_status w4_model_reset(w4_model *m, int32_t n_prompt, void *stream);
+
+/* Current host-side position of the model (next position decode_step takes). */
+int32_t w4_model_pos(const w4_model *m);
+
+/* One decode step at position pos (must equal the model's position):
+ * embeds tokens[pos], runs every layer (RMSNorm, QKV GEMV + bias + RoPE +
+ * KV append, paged attention, O GEMV + residual, RMSNorm, gate/up GEMV +
+ * SwiGLU, down GEMV + residual), the final norm and the fp16 lm_head, writes
+ * logits, and stores the greedy token (lowest index of the maximum) into
+ * tokens[pos+1] unless pos+1 < n_prompt.  When pos % 16 == 0 the step first
+ * appends free_list[pos/16] to the page table.
+ * flags: W4_GRAPH replays the captured graph of the matching variant;
+ * W4_EAGER launches the same kernels one by one.
+ * Errors: W4_ESTATE (pos mismatch), W4_ENOSPC (pos >= 16*max_pages),
+ * W4_EHIP. */
+#define W4_GRAPH 0u
+#define W4_EAGER 1u
+w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream);
+
+/* Number of kernel launches one eager step makes (for the launch-count report). */
+int32_t w4_model_launches_per_step(const w4_model *m);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,602 @@
+// gfx950 W4A16 batch-1 decode library: kernel entry points, glue kernels and
+// the graph-captured decode step.  One translation unit holds every kernel so
+// each template instantiation is registered exactly once.
+#include <math.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string.h>
+
+#include <vector>
+
+#include "w4_attn.hpp"
+#include "w4_gemv.hpp"
+
+namespace w4 {
+
+// ------------------------------------------------------------ glue kernels --
+
+struct StepState {
+    int pos;                 // position the running step works on
+    int n_prompt;            // tokens [0, n_prompt) are teacher-forced
+    unsigned long long best; // argmax key of the step's logits
+};
+
+// x = embed[tokens[pos]] as fp64; clears the argmax key.
+__global__ __launch_bounds__(kThreads) void embed_kernel(const uint16_t *embed, const int *tokens,
+                                                         StepState *st, double *x, int d) {
+    const int tok = tokens[st->pos];
+    const uint16_t *row = embed + static_cast<size_t>(tok) * d;
+    for (int i = threadIdx.x; i < d; i += kThreads) x[i] = static_cast<double>(f16_to_f32(row[i]));
+    if (threadIdx.x == 0) st->best = 0ull;
+}
+
+// a = fp16(x / sqrt(mean(x^2) + eps) * w), computed in fp64 with one rounding.
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const double *x, const uint16_t *w, uint16_t *a,
+                                                       int d, double eps) {
+    __shared__ double red[1024 / 64];
+    double ss = 0.0;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) ss += x[i] * x[i];
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    const int nw = blockDim.x >> 6;
+    for (int i = 0; i < nw; ++i) tot += red[i];
+    const double r = sqrt(tot / d + eps);
+    for (int i = threadIdx.x; i < d; i += blockDim.x)
+        a[i] = f64_to_f16(x[i] / r * static_cast<double>(f16_to_f32(w[i])));
+}
+
+// Boundary-variant first node: the page of the position is appended.
+__global__ void page_append_kernel(StepState *st, int *page_table, const int *free_list) {
+    const int lp = st->pos >> 4;
+    page_table[lp] = free_list[lp];
+}
+
+// Last node: greedy token, history update, position advance.
+__global__ void finalize_kernel(StepState *st, int *tokens) {
+    const int pos = st->pos;
+    const unsigned long long key = st->best;
+    const int tok = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFull));
+    if (pos + 1 >= st->n_prompt) tokens[pos + 1] = tok;
+    st->pos = pos + 1;
+}
+
+// Clears the counter region of a caller-provided workspace at the start of
+// a standalone call: a workspace may be reused across shapes, and a previous
+// call's partials can occupy this call's counter slots.
+__global__ void zero_u32_kernel(unsigned *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+static hipError_t zero_counters(void *ws, int n, hipStream_t s) {
+    const int blocks = std::min((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, s, static_cast<unsigned *>(ws), n);
+    return hipGetLastError();
+}
+
+__global__ void reset_kernel(StepState *st, int n_prompt) {
+    st->pos = 0;
+    st->n_prompt = n_prompt;
+    st->best = 0ull;
+}
+
+// -------------------------------------------------------------- launchers --
+
+template <class Epi>
+static hipError_t launch_w4(const W4Problem &p, const Epi &epi, hipStream_t s) {
+    hipLaunchKernelGGL(w4_gemv_kernel<Epi>, dim3(p.n_rb * p.n_split), dim3(kThreads), 0, s, p, epi);
+    return hipGetLastError();
+}
+
+static hipError_t launch_attn(int G, const AttnProblem &a, hipStream_t s) {
+    const dim3 grid(a.n_kvh * a.n_split), block(kThreads);
+    switch (G) {
+        case 1: hipLaunchKernelGGL(attn_decode_kernel<1>, grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(attn_decode_kernel<2>, grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL(attn_decode_kernel<4>, grid, block, 0, s, a); break;
+        case 7: hipLaunchKernelGGL(attn_decode_kernel<7>, grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL(attn_decode_kernel<8>, grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+static bool gqa_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 7 || g == 8; }
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Workspace of split-K GEMVs that run one after another: a counter region
+// of ctr_rb slots (the largest row-block count among them), then fp64
+// partials.  A fixed counter region keeps every GEMV's counters away from any
+// other GEMV's partials.
+static size_t gemv_ws_bytes(int ctr_rb, size_t max_partials) {
+    return align256(static_cast<size_t>(ctr_rb) * 4) + max_partials * 8;
+}
+
+static void gemv_ws_carve(void *ws, int ctr_rb, W4Problem &p) {
+    p.counter = static_cast<unsigned *>(ws);
+    p.partial = reinterpret_cast<double *>(static_cast<char *>(ws) + align256(static_cast<size_t>(ctr_rb) * 4));
+}
+
+static size_t gemv_partials(int n_rb, int n_split) {
+    return n_split > 1 ? static_cast<size_t>(n_split) * n_rb * 64 : 0;
+}
+
+static size_t attn_ws_bytes(int n_kvh, int G, int n_split) {
+    return align256(static_cast<size_t>(n_kvh) * 4) +
+           align256(static_cast<size_t>(n_kvh) * n_split * G * 2 * 4) +
+           static_cast<size_t>(n_kvh) * n_split * G * 128 * 4;
+}
+
+static void attn_ws_carve(void *ws, int n_kvh, int G, int n_split, AttnProblem &a) {
+    char *b = static_cast<char *>(ws);
+    a.counter = reinterpret_cast<unsigned *>(b);
+    b += align256(static_cast<size_t>(n_kvh) * 4);
+    a.part_ml = reinterpret_cast<float *>(b);
+    b += align256(static_cast<size_t>(n_kvh) * n_split * G * 2 * 4);
+    a.part_acc = reinterpret_cast<float *>(b);
+}
+
+}  // namespace w4
+
+using namespace w4;
+
+// ============================================================ kernel calls ==
+
+extern "C" size_t w4_gemv_ws_bytes(int64_t N, int64_t K) {
+    if (N < 1 || K < kGroup || K % kGroup) return 0;
+    const int n_rb = static_cast<int>((N + 63) / 64);
+    return gemv_ws_bytes(n_rb, gemv_partials(n_rb, gemv_split(n_rb, static_cast<int>(K / kGroup))));
+}
+
+extern "C" w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_s, const uint16_t *x,
+                                uint16_t *y, int64_t N, int64_t K, void *workspace, size_t ws_bytes,
+                                void *stream) {
+    clear_error();
+    W4_CHECK(N >= 1 && N <= (int64_t(1) << 31) - 64, W4_EINVAL, "bad N=%lld", (long long)N);
+    W4_CHECK(K >= kGroup && K % kGroup == 0 && K <= (int64_t(1) << 24), W4_EINVAL,
+             "K=%lld must be a positive multiple of 128", (long long)K);
+    W4_CHECK(aligned16(packed_q) && aligned16(packed_s) && aligned16(x), W4_EALIGN,
+             "packed_q, packed_s and x must be 16-byte aligned device pointers");
+    W4_CHECK(y != nullptr && (reinterpret_cast<uintptr_t>(y) & 1) == 0, W4_EALIGN, "bad y pointer");
+    const int n_rb = static_cast<int>((N + 63) / 64);
+    const int n_groups = static_cast<int>(K / kGroup);
+    const int n_split = gemv_split(n_rb, n_groups);
+    const size_t need = gemv_ws_bytes(n_rb, gemv_partials(n_rb, n_split));
+    W4_CHECK(ws_bytes >= need && aligned16(workspace), W4_EINVAL,
+             "workspace of %zu bytes given (16-byte aligned), %zu needed", ws_bytes, need);
+    W4Problem p;
+    p.wq = reinterpret_cast<const u32x4 *>(packed_q);
+    p.ws = packed_s;
+    p.x = reinterpret_cast<const uint32_t *>(x);
+    p.n_groups = n_groups;
+    p.n_rb = n_rb;
+    p.n_split = n_split;
+    gemv_ws_carve(workspace, n_rb, p);
+    if (n_split > 1) W4_HIP(zero_counters(workspace, n_rb, static_cast<hipStream_t>(stream)));
+    W4_HIP(launch_w4(p, EpiStoreF16{y, static_cast<int>(N)}, static_cast<hipStream_t>(stream)));
+    return W4_OK;
+}
+
+static void mlp_geometry(int64_t D, int64_t F, int &rb_gu, int &sp_gu, int &rb_dn, int &sp_dn, int &ctr,
+                         size_t &parts) {
+    rb_gu = static_cast<int>((2 * F + 63) / 64);
+    sp_gu = gemv_split(rb_gu, static_cast<int>(D / kGroup));
+    rb_dn = static_cast<int>((D + 63) / 64);
+    sp_dn = gemv_split(rb_dn, static_cast<int>(F / kGroup));
+    ctr = std::max(rb_gu, rb_dn);
+    parts = std::max(gemv_partials(rb_gu, sp_gu), gemv_partials(rb_dn, sp_dn));
+}
+
+extern "C" size_t w4_mlp_ws_bytes(int64_t D, int64_t F) {
+    if (D < kGroup || D % kGroup || F < kGroup || F % kGroup) return 0;
+    int rb_gu, sp_gu, rb_dn, sp_dn, ctr;
+    size_t parts;
+    mlp_geometry(D, F, rb_gu, sp_gu, rb_dn, sp_dn, ctr, parts);
+    return gemv_ws_bytes(ctr, parts);
+}
+
+extern "C" w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *down_q,
+                               const uint16_t *down_s, const uint16_t *x, uint16_t *h, uint16_t *y, int64_t D,
+                               int64_t F, void *workspace, size_t ws_bytes, void *stream) {
+    clear_error();
+    W4_CHECK(D >= kGroup && D % kGroup == 0 && F >= kGroup && F % kGroup == 0 && D <= (1 << 24) && F <= (1 << 24),
+             W4_EINVAL, "D=%lld and F=%lld must be positive multiples of 128", (long long)D, (long long)F);
+    W4_CHECK(aligned16(gu_q) && aligned16(gu_s) && aligned16(down_q) && aligned16(down_s) && aligned16(x) &&
+                 aligned16(h) && aligned16(workspace) && y != nullptr,
+             W4_EALIGN, "weights, x, h and workspace must be 16-byte aligned device pointers");
+    int rb_gu, sp_gu, rb_dn, sp_dn, ctr;
+    size_t parts;
+    mlp_geometry(D, F, rb_gu, sp_gu, rb_dn, sp_dn, ctr, parts);
+    const size_t need = gemv_ws_bytes(ctr, parts);
+    W4_CHECK(ws_bytes >= need, W4_EINVAL, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    W4Problem p;
+    p.wq = reinterpret_cast<const u32x4 *>(gu_q);
+    p.ws = gu_s;
+    p.x = reinterpret_cast<const uint32_t *>(x);
+    p.n_groups = static_cast<int>(D / kGroup);
+    p.n_rb = rb_gu;
+    p.n_split = sp_gu;
+    gemv_ws_carve(workspace, ctr, p);
+    W4_HIP(zero_counters(workspace, ctr, s));
+    W4_HIP(launch_w4(p, EpiSwiGLU{h, static_cast<int>(F)}, s));
+    p.wq = reinterpret_cast<const u32x4 *>(down_q);
+    p.ws = down_s;
+    p.x = reinterpret_cast<const uint32_t *>(h);
+    p.n_groups = static_cast<int>(F / kGroup);
+    p.n_rb = rb_dn;
+    p.n_split = sp_dn;
+    W4_HIP(launch_w4(p, EpiStoreF16{y, static_cast<int>(D)}, s));
+    return W4_OK;
+}
+
+extern "C" size_t w4_attn_ws_bytes(int32_t n_qh, int32_t n_kvh, int32_t n_pages_max) {
+    if (n_kvh < 1 || n_qh < 1 || n_qh % n_kvh || n_pages_max < 1) return 0;
+    return attn_ws_bytes(n_kvh, n_qh / n_kvh, attn_n_split(n_pages_max));
+}
+
+extern "C" w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                       const int32_t *page_table, int32_t ctx_len, int32_t n_qh,
+                                       int32_t n_kvh, int32_t head_dim, int32_t n_pages_max, float scale,
+                                       uint16_t *out, void *workspace, size_t ws_bytes, void *stream) {
+    clear_error();
+    W4_CHECK(head_dim == kHeadDim, W4_EINVAL, "head_dim must be 128 (got %d)", head_dim);
+    W4_CHECK(n_kvh >= 1 && n_qh >= 1 && n_qh % n_kvh == 0 && gqa_supported(n_qh / n_kvh), W4_EINVAL,
+             "n_qh=%d / n_kvh=%d must be one of 1, 2, 4, 7, 8", n_qh, n_kvh);
+    W4_CHECK(n_pages_max >= 1 && ctx_len >= 1 && static_cast<int64_t>(ctx_len) <= int64_t(kPage) * n_pages_max,
+             W4_EINVAL, "ctx_len=%d outside [1, 16*n_pages_max=%lld]", ctx_len,
+             (long long)(int64_t(kPage) * n_pages_max));
+    W4_CHECK(std::isfinite(scale), W4_EINVAL, "scale must be finite");
+    W4_CHECK(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(out) && aligned16(workspace) &&
+                 page_table != nullptr,
+             W4_EALIGN, "q, pools, out and workspace must be 16-byte aligned device pointers");
+    const int G = n_qh / n_kvh;
+    const int n_split = attn_n_split(n_pages_max);
+    const size_t need = attn_ws_bytes(n_kvh, G, n_split);
+    W4_CHECK(ws_bytes >= need, W4_EINVAL, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    AttnProblem a;
+    a.q = q;
+    a.kpool = k_pool;
+    a.vpool = v_pool;
+    a.page_table = page_table;
+    a.pos_ptr = nullptr;
+    a.ctx = ctx_len;
+    a.n_kvh = n_kvh;
+    a.pages_per_split = attn_pages_per_split(n_pages_max);
+    a.n_split = n_split;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out = out;
+    attn_ws_carve(workspace, n_kvh, G, n_split, a);
+    W4_HIP(zero_counters(workspace, n_kvh, static_cast<hipStream_t>(stream)));
+    W4_HIP(launch_attn(G, a, static_cast<hipStream_t>(stream)));
+    return W4_OK;
+}
+
+// ================================================================== model ==
+
+struct w4_model {
+    w4_model_config cfg;
+    std::vector<const uint8_t *> qkv_q, o_q, gu_q, down_q;
+    std::vector<const uint16_t *> qkv_s, qkv_bias, o_s, gu_s, down_s, ln1, ln2;
+    const uint16_t *embed, *lnf, *lm_head;
+    uint16_t *k_cache, *v_cache;
+    int32_t *page_table, *tokens;
+    const int32_t *free_list;
+    float *logits;
+
+    // library-owned device memory (one allocation, carved)
+    void *arena;
+    StepState *state;
+    double *x;          // residual [d]
+    uint16_t *a;        // normed input [d]
+    uint16_t *qbuf;     // q after RoPE [n_qh*128]
+    uint16_t *o;        // attention output [n_qh*128]
+    uint16_t *h;        // SwiGLU output [d_ff]
+    double *rope;       // [max_pos][64][2]
+    void *gemv_ws;      // shared by the GEMVs of a step (stream-ordered)
+    void *attn_ws;
+    size_t gemv_ws_size;
+
+    // per-GEMV launch geometry
+    int rb_qkv, sp_qkv, rb_o, sp_o, rb_gu, sp_gu, rb_down, sp_down, rb_head;
+    int ctr_rb;               // counter slots at the start of gemv_ws
+    int attn_pps, attn_split;
+
+    hipStream_t cap_stream;
+    hipGraphExec_t exec[2];   // [0] no page boundary, [1] page boundary
+    int pos;                  // host mirror of the device position
+    int n_prompt;
+    int launches;
+};
+
+namespace w4 {
+
+static size_t layer_kv_elems(const w4_model *m) {
+    return static_cast<size_t>(m->cfg.max_pages) * m->cfg.n_kv_heads * kPage * kHeadDim;
+}
+
+static W4Problem w4_problem(const w4_model *m, const uint8_t *q, const uint16_t *s, const uint16_t *x,
+                            int n_rb, int n_split, int K) {
+    W4Problem p;
+    p.wq = reinterpret_cast<const u32x4 *>(q);
+    p.ws = s;
+    p.x = reinterpret_cast<const uint32_t *>(x);
+    p.n_groups = K / kGroup;
+    p.n_rb = n_rb;
+    p.n_split = n_split;
+    gemv_ws_carve(m->gemv_ws, m->ctr_rb, p);
+    return p;
+}
+
+// Enqueues one whole decode step (boundary: with the page append first).
+static hipError_t enqueue_step(w4_model *m, bool boundary, hipStream_t s) {
+    const w4_model_config &c = m->cfg;
+    const int d = c.d_model, f = c.d_ff, qd = c.n_q_heads * kHeadDim;
+    const int G = c.n_q_heads / c.n_kv_heads;
+    const int *pos_ptr = &m->state->pos;
+    int launches = 0;
+    hipError_t e;
+#define W4_Q(call)                          \
+    do {                                    \
+        e = (call);                         \
+        if (e != hipSuccess) return e;      \
+        ++launches;                         \
+    } while (0)
+    if (boundary) {
+        hipLaunchKernelGGL(page_append_kernel, dim3(1), dim3(1), 0, s, m->state, m->page_table, m->free_list);
+        W4_Q(hipGetLastError());
+    }
+    hipLaunchKernelGGL(embed_kernel, dim3(1), dim3(kThreads), 0, s, m->embed, m->tokens, m->state, m->x, d);
+    W4_Q(hipGetLastError());
+    for (int l = 0; l < c.n_layers; ++l) {
+        uint16_t *kc = m->k_cache + l * layer_kv_elems(m);
+        uint16_t *vc = m->v_cache + l * layer_kv_elems(m);
+        hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, s, m->x, m->ln1[l], m->a, d, double(c.eps));
+        W4_Q(hipGetLastError());
+        EpiQKV eq{m->qkv_bias[l], m->rope, pos_ptr, m->page_table, m->qbuf, kc, vc, c.n_q_heads, c.n_kv_heads};
+        W4_Q(launch_w4(w4_problem(m, m->qkv_q[l], m->qkv_s[l], m->a, m->rb_qkv, m->sp_qkv, d), eq, s));
+        AttnProblem a;
+        a.q = m->qbuf;
+        a.kpool = kc;
+        a.vpool = vc;
+        a.page_table = m->page_table;
+        a.pos_ptr = pos_ptr;
+        a.ctx = 0;
+        a.n_kvh = c.n_kv_heads;
+        a.pages_per_split = m->attn_pps;
+        a.n_split = m->attn_split;
+        a.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(double(kHeadDim)));
+        a.out = m->o;
+        attn_ws_carve(m->attn_ws, c.n_kv_heads, G, m->attn_split, a);
+        W4_Q(launch_attn(G, a, s));
+        W4_Q(launch_w4(w4_problem(m, m->o_q[l], m->o_s[l], m->o, m->rb_o, m->sp_o, qd), EpiResidual{m->x, d}, s));
+        hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, s, m->x, m->ln2[l], m->a, d, double(c.eps));
+        W4_Q(hipGetLastError());
+        W4_Q(launch_w4(w4_problem(m, m->gu_q[l], m->gu_s[l], m->a, m->rb_gu, m->sp_gu, d), EpiSwiGLU{m->h, f}, s));
+        W4_Q(launch_w4(w4_problem(m, m->down_q[l], m->down_s[l], m->h, m->rb_down, m->sp_down, f),
+                       EpiResidual{m->x, d}, s));
+    }
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, s, m->x, m->lnf, m->a, d, double(c.eps));
+    W4_Q(hipGetLastError());
+    F16Problem hp;
+    hp.w = reinterpret_cast<const u32x4 *>(m->lm_head);
+    hp.x = reinterpret_cast<const uint32_t *>(m->a);
+    hp.n_chunks = d / 8;
+    hp.n_rb = m->rb_head;
+    hp.n = c.vocab;
+    hp.out = m->logits;
+    hp.best = &m->state->best;
+    hipLaunchKernelGGL(f16_gemv_kernel, dim3(m->rb_head), dim3(kThreads), 0, s, hp);
+    W4_Q(hipGetLastError());
+    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, s, m->state, m->tokens);
+    W4_Q(hipGetLastError());
+#undef W4_Q
+    m->launches = launches - (boundary ? 1 : 0);
+    return hipSuccess;
+}
+
+static w4_status capture(w4_model *m, bool boundary, hipGraphExec_t *out) {
+    hipGraph_t g = nullptr;
+    W4_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
+    hipError_t e = enqueue_step(m, boundary, m->cap_stream);
+    hipError_t e2 = hipStreamEndCapture(m->cap_stream, &g);
+    if (e != hipSuccess || e2 != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return fail(W4_EHIP, "step capture failed: %s", hipGetErrorString(e != hipSuccess ? e : e2));
+    }
+    e = hipGraphInstantiate(out, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    W4_HIP(e);
+    return W4_OK;
+}
+
+static void model_free(w4_model *m) {
+    if (!m) return;
+    for (int i = 0; i < 2; ++i)
+        if (m->exec[i]) (void)hipGraphExecDestroy(m->exec[i]);
+    if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+    if (m->arena) (void)hipFree(m->arena);
+    delete m;
+}
+
+}  // namespace w4
+
+extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_buffers *buf, w4_model **out) {
+    clear_error();
+    W4_CHECK(cfg && buf && out, W4_EALIGN, "NULL argument");
+    *out = nullptr;
+    const w4_model_config &c = *cfg;
+    W4_CHECK(c.head_dim == kHeadDim, W4_EINVAL, "head_dim must be 128");
+    W4_CHECK(c.n_layers >= 1 && c.n_kv_heads >= 1 && c.n_q_heads >= c.n_kv_heads && c.n_q_heads % c.n_kv_heads == 0 &&
+                 gqa_supported(c.n_q_heads / c.n_kv_heads),
+             W4_EINVAL, "unsupported head configuration");
+    W4_CHECK(c.d_model >= kGroup && c.d_model % kGroup == 0 && c.d_ff >= kGroup && c.d_ff % kGroup == 0, W4_EINVAL,
+             "d_model and d_ff must be positive multiples of 128");
+    W4_CHECK(c.n_q_heads * kHeadDim >= kGroup, W4_EINVAL, "bad head count");
+    W4_CHECK(c.vocab >= 1 && c.max_pages >= 1 && c.eps > 0 && c.theta > 0, W4_EINVAL, "bad vocab/max_pages/eps/theta");
+    const void *ptrs[] = {buf->embed, buf->lnf, buf->lm_head, buf->k_cache, buf->v_cache, buf->page_table,
+                          buf->free_list, buf->tokens, buf->logits};
+    for (const void *p : ptrs) W4_CHECK(p != nullptr, W4_EALIGN, "a model buffer is NULL");
+    W4_CHECK(aligned16(buf->lm_head) && aligned16(buf->k_cache) && aligned16(buf->v_cache), W4_EALIGN,
+             "lm_head and KV caches must be 16-byte aligned");
+    for (int l = 0; l < c.n_layers; ++l) {
+        W4_CHECK(buf->qkv_q && buf->qkv_s && buf->qkv_bias && buf->o_q && buf->o_s && buf->gu_q && buf->gu_s &&
+                     buf->down_q && buf->down_s && buf->ln1 && buf->ln2,
+                 W4_EALIGN, "per-layer pointer arrays must not be NULL");
+        W4_CHECK(aligned16(buf->qkv_q[l]) && aligned16(buf->o_q[l]) && aligned16(buf->gu_q[l]) &&
+                     aligned16(buf->down_q[l]) && buf->qkv_s[l] && buf->o_s[l] && buf->gu_s[l] && buf->down_s[l] &&
+                     buf->qkv_bias[l] && buf->ln1[l] && buf->ln2[l],
+                 W4_EALIGN, "layer %d: packed weights must be 16-byte aligned, others non-NULL", l);
+    }
+
+    w4_model *m = new w4_model();
+    m->cfg = c;
+    m->qkv_q.assign(buf->qkv_q, buf->qkv_q + c.n_layers);
+    m->qkv_s.assign(buf->qkv_s, buf->qkv_s + c.n_layers);
+    m->qkv_bias.assign(buf->qkv_bias, buf->qkv_bias + c.n_layers);
+    m->o_q.assign(buf->o_q, buf->o_q + c.n_layers);
+    m->o_s.assign(buf->o_s, buf->o_s + c.n_layers);
+    m->gu_q.assign(buf->gu_q, buf->gu_q + c.n_layers);
+    m->gu_s.assign(buf->gu_s, buf->gu_s + c.n_layers);
+    m->down_q.assign(buf->down_q, buf->down_q + c.n_layers);
+    m->down_s.assign(buf->down_s, buf->down_s + c.n_layers);
+    m->ln1.assign(buf->ln1, buf->ln1 + c.n_layers);
+    m->ln2.assign(buf->ln2, buf->ln2 + c.n_layers);
+    m->embed = buf->embed;
+    m->lnf = buf->lnf;
+    m->lm_head = buf->lm_head;
+    m->k_cache = buf->k_cache;
+    m->v_cache = buf->v_cache;
+    m->page_table = buf->page_table;
+    m->free_list = buf->free_list;
+    m->tokens = buf->tokens;
+    m->logits = buf->logits;
+
+    const int d = c.d_model, f = c.d_ff, qd = c.n_q_heads * kHeadDim;
+    const int qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
+    m->rb_qkv = (qkv_rows + 63) / 64;
+    m->sp_qkv = gemv_split(m->rb_qkv, d / kGroup);
+    m->rb_o = (d + 63) / 64;
+    m->sp_o = gemv_split(m->rb_o, qd / kGroup);
+    m->rb_gu = (2 * f + 63) / 64;
+    m->sp_gu = gemv_split(m->rb_gu, d / kGroup);
+    m->rb_down = (d + 63) / 64;
+    m->sp_down = gemv_split(m->rb_down, f / kGroup);
+    m->rb_head = (c.vocab + 63) / 64;
+    m->attn_pps = attn_pages_per_split(c.max_pages);
+    m->attn_split = attn_n_split(c.max_pages);
+    const int G = c.n_q_heads / c.n_kv_heads;
+
+    // counters for up to rb_head row blocks (the largest row-block count) + partials
+    size_t part = 0;
+    const int rbs[4] = {m->rb_qkv, m->rb_o, m->rb_gu, m->rb_down};
+    const int sps[4] = {m->sp_qkv, m->sp_o, m->sp_gu, m->sp_down};
+    int max_rb = 1;
+    for (int i = 0; i < 4; ++i) {
+        part = std::max(part, gemv_partials(rbs[i], sps[i]));
+        max_rb = std::max(max_rb, rbs[i]);
+    }
+    m->ctr_rb = max_rb;
+    const size_t max_pos = static_cast<size_t>(c.max_pages) * kPage;
+    size_t sizes[9] = {
+        align256(sizeof(StepState)),
+        align256(static_cast<size_t>(d) * 8),
+        align256(static_cast<size_t>(std::max(d, qd)) * 2),
+        align256(static_cast<size_t>(qd) * 2),
+        align256(static_cast<size_t>(qd) * 2),
+        align256(static_cast<size_t>(f) * 2),
+        align256(max_pos * 64 * 2 * 8),
+        align256(gemv_ws_bytes(max_rb, part)),
+        align256(attn_ws_bytes(c.n_kv_heads, G, m->attn_split)),
+    };
+    size_t total = 0;
+    for (size_t s : sizes) total += s;
+    hipError_t e = hipMalloc(&m->arena, total);
+    if (e != hipSuccess) {
+        model_free(m);
+        return fail(W4_EHIP, "hipMalloc(%zu) failed: %s", total, hipGetErrorString(e));
+    }
+    char *b = static_cast<char *>(m->arena);
+    m->state = reinterpret_cast<StepState *>(b); b += sizes[0];
+    m->x = reinterpret_cast<double *>(b); b += sizes[1];
+    m->a = reinterpret_cast<uint16_t *>(b); b += sizes[2];
+    m->qbuf = reinterpret_cast<uint16_t *>(b); b += sizes[3];
+    m->o = reinterpret_cast<uint16_t *>(b); b += sizes[4];
+    m->h = reinterpret_cast<uint16_t *>(b); b += sizes[5];
+    m->rope = reinterpret_cast<double *>(b); b += sizes[6];
+    m->gemv_ws = b; b += sizes[7];
+    m->attn_ws = b; b += sizes[8];
+    m->gemv_ws_size = sizes[7];
+
+    // RoPE angles in fp64 on the host: pair i of position p turns by p * theta^(-2i/128)
+    std::vector<double> rope(max_pos * 64 * 2);
+    for (size_t p = 0; p < max_pos; ++p)
+        for (int i = 0; i < 64; ++i) {
+            const double inv = pow(c.theta, -2.0 * i / kHeadDim);
+            const double phi = static_cast<double>(p) * inv;
+            rope[(p * 64 + i) * 2] = cos(phi);
+            rope[(p * 64 + i) * 2 + 1] = sin(phi);
+        }
+    e = hipMemcpy(m->rope, rope.data(), rope.size() * 8, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(m->arena, 0, sizes[0]);
+    if (e == hipSuccess) e = hipMemset(m->gemv_ws, 0, sizes[7] + sizes[8]);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        model_free(m);
+        return fail(W4_EHIP, "model setup failed: %s", hipGetErrorString(e));
+    }
+    w4_status st = capture(m, false, &m->exec[0]);
+    if (st == W4_OK) st = capture(m, true, &m->exec[1]);
+    if (st != W4_OK) {
+        model_free(m);
+        return st;
+    }
+    m->pos = 0;
+    m->n_prompt = 0;
+    *out = m;
+    return W4_OK;
+}
+
+extern "C" void w4_model_destroy(w4_model *m) {
+    if (m) (void)hipDeviceSynchronize();
+    model_free(m);
+}
+
+extern "C" w4_status w4_model_reset(w4_model *m, int32_t n_prompt, void *stream) {
+    clear_error();
+    W4_CHECK(m != nullptr, W4_ESTATE, "no model");
+    W4_CHECK(n_prompt >= 1 && n_prompt <= m->cfg.max_pages * kPage, W4_EINVAL, "n_prompt=%d out of range", n_prompt);
+    hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), m->state, n_prompt);
+    W4_HIP(hipGetLastError());
+    m->pos = 0;
+    m->n_prompt = n_prompt;
+    return W4_OK;
+}
+
+extern "C" int32_t w4_model_pos(const w4_model *m) { return m ? m->pos : -1; }
+
+extern "C" int32_t w4_model_launches_per_step(const w4_model *m) { return m ? m->launches : 0; }
+
+extern "C" w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream) {
+    clear_error();
+    W4_CHECK(m != nullptr, W4_ESTATE, "no model");
+    W4_CHECK(m->n_prompt >= 1, W4_ESTATE, "w4_model_reset was not called");
+    W4_CHECK(pos == m->pos, W4_ESTATE, "position %d out of sequence (model is at %d)", pos, m->pos);
+    W4_CHECK(pos < m->cfg.max_pages * kPage, W4_ENOSPC, "position %d beyond the KV pool (%d tokens)", pos,
+             m->cfg.max_pages * kPage);
+    W4_CHECK(flags == W4_GRAPH || flags == W4_EAGER, W4_EINVAL, "unknown flags %u", flags);
+    const bool boundary = (pos % kPage) == 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags == W4_EAGER) {
+        W4_HIP(enqueue_step(m, boundary, s));
+    } else {
+        W4_HIP(hipGraphLaunch(m->exec[boundary ? 1 : 0], s));
+    }
+    m->pos = pos + 1;
+    return W4_OK;
+}

@@ -1,0 +1,121 @@
+"""Decoder model on the GPU: packs synthetic weights, uploads them, and drives
+the library's graph-captured decode step.  Marshalling only; every step of the
+decode runs in libw4a16's kernels."""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _to_dev(a: np.ndarray, device) -> torch.Tensor:
+    """Upload raw bytes of a numpy array (fp16 travels as int16 bits)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16 or a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class DecodeModel:
+    """A Qwen2.5-7B-shaped decoder held in device memory.
+
+    dims: a ``synth.ModelDims``; layer_fn(l) returns the layer's LayerWeights
+    (codes, scales and fp16 tensors as numpy arrays); glob the GlobalWeights;
+    free_list the physical page for each successive logical page.
+    """
+
+    def __init__(self, dims, layer_fn, glob, free_list: np.ndarray, max_pages: int,
+                 device="cuda", progress=None):
+        self.dims = dims
+        self.device = torch.device(device)
+        cfg = L.ModelConfig(d_model=dims.d_model, d_ff=dims.d_ff, n_layers=dims.n_layers,
+                            n_q_heads=dims.n_q_heads, n_kv_heads=dims.n_kv_heads,
+                            head_dim=dims.head_dim, vocab=dims.vocab, max_pages=max_pages,
+                            eps=dims.eps, theta=dims.theta)
+        self.cfg = cfg
+        self.max_pages = max_pages
+        perm_qkv = L.model_row_perm(L.W4_PERM_QKV, cfg)
+        perm_gu = L.model_row_perm(L.W4_PERM_GATE_UP, cfg)
+        keep = []                        # device tensors must outlive the model
+        names = ("qkv_q", "qkv_s", "qkv_bias", "o_q", "o_s", "gu_q", "gu_s", "down_q", "down_s",
+                 "ln1", "ln2")
+        ptrs = {n: [] for n in names}
+        dev = self.device
+        for l in range(dims.n_layers):
+            lw = layer_fn(l)
+            pq, ps = L.pack_int4_weights(*lw.qkv, row_perm=perm_qkv)
+            parts = {"qkv_q": pq, "qkv_s": ps, "qkv_bias": lw.bqkv, "ln1": lw.ln1, "ln2": lw.ln2}
+            parts["o_q"], parts["o_s"] = L.pack_int4_weights(*lw.o)
+            gq = np.concatenate([lw.gate[0], lw.up[0]])
+            gs = np.concatenate([lw.gate[1], lw.up[1]])
+            parts["gu_q"], parts["gu_s"] = L.pack_int4_weights(gq, gs, row_perm=perm_gu)
+            del gq, gs
+            parts["down_q"], parts["down_s"] = L.pack_int4_weights(*lw.down)
+            del lw
+            for n in names:
+                t = _to_dev(parts[n], dev)
+                keep.append(t)
+                ptrs[n].append(t.data_ptr())
+            if progress:
+                progress(l)
+        self.embed = _to_dev(glob.embed, dev)
+        self.lnf = _to_dev(glob.lnf, dev)
+        self.lm_head = _to_dev(L.pack_f16_matrix(glob.lm_head), dev)
+        kv_elems = dims.n_layers * max_pages * dims.n_kv_heads * 16 * dims.head_dim
+        self.k_cache = torch.zeros(kv_elems, dtype=torch.float16, device=dev)
+        self.v_cache = torch.zeros(kv_elems, dtype=torch.float16, device=dev)
+        self.page_table = torch.full((max_pages,), -1, dtype=torch.int32, device=dev)
+        self.free_list = torch.from_numpy(np.ascontiguousarray(free_list, dtype=np.int32)).to(dev)
+        self.tokens = torch.zeros(16 * max_pages + 1, dtype=torch.int32, device=dev)
+        self.logits = torch.zeros(dims.vocab, dtype=torch.float32, device=dev)
+        self._keep = keep
+        self._arrays = {n: (C.c_void_p * dims.n_layers)(*ptrs[n]) for n in names}
+        buf = L.ModelBuffers()
+        for n in names:
+            setattr(buf, n, C.cast(self._arrays[n], C.POINTER(C.c_void_p)))
+        buf.embed, buf.lnf, buf.lm_head = self.embed.data_ptr(), self.lnf.data_ptr(), self.lm_head.data_ptr()
+        buf.k_cache, buf.v_cache = self.k_cache.data_ptr(), self.v_cache.data_ptr()
+        buf.page_table, buf.free_list = self.page_table.data_ptr(), self.free_list.data_ptr()
+        buf.tokens, buf.logits = self.tokens.data_ptr(), self.logits.data_ptr()
+        self._buf = buf
+        torch.cuda.synchronize(dev)
+        handle = C.c_void_p()
+        L.check(L.lib().w4_model_create(C.byref(cfg), C.byref(buf), C.byref(handle)))
+        self._m = handle
+
+    # ------------------------------------------------------------------
+    def reset(self, prompt: np.ndarray, stream=None) -> None:
+        prompt = np.ascontiguousarray(prompt, dtype=np.int32)
+        self.tokens.zero_()
+        self.tokens[: len(prompt)] = torch.from_numpy(prompt).to(self.device)
+        self.page_table.fill_(-1)
+        L.check(L.lib().w4_model_reset(self._m, len(prompt), L._stream(stream)))
+
+    @property
+    def pos(self) -> int:
+        return L.lib().w4_model_pos(self._m)
+
+    def step(self, flags: int = L.W4_GRAPH, stream=None) -> None:
+        decode_step(self, self.pos, flags, stream)
+
+    def launches_per_step(self) -> int:
+        return L.lib().w4_model_launches_per_step(self._m)
+
+    def close(self) -> None:
+        if getattr(self, "_m", None):
+            L.lib().w4_model_destroy(self._m)
+            self._m = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def decode_step(model: DecodeModel, pos: int, flags: int = L.W4_GRAPH, stream=None) -> None:
+    """One decode step at position pos (graph replay by default)."""
+    L.check(L.lib().decode_step(model._m, int(pos), int(flags), L._stream(stream)))

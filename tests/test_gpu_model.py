@@ -1,0 +1,112 @@
+"""Decode-step parity: the graph-captured GPU step against the oracle's
+teacher-forced pass, graph == eager bitwise, page-table bookkeeping, and the
+step's error paths."""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import int4_weight_only_dequant_amd as w4
+from int4_weight_only_dequant_amd import _lib as L
+from tests._tol import LOGIT_ATOL
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_model(model, prompt, n_steps, flags=L.W4_GRAPH):
+    """Teacher-forced prompt, then free-running greedy steps; returns per-step
+    logits (float32 [n_steps, V]) and the token history."""
+    model.reset(prompt)
+    out = []
+    for _ in range(n_steps):
+        model.step(flags)
+        out.append(model.logits.clone())
+    torch.cuda.synchronize()
+    toks = model.tokens[: n_steps + 1].cpu().numpy()
+    return torch.stack(out).cpu().numpy(), toks
+
+
+def compare_with_oracle(dims, layers, glob, logits, toks, n_prompt, positions):
+    ref = oracle.forward_teacher_forced(dims, layers, glob, toks[: positions[-1] + 1], positions,
+                                        progress=lambda l: say(f"  oracle layer {l} done"))
+    err = np.abs(logits[positions] - ref)
+    worst = float(err.max())
+    mism = []
+    for i, p in enumerate(positions):
+        want = oracle.argmax_first(ref[i])
+        srt = np.sort(ref[i])
+        margin = float(srt[-1] - srt[-2])
+        if p + 1 >= n_prompt and toks[p + 1] != want:
+            mism.append((int(p), int(toks[p + 1]), want, margin))
+    return worst, mism
+
+
+def test_tiny_model_parity_graph_eager_and_pages():
+    dims = synth.TINY
+    layers = [synth.layer_weights(dims, l, cfg=102) for l in range(dims.n_layers)]
+    glob = synth.global_weights(dims, cfg=102)
+    max_pages = 4
+    free = synth.page_free_list(max_pages, cfg=102)
+    prompt = synth.prompt_ids(dims, 20, cfg=102)
+    say("case: tiny model (2 layers) 20-token prompt + 44 steps, 4 shuffled pages")
+    model = w4.DecodeModel(dims, lambda l: layers[l], glob, free, max_pages)
+    try:
+        n = 64
+        lg, tk = run_model(model, prompt, n, L.W4_GRAPH)
+        pt = model.page_table.cpu().numpy()
+        assert np.array_equal(pt, free)                    # every boundary appended its page
+        le, te = run_model(model, prompt, n, L.W4_EAGER)
+        assert np.array_equal(tk, te)
+        assert np.array_equal(lg.view(np.uint32), le.view(np.uint32))   # graph == eager bitwise
+        assert np.array_equal(tk[:20], prompt)
+        worst, mism = compare_with_oracle(dims, layers, glob, lg, tk, 20, np.arange(n))
+        say(f"tiny: max |logit err| {worst:.3e}; token mismatches {mism}")
+        assert worst <= LOGIT_ATOL
+        assert not mism
+        # error paths
+        with pytest.raises(w4.W4Error) as e:
+            w4.decode_step(model, 3, L.W4_GRAPH)
+        assert e.value.status == L.W4_ESTATE
+        with pytest.raises(w4.W4Error) as e:
+            model.step()                                   # position 64 = 16 * max_pages: pool full
+        assert e.value.status == L.W4_ENOSPC
+    finally:
+        model.close()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1500)
+def test_full_model_512_plus_128():
+    """The Qwen2.5-7B-shaped step: 512-token prompt, 128 greedy graph steps
+    crossing 8 page boundaries; 129 logit vectors and tokens vs the oracle."""
+    dims = synth.QWEN7B
+    t0 = time.time()
+    say("case: full model 28 layers, prompt 512 + 128 generated, 40 shuffled pages")
+    glob = synth.global_weights(dims)
+    free = synth.page_free_list(40)
+    prompt = synth.prompt_ids(dims, 512)
+    model = w4.DecodeModel(dims, lambda l: synth.layer_weights(dims, l), glob, free, 40,
+                           progress=lambda l: say(f"  packed+uploaded layer {l} ({time.time() - t0:.0f}s)"))
+    try:
+        say(f"model ready {time.time() - t0:.0f}s")
+        lg, tk = run_model(model, prompt, 640, L.W4_GRAPH)
+        pt = model.page_table.cpu().numpy()
+    finally:
+        model.close()
+    say(f"GPU run done {time.time() - t0:.0f}s; tokens {tk[512:530]}...")
+    assert np.array_equal(pt, free)
+    positions = np.arange(511, 640)
+    worst, mism = compare_with_oracle(dims, lambda l: synth.layer_weights(dims, l), glob, lg, tk,
+                                      512, positions)
+    say(f"full: max |logit err| over 129 positions {worst:.3e}; mismatches {mism} ({time.time() - t0:.0f}s)")
+    assert worst <= LOGIT_ATOL
+    assert not mism
