@@ -254,6 +254,19 @@ w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream);
 /* Number of kernel launches one eager step makes (for the launch-count report). */
 int32_t w4_model_launches_per_step(const w4_model *m);
 
+/* Measurement hook: enqueues `reps` launches of one of the step's kernels,
+ * with the step's launch geometry, cycling over the layers' weights (so
+ * consecutive launches stream distinct weights from HBM).  The launches read
+ * and overwrite the model's activation scratch: call w4_model_reset before
+ * the next decode_step.  kind: W4_KERNEL_GATE_UP (gate+up GEMV + SwiGLU),
+ * W4_KERNEL_DOWN (down GEMV + residual), W4_KERNEL_O (O GEMV + residual),
+ * W4_KERNEL_LM_HEAD (fp16 lm_head GEMV + argmax).  Errors: W4_EINVAL. */
+#define W4_KERNEL_GATE_UP 0
+#define W4_KERNEL_DOWN    1
+#define W4_KERNEL_O       2
+#define W4_KERNEL_LM_HEAD 3
+w4_status w4_model_kernel_replay(w4_model *m, int32_t kind, int32_t reps, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libw4a16.so")
 W4_OK, W4_EINVAL, W4_EALIGN, W4_ERANGE, W4_ESTATE, W4_ENOSPC, W4_EHIP = 0, -1, -2, -3, -4, -5, -6
 W4_PERM_QKV, W4_PERM_GATE_UP = 0, 1
 W4_GRAPH, W4_EAGER = 0, 1
+W4_KERNEL_GATE_UP, W4_KERNEL_DOWN, W4_KERNEL_O, W4_KERNEL_LM_HEAD = 0, 1, 2, 3
 
 _STATUS = {W4_EINVAL: "W4_EINVAL", W4_EALIGN: "W4_EALIGN", W4_ERANGE: "W4_ERANGE",
            W4_ESTATE: "W4_ESTATE", W4_ENOSPC: "W4_ENOSPC", W4_EHIP: "W4_EHIP"}
@@ -75,6 +76,7 @@ def _declare(lib):
         "w4_model_pos": (i32, [vp]),
         "decode_step": (i32, [vp, i32, u32, vp]),
         "w4_model_launches_per_step": (i32, [vp]),
+        "w4_model_kernel_replay": (i32, [vp, i32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -17,8 +17,10 @@
 // end the 16 slots are merged through LDS, the work-group publishes its
 // partial, and the last work-group of the kv head merges all splits and
 // writes fp16 outputs.  Every barrier is reached by all waves (no barrier in
-// lane- or wave-dependent control flow), and the last-arriver exchange uses
-// device-scope fences, so no work-group reads a partial before it is complete.
+// lane- or wave-dependent control flow).  Partials travel through device-scope
+// (sc1) stores and loads; every wave waits for its stores to be acknowledged
+// before the barrier that precedes the arrival atomic, so the last work-group
+// never reads a partial before it is complete.
 #pragma once
 
 #include "w4_device.hpp"
@@ -44,11 +46,28 @@ struct AttnProblem {
 
 inline int attn_pages_per_split(int n_pages_max) {
     int pps = (n_pages_max + 63) / 64;
-    return pps < 2 ? 2 : pps;
+    return pps < 4 ? 4 : pps;
 }
 inline int attn_n_split(int n_pages_max) {
     const int pps = attn_pages_per_split(n_pages_max);
     return (n_pages_max + pps - 1) / pps;
+}
+
+constexpr int kAttnChunk = 4;   // pages loaded together (8 x 16 B per lane)
+
+template <int G>
+__device__ __forceinline__ void attn_load_chunk(const AttnProblem &a, int j, int c0, int p_end, size_t lane_off,
+                                                u32x4 (&k)[kAttnChunk], u32x4 (&v)[kAttnChunk]) {
+    const size_t slice = static_cast<size_t>(kPage) * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < kAttnChunk; ++i) {
+        if (c0 + i < p_end) {
+            const int phys = a.page_table[c0 + i];
+            const size_t base = (static_cast<size_t>(phys) * a.n_kvh + j) * slice + lane_off;
+            k[i] = *reinterpret_cast<const u32x4 *>(a.kpool + base);
+            v[i] = *reinterpret_cast<const u32x4 *>(a.vpool + base);
+        }
+    }
 }
 
 template <int G>
@@ -68,6 +87,11 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
     const int p_begin = sp * a.pages_per_split;
     int p_end = p_begin + a.pages_per_split;
     if (p_end > n_pages) p_end = n_pages;
+    const size_t lane_off = static_cast<size_t>(slot) * kHeadDim + dc * 8;
+
+    // issue the first chunk of K/V loads before anything else
+    u32x4 kb[kAttnChunk], vb[kAttnChunk];
+    attn_load_chunk<G>(a, j, p_begin, p_end, lane_off, kb, vb);
 
     // query heads of this kv head, 8 dims each
     uint32_t qv[G][4];
@@ -85,45 +109,39 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
         for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
     }
 
-    const size_t slice = static_cast<size_t>(kPage) * kHeadDim;     // halves per kv-head slice
-    const size_t lane_off = static_cast<size_t>(slot) * kHeadDim + dc * 8;
-    u32x4 kn = {0, 0, 0, 0}, vn = {0, 0, 0, 0};
-    if (p_begin < p_end) {
-        const int phys = a.page_table[p_begin];
-        const size_t base = (static_cast<size_t>(phys) * a.n_kvh + j) * slice + lane_off;
-        kn = *reinterpret_cast<const u32x4 *>(a.kpool + base);
-        vn = *reinterpret_cast<const u32x4 *>(a.vpool + base);
-    }
-    for (int lp = p_begin; lp < p_end; ++lp) {
-        const u32x4 kc = kn, vc = vn;
-        if (lp + 1 < p_end) {            // prefetch the next page of this split
-            const int phys = a.page_table[lp + 1];
-            const size_t base = (static_cast<size_t>(phys) * a.n_kvh + j) * slice + lane_off;
-            kn = *reinterpret_cast<const u32x4 *>(a.kpool + base);
-            vn = *reinterpret_cast<const u32x4 *>(a.vpool + base);
-        }
-        const int tok = lp * kPage + slot;
-        float vf[8];
-        vf[0] = static_cast<float>(as_h2(vc.x)[0]); vf[1] = static_cast<float>(as_h2(vc.x)[1]);
-        vf[2] = static_cast<float>(as_h2(vc.y)[0]); vf[3] = static_cast<float>(as_h2(vc.y)[1]);
-        vf[4] = static_cast<float>(as_h2(vc.z)[0]); vf[5] = static_cast<float>(as_h2(vc.z)[1]);
-        vf[6] = static_cast<float>(as_h2(vc.w)[0]); vf[7] = static_cast<float>(as_h2(vc.w)[1]);
+    for (int c0 = p_begin; c0 < p_end; c0 += kAttnChunk) {
+        u32x4 kc[kAttnChunk], vc[kAttnChunk];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float s = 0.f;
-            s = __builtin_amdgcn_fdot2(as_h2(qv[h][0]), as_h2(kc.x), s, false);
-            s = __builtin_amdgcn_fdot2(as_h2(qv[h][1]), as_h2(kc.y), s, false);
-            s = __builtin_amdgcn_fdot2(as_h2(qv[h][2]), as_h2(kc.z), s, false);
-            s = __builtin_amdgcn_fdot2(as_h2(qv[h][3]), as_h2(kc.w), s, false);
-            s = row16_sum(s) * a.scale_log2;
-            if (tok < ctx) {             // uniform over the 16 lanes of a row
-                const float m_new = fmaxf(m[h], s);
-                const float corr = exp2f(m[h] - m_new);   // 0 on the first token (m = -inf)
-                const float pw = exp2f(s - m_new);
-                l[h] = l[h] * corr + pw;
+        for (int i = 0; i < kAttnChunk; ++i) { kc[i] = kb[i]; vc[i] = vb[i]; }
+        if (c0 + kAttnChunk < p_end)                      // prefetch the next chunk
+            attn_load_chunk<G>(a, j, c0 + kAttnChunk, p_end, lane_off, kb, vb);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * corr + pw * vf[i];
-                m[h] = m_new;
+        for (int i = 0; i < kAttnChunk; ++i) {
+            const int lp = c0 + i;
+            if (lp >= p_end) break;                       // uniform across the work-group
+            const int tok = lp * kPage + slot;
+            float vf[8];
+            vf[0] = static_cast<float>(as_h2(vc[i].x)[0]); vf[1] = static_cast<float>(as_h2(vc[i].x)[1]);
+            vf[2] = static_cast<float>(as_h2(vc[i].y)[0]); vf[3] = static_cast<float>(as_h2(vc[i].y)[1]);
+            vf[4] = static_cast<float>(as_h2(vc[i].z)[0]); vf[5] = static_cast<float>(as_h2(vc[i].z)[1]);
+            vf[6] = static_cast<float>(as_h2(vc[i].w)[0]); vf[7] = static_cast<float>(as_h2(vc[i].w)[1]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float sc = 0.f;
+                sc = __builtin_amdgcn_fdot2(as_h2(qv[h][0]), as_h2(kc[i].x), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv[h][1]), as_h2(kc[i].y), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv[h][2]), as_h2(kc[i].z), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv[h][3]), as_h2(kc[i].w), sc, false);
+                sc = row16_sum(sc) * a.scale_log2;
+                if (tok < ctx) {                          // uniform over the 16 lanes of a row
+                    const float m_new = fmaxf(m[h], sc);
+                    const float corr = exp2f(m[h] - m_new);   // 0 on the first token (m = -inf)
+                    const float pw = exp2f(sc - m_new);
+                    l[h] = l[h] * corr + pw;
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) acc[h][d] = acc[h][d] * corr + pw * vf[d];
+                    m[h] = m_new;
+                }
             }
         }
     }
@@ -155,6 +173,9 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
             store_agent(a.part_ml + (pbase + h) * 2 + 1, L);
         }
     }
+    // every wave waits until its partial stores are acknowledged before the
+    // barrier, so wave 0's arrival below is ordered after all of them
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t < 64) {
         const bool last = arrive_last(a.counter + j, static_cast<unsigned>(a.n_split));
@@ -162,23 +183,54 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    // merge all splits of kv head j (fixed order: deterministic)
-    for (int idx = t; idx < G * 128; idx += kThreads) {
-        const int h = idx >> 7, d = idx & 127;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+    // merge all splits of kv head j in split order (deterministic).  The
+    // (max, sum) pairs go through LDS (reusing s_acc); then lane (h, 4 dims)
+    // streams its n_split float4 partials with independent loads.
+    float *sml = &s_acc[0][0][0];
+    const int n_ml = a.n_split * G;
+    for (int i = t; i < n_ml; i += kThreads) {
+        const size_t pb = static_cast<size_t>(j) * a.n_split * G + i;   // (s, h) flattened
+        sml[2 * i] = load_agent(a.part_ml + pb * 2);
+        sml[2 * i + 1] = load_agent(a.part_ml + pb * 2 + 1);
+    }
+    __syncthreads();
+    if (t < G * 32) {
+        const int h = t >> 5, d4 = (t & 31) * 4;
         float M = -INFINITY;
-        for (int s = 0; s < a.n_split; ++s)
-            M = fmaxf(M, load_agent(a.part_ml + ((static_cast<size_t>(j) * a.n_split + s) * G + h) * 2));
-        float L = 0.f, A = 0.f;
-        for (int s = 0; s < a.n_split; ++s) {
-            const size_t pb = (static_cast<size_t>(j) * a.n_split + s) * G + h;
-            const float ms = load_agent(a.part_ml + pb * 2);
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            L += load_agent(a.part_ml + pb * 2 + 1) * f;
-            A += load_agent(a.part_acc + pb * 128 + d) * f;
+        for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, sml[2 * (s * G + h)]);
+        float L = 0.f, A0 = 0.f, A1 = 0.f, A2 = 0.f, A3 = 0.f;
+        const float *base = a.part_acc + (static_cast<size_t>(j) * a.n_split * G + h) * 128 + d4;
+        const size_t stride = static_cast<size_t>(G) * 128;
+        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
+            float4 pa[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (s0 + u < a.n_split) {
+                    const float *pp = base + (s0 + u) * stride;
+                    pa[u] = make_float4(load_agent(pp), load_agent(pp + 1), load_agent(pp + 2), load_agent(pp + 3));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s = s0 + u;
+                if (s < a.n_split) {
+                    const float ms = sml[2 * (s * G + h)];
+                    if (ms != -INFINITY) {
+                        const float f = exp2f(ms - M);
+                        L += sml[2 * (s * G + h) + 1] * f;
+                        A0 += pa[u].x * f; A1 += pa[u].y * f; A2 += pa[u].z * f; A3 += pa[u].w * f;
+                    }
+                }
+            }
         }
-        a.out[(j * G + h) * 128 + d] = f32_to_f16(A / L);
+        const float inv = 1.0f / L;
+        uint16_t *o = a.out + (j * G + h) * 128 + d4;
+        o[0] = f32_to_f16(A0 * inv);
+        o[1] = f32_to_f16(A1 * inv);
+        o[2] = f32_to_f16(A2 * inv);
+        o[3] = f32_to_f16(A3 * inv);
     }
 }
 

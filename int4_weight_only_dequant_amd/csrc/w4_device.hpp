@@ -79,16 +79,26 @@ __device__ __forceinline__ T load_agent(const T *p) {
 }
 
 // Last-arriver election: every work-group of a reduction calls this once
-// (from one wave) after publishing its partial; returns true in exactly one
-// of them, which then sees all partials.  The winner resets the counter.
+// (from one full wave) after publishing its partial; returns true in exactly
+// one of them, which then sees all partials.  The winner resets the counter.
+//
+// Partials are written with store_agent and read with load_agent: device-
+// scope accesses (sc1) that complete at the device's coherence point, past
+// the per-XCD L2s.  So a work-group fence (wait until this wave's stores are
+// acknowledged, no compiler reordering) is enough before the arrival atomic;
+// an agent-scope fence would also write back and invalidate the whole L2,
+// which costs microseconds per work-group.  Partials stored by other waves of
+// the work-group are covered by the __syncthreads() the callers place before
+// this call (its release waits for their stores).
 __device__ __forceinline__ bool arrive_last(unsigned *counter, unsigned n_arrivals) {
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
     unsigned old = 0;
     if ((threadIdx.x & 63) == 0) old = atomicAdd(counter, 1u);
     old = __builtin_amdgcn_readfirstlane(old);
     const bool last = old == n_arrivals - 1;
     if (last) {
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         if ((threadIdx.x & 63) == 0) store_agent(counter, 0u);
     }
     return last;

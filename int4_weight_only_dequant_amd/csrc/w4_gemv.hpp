@@ -72,6 +72,7 @@ __device__ __forceinline__ double wg_sum4(double v, double *lds) {
 template <class Epi>
 __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(W4Problem p, Epi epi) {
     __shared__ double red[4 * 64];
+    __shared__ int s_flag;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int rb = blockIdx.x % p.n_rb;
@@ -103,25 +104,44 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(W4Problem p, Epi epi)
         acc += static_cast<double>(group_sum) * static_cast<double>(f16_to_f32(sbits));
     }
 
-    const double total = wg_sum4(acc, red);
-    if (wave != 0) return;
+    double total = wg_sum4(acc, red);
     const int row = rb * 64 + lane;
-    if (p.n_split == 1) {
-        epi(row, lane, total);
-        return;
+    if (p.n_split > 1) {
+        // publish this split's partial; the last work-group of the row block
+        // sums all of them (all 4 waves load in parallel, fixed order)
+        const size_t n_rows = static_cast<size_t>(p.n_rb) * 64;
+        if (wave == 0) {
+            store_agent(p.partial + sp * n_rows + row, total);
+            const bool last = arrive_last(p.counter + rb, static_cast<unsigned>(p.n_split));
+            if (lane == 0) s_flag = last ? 1 : 0;
+        }
+        __syncthreads();
+        if (!s_flag) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        double part = 0.0;
+        int s = wave;
+        for (; s + 12 < p.n_split; s += 16) {
+            const double a0 = load_agent(p.partial + s * n_rows + row);
+            const double a1 = load_agent(p.partial + (s + 4) * n_rows + row);
+            const double a2 = load_agent(p.partial + (s + 8) * n_rows + row);
+            const double a3 = load_agent(p.partial + (s + 12) * n_rows + row);
+            part += a0;
+            part += a1;
+            part += a2;
+            part += a3;
+        }
+        for (; s < p.n_split; s += 4) part += load_agent(p.partial + s * n_rows + row);
+        total = wg_sum4(part, red);
     }
-    const size_t n_rows = static_cast<size_t>(p.n_rb) * 64;
-    store_agent(p.partial + sp * n_rows + row, total);
-    if (!arrive_last(p.counter + rb, static_cast<unsigned>(p.n_split))) return;
-    double sum = 0.0;
-    for (int s = 0; s < p.n_split; ++s) sum += load_agent(p.partial + s * n_rows + row);
-    epi(row, lane, sum);
+    if (wave == 0) epi(row, lane, total);
+    if constexpr (Epi::kGridTail) epi.grid_tail(p.n_rb, s_flag);
 }
 
 // ---------------------------------------------------------------- epilogues --
 // Called by all 64 lanes of one wave with (packed row, lane, fp64 result).
 
 struct EpiStoreF16 {          // y[row] = fp16(v)
+    static constexpr bool kGridTail = false;
     uint16_t *y;
     int n;
     __device__ void operator()(int row, int, double v) const {
@@ -130,6 +150,7 @@ struct EpiStoreF16 {          // y[row] = fp16(v)
 };
 
 struct EpiResidual {          // x[row] += v   (fp64 residual stream)
+    static constexpr bool kGridTail = false;
     double *x;
     int n;
     __device__ void operator()(int row, int, double v) const {
@@ -137,9 +158,57 @@ struct EpiResidual {          // x[row] += v   (fp64 residual stream)
     }
 };
 
+// Residual update followed by the RMSNorm that feeds the next GEMV:
+// x[row] += v; then, once every row block is done, the last work-group to
+// finish computes a = fp16(x / sqrt(mean(x^2) + eps) * w) for all of x.
+// Each row block publishes the sum of squares of its 64 new values; the
+// grand total is summed in row-block order, so results are deterministic.
+struct EpiResidualNorm {
+    static constexpr bool kGridTail = true;
+    double *x;
+    int n;
+    const uint16_t *w;        // norm weight [n]
+    uint16_t *a;              // fp16 output [n]
+    double *ss;               // [n_rb] sums of squares
+    unsigned *counter;        // arrivals of row blocks (zero between calls)
+    double eps;
+    __device__ void operator()(int row, int lane, double v) const {
+        double xn = 0.0;
+        if (row < n) {
+            xn = x[row] + v;
+            store_agent(x + row, xn);
+        }
+        double sq = xn * xn;
+        for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+        if (lane == 0) store_agent(ss + (row >> 6), sq);
+    }
+    // all 4 waves; block_last = whether this work-group ran the epilogue
+    __device__ void grid_tail(int n_rb, int &flag) const {
+        __shared__ double s_rms;
+        const int t = threadIdx.x;
+        if (t < 64) {
+            const bool last = arrive_last(counter, static_cast<unsigned>(n_rb));
+            if (t == 0) flag = last ? 1 : 0;
+        }
+        __syncthreads();
+        if (!flag) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        if (t < 64) {
+            double tot = 0.0;
+            for (int b = 0; b < n_rb; ++b) tot += load_agent(ss + b);   // fixed order
+            if (t == 0) s_rms = sqrt(tot / n + eps);
+        }
+        __syncthreads();
+        const double r = s_rms;
+        for (int i = t; i < n; i += kThreads)
+            a[i] = f64_to_f16(load_agent(x + i) / r * static_cast<double>(f16_to_f32(w[i])));
+    }
+};
+
 // gate/up interleaved rows: even lane holds gate_i, odd lane up_i;
 // h[i] = fp16(silu(gate_i) * up_i).
 struct EpiSwiGLU {
+    static constexpr bool kGridTail = false;
     uint16_t *h;
     int n_pairs;
     __device__ void operator()(int row, int lane, double v) const {
@@ -155,6 +224,7 @@ struct EpiSwiGLU {
 // i+64): adds the bias, rotates q and k heads by the position's angles, rounds
 // to fp16, writes q to qbuf and k, v to the paged cache slot of the position.
 struct EpiQKV {
+    static constexpr bool kGridTail = false;
     const uint16_t *bias;     // fp16 [rows], logical order
     const double *rope;       // [max_pos][64][2] = (cos, sin)
     const int *pos_ptr;       // current position

@@ -23,30 +23,27 @@ struct StepState {
     unsigned long long best; // argmax key of the step's logits
 };
 
-// x = embed[tokens[pos]] as fp64; clears the argmax key.
+// x = embed[tokens[pos]] as fp64, a = fp16(RMSNorm(x) * w) for the first
+// layer; clears the argmax key.  One work-group.
 __global__ __launch_bounds__(kThreads) void embed_kernel(const uint16_t *embed, const int *tokens,
-                                                         StepState *st, double *x, int d) {
+                                                         StepState *st, double *x, const uint16_t *w,
+                                                         uint16_t *a, int d, double eps) {
+    __shared__ double red[kThreads / 64];
     const int tok = tokens[st->pos];
     const uint16_t *row = embed + static_cast<size_t>(tok) * d;
-    for (int i = threadIdx.x; i < d; i += kThreads) x[i] = static_cast<double>(f16_to_f32(row[i]));
-    if (threadIdx.x == 0) st->best = 0ull;
-}
-
-// a = fp16(x / sqrt(mean(x^2) + eps) * w), computed in fp64 with one rounding.
-__global__ __launch_bounds__(1024) void rmsnorm_kernel(const double *x, const uint16_t *w, uint16_t *a,
-                                                       int d, double eps) {
-    __shared__ double red[1024 / 64];
     double ss = 0.0;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) ss += x[i] * x[i];
+    for (int i = threadIdx.x; i < d; i += kThreads) {
+        const double v = static_cast<double>(f16_to_f32(row[i]));
+        x[i] = v;
+        ss += v * v;
+    }
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    double tot = 0.0;
-    const int nw = blockDim.x >> 6;
-    for (int i = 0; i < nw; ++i) tot += red[i];
-    const double r = sqrt(tot / d + eps);
-    for (int i = threadIdx.x; i < d; i += blockDim.x)
-        a[i] = f64_to_f16(x[i] / r * static_cast<double>(f16_to_f32(w[i])));
+    const double r = sqrt((((red[0] + red[1]) + red[2]) + red[3]) / d + eps);
+    for (int i = threadIdx.x; i < d; i += kThreads)
+        a[i] = f64_to_f16(static_cast<double>(f16_to_f32(row[i])) / r * static_cast<double>(f16_to_f32(w[i])));
+    if (threadIdx.x == 0) st->best = 0ull;
 }
 
 // Boundary-variant first node: the page of the position is appended.
@@ -298,6 +295,8 @@ struct w4_model {
     uint16_t *h;        // SwiGLU output [d_ff]
     double *rope;       // [max_pos][64][2]
     void *gemv_ws;      // shared by the GEMVs of a step (stream-ordered)
+    double *norm_ss;    // per-row-block sums of squares of the fused RMSNorm
+    unsigned *norm_ctr; // row-block arrivals of the fused RMSNorm
     void *attn_ws;
     size_t gemv_ws_size;
 
@@ -350,13 +349,13 @@ static hipError_t enqueue_step(w4_model *m, bool boundary, hipStream_t s) {
         hipLaunchKernelGGL(page_append_kernel, dim3(1), dim3(1), 0, s, m->state, m->page_table, m->free_list);
         W4_Q(hipGetLastError());
     }
-    hipLaunchKernelGGL(embed_kernel, dim3(1), dim3(kThreads), 0, s, m->embed, m->tokens, m->state, m->x, d);
+    hipLaunchKernelGGL(embed_kernel, dim3(1), dim3(kThreads), 0, s, m->embed, m->tokens, m->state, m->x, m->ln1[0],
+                       m->a, d, double(c.eps));
     W4_Q(hipGetLastError());
     for (int l = 0; l < c.n_layers; ++l) {
         uint16_t *kc = m->k_cache + l * layer_kv_elems(m);
         uint16_t *vc = m->v_cache + l * layer_kv_elems(m);
-        hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, s, m->x, m->ln1[l], m->a, d, double(c.eps));
-        W4_Q(hipGetLastError());
+        // a holds RMSNorm(x) * ln1[l] (from the embedding or the previous down GEMV)
         EpiQKV eq{m->qkv_bias[l], m->rope, pos_ptr, m->page_table, m->qbuf, kc, vc, c.n_q_heads, c.n_kv_heads};
         W4_Q(launch_w4(w4_problem(m, m->qkv_q[l], m->qkv_s[l], m->a, m->rb_qkv, m->sp_qkv, d), eq, s));
         AttnProblem a;
@@ -373,15 +372,15 @@ static hipError_t enqueue_step(w4_model *m, bool boundary, hipStream_t s) {
         a.out = m->o;
         attn_ws_carve(m->attn_ws, c.n_kv_heads, G, m->attn_split, a);
         W4_Q(launch_attn(G, a, s));
-        W4_Q(launch_w4(w4_problem(m, m->o_q[l], m->o_s[l], m->o, m->rb_o, m->sp_o, qd), EpiResidual{m->x, d}, s));
-        hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, s, m->x, m->ln2[l], m->a, d, double(c.eps));
-        W4_Q(hipGetLastError());
+        // x += Wo o, then a = RMSNorm(x) * ln2[l]
+        EpiResidualNorm eo{m->x, d, m->ln2[l], m->a, m->norm_ss, m->norm_ctr, double(c.eps)};
+        W4_Q(launch_w4(w4_problem(m, m->o_q[l], m->o_s[l], m->o, m->rb_o, m->sp_o, qd), eo, s));
         W4_Q(launch_w4(w4_problem(m, m->gu_q[l], m->gu_s[l], m->a, m->rb_gu, m->sp_gu, d), EpiSwiGLU{m->h, f}, s));
-        W4_Q(launch_w4(w4_problem(m, m->down_q[l], m->down_s[l], m->h, m->rb_down, m->sp_down, f),
-                       EpiResidual{m->x, d}, s));
+        // x += Wd h, then a = RMSNorm(x) * (ln1[l+1] or the final norm)
+        const uint16_t *next_w = l + 1 < c.n_layers ? m->ln1[l + 1] : m->lnf;
+        EpiResidualNorm ed{m->x, d, next_w, m->a, m->norm_ss, m->norm_ctr, double(c.eps)};
+        W4_Q(launch_w4(w4_problem(m, m->down_q[l], m->down_s[l], m->h, m->rb_down, m->sp_down, f), ed, s));
     }
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, s, m->x, m->lnf, m->a, d, double(c.eps));
-    W4_Q(hipGetLastError());
     F16Problem hp;
     hp.w = reinterpret_cast<const u32x4 *>(m->lm_head);
     hp.x = reinterpret_cast<const uint32_t *>(m->a);
@@ -502,7 +501,7 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
     }
     m->ctr_rb = max_rb;
     const size_t max_pos = static_cast<size_t>(c.max_pages) * kPage;
-    size_t sizes[9] = {
+    size_t sizes[10] = {
         align256(sizeof(StepState)),
         align256(static_cast<size_t>(d) * 8),
         align256(static_cast<size_t>(std::max(d, qd)) * 2),
@@ -512,6 +511,7 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
         align256(max_pos * 64 * 2 * 8),
         align256(gemv_ws_bytes(max_rb, part)),
         align256(attn_ws_bytes(c.n_kv_heads, G, m->attn_split)),
+        align256(static_cast<size_t>(max_rb) * 8) + 256,
     };
     size_t total = 0;
     for (size_t s : sizes) total += s;
@@ -530,6 +530,8 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
     m->rope = reinterpret_cast<double *>(b); b += sizes[6];
     m->gemv_ws = b; b += sizes[7];
     m->attn_ws = b; b += sizes[8];
+    m->norm_ctr = reinterpret_cast<unsigned *>(b);
+    m->norm_ss = reinterpret_cast<double *>(b + 256); b += sizes[9];
     m->gemv_ws_size = sizes[7];
 
     // RoPE angles in fp64 on the host: pair i of position p turns by p * theta^(-2i/128)
@@ -543,7 +545,7 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
         }
     e = hipMemcpy(m->rope, rope.data(), rope.size() * 8, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(m->arena, 0, sizes[0]);
-    if (e == hipSuccess) e = hipMemset(m->gemv_ws, 0, sizes[7] + sizes[8]);
+    if (e == hipSuccess) e = hipMemset(m->gemv_ws, 0, sizes[7] + sizes[8] + sizes[9]);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -598,5 +600,47 @@ extern "C" w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void 
         W4_HIP(hipGraphLaunch(m->exec[boundary ? 1 : 0], s));
     }
     m->pos = pos + 1;
+    return W4_OK;
+}
+
+extern "C" w4_status w4_model_kernel_replay(w4_model *m, int32_t kind, int32_t reps, void *stream) {
+    clear_error();
+    W4_CHECK(m != nullptr, W4_ESTATE, "no model");
+    W4_CHECK(reps >= 1, W4_EINVAL, "reps must be positive");
+    const w4_model_config &c = m->cfg;
+    const int d = c.d_model, f = c.d_ff, qd = c.n_q_heads * kHeadDim;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int r = 0; r < reps; ++r) {
+        const int l = r % c.n_layers;
+        switch (kind) {
+            case W4_KERNEL_GATE_UP:
+                W4_HIP(launch_w4(w4_problem(m, m->gu_q[l], m->gu_s[l], m->a, m->rb_gu, m->sp_gu, d),
+                                 EpiSwiGLU{m->h, f}, s));
+                break;
+            case W4_KERNEL_DOWN:
+                W4_HIP(launch_w4(w4_problem(m, m->down_q[l], m->down_s[l], m->h, m->rb_down, m->sp_down, f),
+                                 EpiResidual{m->x, d}, s));
+                break;
+            case W4_KERNEL_O:
+                W4_HIP(launch_w4(w4_problem(m, m->o_q[l], m->o_s[l], m->o, m->rb_o, m->sp_o, qd),
+                                 EpiResidual{m->x, d}, s));
+                break;
+            case W4_KERNEL_LM_HEAD: {
+                F16Problem hp;
+                hp.w = reinterpret_cast<const u32x4 *>(m->lm_head);
+                hp.x = reinterpret_cast<const uint32_t *>(m->a);
+                hp.n_chunks = d / 8;
+                hp.n_rb = m->rb_head;
+                hp.n = c.vocab;
+                hp.out = m->logits;
+                hp.best = &m->state->best;
+                hipLaunchKernelGGL(f16_gemv_kernel, dim3(m->rb_head), dim3(kThreads), 0, s, hp);
+                W4_HIP(hipGetLastError());
+                break;
+            }
+            default:
+                return fail(W4_EINVAL, "unknown kernel kind %d", kind);
+        }
+    }
     return W4_OK;
 }

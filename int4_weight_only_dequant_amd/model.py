@@ -104,6 +104,10 @@ class DecodeModel:
     def launches_per_step(self) -> int:
         return L.lib().w4_model_launches_per_step(self._m)
 
+    def kernel_replay(self, kind: int, reps: int, stream=None) -> None:
+        """Enqueue reps launches of one step kernel (timing hook; scratch is clobbered)."""
+        L.check(L.lib().w4_model_kernel_replay(self._m, kind, reps, L._stream(stream)))
+
     def close(self) -> None:
         if getattr(self, "_m", None):
             L.lib().w4_model_destroy(self._m)
