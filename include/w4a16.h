@@ -243,13 +243,25 @@ int32_t w4_model_pos(const w4_model *m);
  * logits, and stores the greedy token (lowest index of the maximum) into
  * tokens[pos+1] unless pos+1 < n_prompt.  When pos % 16 == 0 the step first
  * appends free_list[pos/16] to the page table.
+ * The step runs as one persistent kernel (dependencies between phases are
+ * resolved on the device) or, with W4_MULTI, as one kernel per operation.
  * flags: W4_GRAPH replays the captured graph of the matching variant;
- * W4_EAGER launches the same kernels one by one.
+ * W4_EAGER launches the same kernels directly.
  * Errors: W4_ESTATE (pos mismatch), W4_ENOSPC (pos >= 16*max_pages),
  * W4_EHIP. */
-#define W4_GRAPH 0u
-#define W4_EAGER 1u
+#define W4_GRAPH 0u   /* replay the captured graph (default)                 */
+#define W4_EAGER 1u   /* launch the same kernels directly                     */
+#define W4_MULTI 2u   /* with W4_GRAPH/W4_EAGER: the one-kernel-per-operation
+                         step (143 launches) instead of the persistent one    */
 w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream);
+
+/* Synchronises the device and reports the persistent step's error word:
+ * 0 = no error; otherwise a dependency wait exceeded its spin limit (the step
+ * bailed out and its outputs are invalid). */
+w4_status w4_model_status(w4_model *m, int32_t *device_error);
+
+/* Work-groups of the persistent step (all resident at once). */
+int32_t w4_model_grid(const w4_model *m);
 
 /* Number of kernel launches one eager step makes (for the launch-count report). */
 int32_t w4_model_launches_per_step(const w4_model *m);

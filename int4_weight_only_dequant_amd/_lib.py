@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 W4_OK, W4_EINVAL, W4_EALIGN, W4_ERANGE, W4_ESTATE, W4_ENOSPC, W4_EHIP = 0, -1, -2, -3, -4, -5, -6
 W4_PERM_QKV, W4_PERM_GATE_UP = 0, 1
-W4_GRAPH, W4_EAGER = 0, 1
+W4_GRAPH, W4_EAGER, W4_MULTI = 0, 1, 2
 W4_KERNEL_GATE_UP, W4_KERNEL_DOWN, W4_KERNEL_O, W4_KERNEL_LM_HEAD = 0, 1, 2, 3
 
 _STATUS = {W4_EINVAL: "W4_EINVAL", W4_EALIGN: "W4_EALIGN", W4_ERANGE: "W4_ERANGE",
@@ -77,6 +77,8 @@ def _declare(lib):
         "decode_step": (i32, [vp, i32, u32, vp]),
         "w4_model_launches_per_step": (i32, [vp]),
         "w4_model_kernel_replay": (i32, [vp, i32, i32, vp]),
+        "w4_model_status": (i32, [vp, C.POINTER(i32)]),
+        "w4_model_grid": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

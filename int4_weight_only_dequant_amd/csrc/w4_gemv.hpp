@@ -58,6 +58,22 @@ __device__ __forceinline__ void dot8(uint32_t w, const_u32_ptr xs, float &acc1, 
     acc16 = __builtin_amdgcn_fdot2(q67, as_h2(xs[3]), acc16, false);
 }
 
+// Same as dot8 with the 4 activation pairs in VGPRs (broadcast LDS reads).
+__device__ __forceinline__ void dot8v(uint32_t w, const uint32_t (&xs)[4], float &acc1, float &acc16,
+                                      uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+    const h2 k1032 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const h2 k1152 = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    const uint32_t w8 = w >> 8;
+    const h2 q01 = as_h2((w & m_lo) | magic) - k1032;
+    const h2 q23 = as_h2((w & m_hi) | magic) - k1152;
+    const h2 q45 = as_h2((w8 & m_lo) | magic) - k1032;
+    const h2 q67 = as_h2((w8 & m_hi) | magic) - k1152;
+    acc1 = __builtin_amdgcn_fdot2(q01, as_h2(xs[0]), acc1, false);
+    acc16 = __builtin_amdgcn_fdot2(q23, as_h2(xs[1]), acc16, false);
+    acc1 = __builtin_amdgcn_fdot2(q45, as_h2(xs[2]), acc1, false);
+    acc16 = __builtin_amdgcn_fdot2(q67, as_h2(xs[3]), acc16, false);
+}
+
 // Sum over the work-group's 4 waves of one fp64 value per lane; result valid
 // in wave 0.
 __device__ __forceinline__ double wg_sum4(double v, double *lds) {

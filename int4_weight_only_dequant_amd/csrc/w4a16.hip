@@ -6,22 +6,18 @@
 
 #include <algorithm>
 #include <cmath>
+#include <string>
 #include <string.h>
 
 #include <vector>
 
 #include "w4_attn.hpp"
 #include "w4_gemv.hpp"
+#include "w4_persistent.hpp"
 
 namespace w4 {
 
 // ------------------------------------------------------------ glue kernels --
-
-struct StepState {
-    int pos;                 // position the running step works on
-    int n_prompt;            // tokens [0, n_prompt) are teacher-forced
-    unsigned long long best; // argmax key of the step's logits
-};
 
 // x = embed[tokens[pos]] as fp64, a = fp16(RMSNorm(x) * w) for the first
 // layer; clears the argmax key.  One work-group.
@@ -74,10 +70,15 @@ static hipError_t zero_counters(void *ws, int n, hipStream_t s) {
     return hipGetLastError();
 }
 
-__global__ void reset_kernel(StepState *st, int n_prompt) {
-    st->pos = 0;
-    st->n_prompt = n_prompt;
-    st->best = 0ull;
+__global__ void reset_kernel(StepState *st, int n_prompt, unsigned *ctr, int n_ctr, int *err) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_ctr; i += gridDim.x * blockDim.x) ctr[i] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->pos = 0;
+        st->n_prompt = n_prompt;
+        st->best = 0ull;
+        st->step = 0u;
+        *err = 0;
+    }
 }
 
 // -------------------------------------------------------------- launchers --
@@ -287,6 +288,7 @@ struct w4_model {
 
     // library-owned device memory (one allocation, carved)
     void *arena;
+    void *pk_arena;
     StepState *state;
     double *x;          // residual [d]
     uint16_t *a;        // normed input [d]
@@ -305,8 +307,16 @@ struct w4_model {
     int ctr_rb;               // counter slots at the start of gemv_ws
     int attn_pps, attn_split;
 
+    // persistent step
+    PKParams pk;
+    PKLayer *pk_layers;       // device array
+    PKParams *pk_dev;         // device copy of pk
+    int pk_grid;              // resident work-groups
+    int n_ctr;
+
     hipStream_t cap_stream;
-    hipGraphExec_t exec[2];   // [0] no page boundary, [1] page boundary
+    hipGraphExec_t exec[2];   // persistent step: [0] no page boundary, [1] page boundary
+    hipGraphExec_t exec_multi[2];   // kernel-per-op step, same variants
     int pos;                  // host mirror of the device position
     int n_prompt;
     int launches;
@@ -398,10 +408,21 @@ static hipError_t enqueue_step(w4_model *m, bool boundary, hipStream_t s) {
     return hipSuccess;
 }
 
-static w4_status capture(w4_model *m, bool boundary, hipGraphExec_t *out) {
+static hipError_t enqueue_persistent(w4_model *m, bool boundary, hipStream_t s) {
+    if (boundary) {
+        hipLaunchKernelGGL(page_append_kernel, dim3(1), dim3(1), 0, s, m->state, m->page_table, m->free_list);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(decode_persistent_kernel, dim3(m->pk_grid), dim3(kThreads), 0, s,
+                       static_cast<const PKParams *>(m->pk_dev));
+    return hipGetLastError();
+}
+
+static w4_status capture(w4_model *m, bool boundary, bool multi, hipGraphExec_t *out) {
     hipGraph_t g = nullptr;
     W4_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-    hipError_t e = enqueue_step(m, boundary, m->cap_stream);
+    hipError_t e = multi ? enqueue_step(m, boundary, m->cap_stream) : enqueue_persistent(m, boundary, m->cap_stream);
     hipError_t e2 = hipStreamEndCapture(m->cap_stream, &g);
     if (e != hipSuccess || e2 != hipSuccess) {
         if (g) (void)hipGraphDestroy(g);
@@ -415,11 +436,138 @@ static w4_status capture(w4_model *m, bool boundary, hipGraphExec_t *out) {
 
 static void model_free(w4_model *m) {
     if (!m) return;
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
         if (m->exec[i]) (void)hipGraphExecDestroy(m->exec[i]);
+        if (m->exec_multi[i]) (void)hipGraphExecDestroy(m->exec_multi[i]);
+    }
     if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
     if (m->arena) (void)hipFree(m->arena);
+    if (m->pk_arena) (void)hipFree(m->pk_arena);
     delete m;
+}
+
+// Largest number of work-groups that split one row block, and the checks
+// that every work-group's range fits the kernel's LDS areas.
+static bool phase_geometry(int T, int nk, int V, int P, int &slots, std::string &why) {
+    slots = 1;
+    const int n_rb = T / nk;
+    if (T < P) {
+        slots = nk;                       // one work-group per tile
+    } else {
+        for (int rb = 0; rb < n_rb; ++rb) {
+            const int first = static_cast<int>((static_cast<int64_t>(rb) * nk * P) / T);
+            const int last = static_cast<int>((static_cast<int64_t>(rb * nk + nk - 1) * P) / T);
+            slots = std::max(slots, last - first + 1);
+        }
+    }
+    for (int B = 0; B < P; ++B) {
+        const int b = static_cast<int>((static_cast<int64_t>(B) * T + P - 1) / P);
+        const int e = static_cast<int>((static_cast<int64_t>(B + 1) * T + P - 1) / P);
+        if (e <= b) continue;
+        const int staged = (e - b >= nk ? nk : e - b) * V;   // whole vector or the range's slices
+        if (staged * 2 > kStageBytes) { why = "staged input exceeds LDS"; return false; }
+        if (staged > kStageMax * kThreads) { why = "staged input exceeds the per-thread batch"; return false; }
+        if ((e - 1) / nk - b / nk + 1 > kMaxRbPerWg) { why = "range touches too many row blocks"; return false; }
+    }
+    return true;
+}
+
+static w4_status setup_persistent(w4_model *m) {
+    const w4_model_config &c = m->cfg;
+    int dev = 0, n_cu = 0, occ = 0;
+    W4_HIP(hipGetDevice(&dev));
+    W4_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+    W4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_persistent_kernel, kThreads, 0));
+    W4_CHECK(occ >= 1 && n_cu >= 1, W4_EHIP, "persistent kernel cannot be resident (occupancy %d)", occ);
+    const int P = n_cu * std::min(occ, 2);
+    const int L = c.n_layers, d = c.d_model, f = c.d_ff;
+    const int nq = d / kGroup, nf = f / kGroup, nkc = d / 32, no = c.n_q_heads * kHeadDim / kGroup;
+    const int rb_q = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim / 64, rb_d = d / 64, rb_gu = 2 * f / 64;
+    const int rb_lm = (c.vocab + 63) / 64;
+    PKParams &pk = m->pk;
+    pk = PKParams{};
+    pk.P = P;
+    std::string why;
+    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, pk.slots_q, why) &&
+                    phase_geometry(rb_d * no, no, kGroup, P, pk.slots_o, why) &&
+                    phase_geometry(rb_gu * nq, nq, kGroup, P, pk.slots_gu, why) &&
+                    phase_geometry(rb_d * nf, nf, kGroup, P, pk.slots_d, why) &&
+                    phase_geometry(rb_lm * nkc, nkc, 32, P, pk.slots_lm, why);
+    W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
+    pk.att_pps = std::max(4, (c.max_pages + 63) / 64);
+    pk.att_smax = (c.max_pages + pk.att_pps - 1) / pk.att_pps;
+    W4_CHECK(c.n_q_heads * pk.att_smax <= 4 * P, W4_EINVAL, "too many attention splits for the grid");
+
+    // library-owned persistent buffers
+    const size_t part = std::max({static_cast<size_t>(rb_q) * pk.slots_q, static_cast<size_t>(rb_d) * pk.slots_o,
+                                  static_cast<size_t>(rb_gu) * pk.slots_gu, static_cast<size_t>(rb_d) * pk.slots_d,
+                                  static_cast<size_t>(rb_lm) * pk.slots_lm}) * 64 * 8;
+    const int n_ctr = 2 + 5 * L + rb_q + rb_d + rb_gu + rb_d + rb_lm + c.n_q_heads + n_groups(rb_q) + n_groups(rb_d) +
+                      n_groups(rb_gu) + n_groups(rb_d) + n_groups(rb_lm) + n_groups(c.n_q_heads);
+    const size_t qd = static_cast<size_t>(c.n_q_heads) * kHeadDim;
+    const size_t per_layer = align256(qd * 2) * 2 + align256(static_cast<size_t>(f) * 2) +
+                             align256(static_cast<size_t>(d) * 8) * 2 + align256(static_cast<size_t>(rb_d) * 8) * 2;
+    const size_t total = align256(sizeof(PKLayer) * L) + align256(sizeof(PKParams)) +
+                         align256(static_cast<size_t>(d) * 8) + 256 + align256(part) +
+                         align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) +
+                         align256(static_cast<size_t>(n_ctr) * kCS * 4) + 256 + per_layer * L;
+    W4_HIP(hipMalloc(&m->pk_arena, total));
+    W4_HIP(hipMemset(m->pk_arena, 0, total));
+    char *b = static_cast<char *>(m->pk_arena);
+    m->pk_layers = reinterpret_cast<PKLayer *>(b); b += align256(sizeof(PKLayer) * L);
+    m->pk_dev = reinterpret_cast<PKParams *>(b); b += align256(sizeof(PKParams));
+    pk.x0 = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
+    pk.ss0 = reinterpret_cast<double *>(b); b += 256;
+    pk.partial = reinterpret_cast<double *>(b); b += align256(part);
+    pk.att_part = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4);
+    pk.ctr = reinterpret_cast<unsigned *>(b); b += align256(static_cast<size_t>(n_ctr) * kCS * 4);
+    pk.err = reinterpret_cast<int *>(b); b += 256;
+    std::vector<PKLayer> hl(L);
+    const size_t kv_layer = layer_kv_elems(m);
+    for (int l = 0; l < L; ++l) {
+        PKLayer &y = hl[l];
+        y.qkv_q = reinterpret_cast<const u32x4 *>(m->qkv_q[l]); y.qkv_s = m->qkv_s[l]; y.qkv_b = m->qkv_bias[l];
+        y.o_q = reinterpret_cast<const u32x4 *>(m->o_q[l]); y.o_s = m->o_s[l];
+        y.gu_q = reinterpret_cast<const u32x4 *>(m->gu_q[l]); y.gu_s = m->gu_s[l];
+        y.dn_q = reinterpret_cast<const u32x4 *>(m->down_q[l]); y.dn_s = m->down_s[l];
+        y.ln1 = m->ln1[l]; y.ln2 = m->ln2[l];
+        y.kc = m->k_cache + l * kv_layer; y.vc = m->v_cache + l * kv_layer;
+        y.q = reinterpret_cast<uint16_t *>(b); b += align256(qd * 2);
+        y.o = reinterpret_cast<uint16_t *>(b); b += align256(qd * 2);
+        y.h = reinterpret_cast<uint16_t *>(b); b += align256(static_cast<size_t>(f) * 2);
+        y.xo = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
+        y.xd = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
+        y.sso = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(rb_d) * 8);
+        y.ssd = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(rb_d) * 8);
+    }
+    W4_HIP(hipMemcpy(m->pk_layers, hl.data(), sizeof(PKLayer) * L, hipMemcpyHostToDevice));
+    pk.layers = m->pk_layers;
+    pk.n_layers = L; pk.d = d; pk.f = f; pk.n_qh = c.n_q_heads; pk.n_kvh = c.n_kv_heads; pk.vocab = c.vocab;
+    pk.embed = m->embed; pk.lnf = m->lnf; pk.lm = reinterpret_cast<const u32x4 *>(m->lm_head);
+    pk.page_table = m->page_table; pk.tokens = m->tokens; pk.logits = m->logits;
+    pk.rope = m->rope;
+    pk.st = m->state;
+    pk.att_scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(double(kHeadDim)));
+    pk.eps = static_cast<double>(c.eps);
+    int o = 2;
+    pk.c_layer = o; o += 5 * L;
+    pk.c_arr_q = o; o += rb_q;
+    pk.c_arr_o = o; o += rb_d;
+    pk.c_arr_gu = o; o += rb_gu;
+    pk.c_arr_d = o; o += rb_d;
+    pk.c_arr_lm = o; o += rb_lm;
+    pk.c_arr_att = o; o += c.n_q_heads;
+    pk.c_grp_q = o; o += n_groups(rb_q);
+    pk.c_grp_o = o; o += n_groups(rb_d);
+    pk.c_grp_gu = o; o += n_groups(rb_gu);
+    pk.c_grp_d = o; o += n_groups(rb_d);
+    pk.c_grp_lm = o; o += n_groups(rb_lm);
+    pk.c_grp_att = o; o += n_groups(c.n_q_heads);
+    W4_CHECK(o <= n_ctr, W4_EINVAL, "counter layout overflow");
+    m->n_ctr = o * kCS;
+    m->pk_grid = P;
+    W4_HIP(hipMemcpy(m->pk_dev, &pk, sizeof(PKParams), hipMemcpyHostToDevice));
+    return W4_OK;
 }
 
 }  // namespace w4
@@ -552,8 +700,11 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
         model_free(m);
         return fail(W4_EHIP, "model setup failed: %s", hipGetErrorString(e));
     }
-    w4_status st = capture(m, false, &m->exec[0]);
-    if (st == W4_OK) st = capture(m, true, &m->exec[1]);
+    w4_status st = setup_persistent(m);
+    if (st == W4_OK) st = capture(m, false, false, &m->exec[0]);
+    if (st == W4_OK) st = capture(m, true, false, &m->exec[1]);
+    if (st == W4_OK) st = capture(m, false, true, &m->exec_multi[0]);
+    if (st == W4_OK) st = capture(m, true, true, &m->exec_multi[1]);
     if (st != W4_OK) {
         model_free(m);
         return st;
@@ -573,7 +724,8 @@ extern "C" w4_status w4_model_reset(w4_model *m, int32_t n_prompt, void *stream)
     clear_error();
     W4_CHECK(m != nullptr, W4_ESTATE, "no model");
     W4_CHECK(n_prompt >= 1 && n_prompt <= m->cfg.max_pages * kPage, W4_EINVAL, "n_prompt=%d out of range", n_prompt);
-    hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), m->state, n_prompt);
+    hipLaunchKernelGGL(reset_kernel, dim3(64), dim3(256), 0, static_cast<hipStream_t>(stream), m->state, n_prompt,
+                       m->pk.ctr, m->n_ctr, m->pk.err);
     W4_HIP(hipGetLastError());
     m->pos = 0;
     m->n_prompt = n_prompt;
@@ -591,13 +743,14 @@ extern "C" w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void 
     W4_CHECK(pos == m->pos, W4_ESTATE, "position %d out of sequence (model is at %d)", pos, m->pos);
     W4_CHECK(pos < m->cfg.max_pages * kPage, W4_ENOSPC, "position %d beyond the KV pool (%d tokens)", pos,
              m->cfg.max_pages * kPage);
-    W4_CHECK(flags == W4_GRAPH || flags == W4_EAGER, W4_EINVAL, "unknown flags %u", flags);
+    W4_CHECK(flags <= (W4_EAGER | W4_MULTI), W4_EINVAL, "unknown flags %u", flags);
     const bool boundary = (pos % kPage) == 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (flags == W4_EAGER) {
-        W4_HIP(enqueue_step(m, boundary, s));
+    const bool eager = flags & W4_EAGER, multi = flags & W4_MULTI;
+    if (eager) {
+        W4_HIP(multi ? enqueue_step(m, boundary, s) : enqueue_persistent(m, boundary, s));
     } else {
-        W4_HIP(hipGraphLaunch(m->exec[boundary ? 1 : 0], s));
+        W4_HIP(hipGraphLaunch((multi ? m->exec_multi : m->exec)[boundary ? 1 : 0], s));
     }
     m->pos = pos + 1;
     return W4_OK;
@@ -644,3 +797,15 @@ extern "C" w4_status w4_model_kernel_replay(w4_model *m, int32_t kind, int32_t r
     }
     return W4_OK;
 }
+
+extern "C" w4_status w4_model_status(w4_model *m, int32_t *device_error) {
+    clear_error();
+    W4_CHECK(m != nullptr && device_error != nullptr, W4_ESTATE, "no model");
+    W4_HIP(hipDeviceSynchronize());
+    int v = 0;
+    W4_HIP(hipMemcpy(&v, m->pk.err, sizeof(int), hipMemcpyDeviceToHost));
+    *device_error = v;
+    return W4_OK;
+}
+
+extern "C" int32_t w4_model_grid(const w4_model *m) { return m ? m->pk_grid : 0; }

@@ -101,6 +101,15 @@ class DecodeModel:
     def step(self, flags: int = L.W4_GRAPH, stream=None) -> None:
         decode_step(self, self.pos, flags, stream)
 
+    def device_error(self) -> int:
+        """Synchronise and return the persistent step's error word (0 = ok)."""
+        v = C.c_int32()
+        L.check(L.lib().w4_model_status(self._m, C.byref(v)))
+        return v.value
+
+    def grid(self) -> int:
+        return L.lib().w4_model_grid(self._m)
+
     def launches_per_step(self) -> int:
         return L.lib().w4_model_launches_per_step(self._m)
 

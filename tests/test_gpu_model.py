@@ -50,26 +50,31 @@ def compare_with_oracle(dims, layers, glob, logits, toks, n_prompt, positions):
     return worst, mism
 
 
-def test_tiny_model_parity_graph_eager_and_pages():
+@pytest.mark.parametrize("path", ["persistent", "multi"])
+def test_tiny_model_parity_graph_eager_and_pages(path):
     dims = synth.TINY
     layers = [synth.layer_weights(dims, l, cfg=102) for l in range(dims.n_layers)]
     glob = synth.global_weights(dims, cfg=102)
     max_pages = 4
     free = synth.page_free_list(max_pages, cfg=102)
     prompt = synth.prompt_ids(dims, 20, cfg=102)
-    say("case: tiny model (2 layers) 20-token prompt + 44 steps, 4 shuffled pages")
+    extra = L.W4_MULTI if path == "multi" else 0
+    say(f"case: tiny model (2 layers) {path} path, 20-token prompt + 44 steps, 4 shuffled pages")
     model = w4.DecodeModel(dims, lambda l: layers[l], glob, free, max_pages)
     try:
+        say(f"  persistent grid {model.grid()} work-groups")
         n = 64
-        lg, tk = run_model(model, prompt, n, L.W4_GRAPH)
+        lg, tk = run_model(model, prompt, n, L.W4_GRAPH | extra)
+        assert model.device_error() == 0
         pt = model.page_table.cpu().numpy()
         assert np.array_equal(pt, free)                    # every boundary appended its page
-        le, te = run_model(model, prompt, n, L.W4_EAGER)
+        le, te = run_model(model, prompt, n, L.W4_EAGER | extra)
+        assert model.device_error() == 0
         assert np.array_equal(tk, te)
         assert np.array_equal(lg.view(np.uint32), le.view(np.uint32))   # graph == eager bitwise
         assert np.array_equal(tk[:20], prompt)
         worst, mism = compare_with_oracle(dims, layers, glob, lg, tk, 20, np.arange(n))
-        say(f"tiny: max |logit err| {worst:.3e}; token mismatches {mism}")
+        say(f"tiny {path}: max |logit err| {worst:.3e}; token mismatches {mism}")
         assert worst <= LOGIT_ATOL
         assert not mism
         # error paths
@@ -81,6 +86,28 @@ def test_tiny_model_parity_graph_eager_and_pages():
         assert e.value.status == L.W4_ENOSPC
     finally:
         model.close()
+
+
+def test_tiny_persistent_matches_multikernel():
+    """Both step implementations on the same model agree closely (different
+    summation orders, same fp16 storage points)."""
+    dims = synth.TINY
+    layers = [synth.layer_weights(dims, l, cfg=103) for l in range(dims.n_layers)]
+    glob = synth.global_weights(dims, cfg=103)
+    free = synth.page_free_list(4, cfg=103)
+    prompt = synth.prompt_ids(dims, 40, cfg=103)
+    say("case: tiny model persistent vs kernel-per-op, 40 prompt + 24 steps")
+    model = w4.DecodeModel(dims, lambda l: layers[l], glob, free, 4)
+    try:
+        la, ta = run_model(model, prompt, 64, L.W4_GRAPH)
+        lb, tb = run_model(model, prompt, 64, L.W4_GRAPH | L.W4_MULTI)
+        assert model.device_error() == 0
+    finally:
+        model.close()
+    diff = float(np.max(np.abs(la - lb)))
+    say(f"persistent vs multi: max |logit diff| {diff:.3e}")
+    assert diff <= 1e-2
+    assert np.array_equal(ta, tb)
 
 
 @pytest.mark.slow
@@ -99,6 +126,7 @@ def test_full_model_512_plus_128():
     try:
         say(f"model ready {time.time() - t0:.0f}s")
         lg, tk = run_model(model, prompt, 640, L.W4_GRAPH)
+        assert model.device_error() == 0
         pt = model.page_table.cpu().numpy()
     finally:
         model.close()
