@@ -491,6 +491,8 @@ struct PKFinLogits {
 // publish (max, sum, 128 weighted-V sums); the last split of a head merges in
 // split order and writes fp16 o.
 
+constexpr int kAttPages = 2;   // pages loaded together per wave (8 x 16 B per lane per page)
+
 __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L, int h, int sp, int n_split,
                                              int ctx, int done_idx) {
     unsigned *arr = p.ctr + (p.c_arr_att + h) * kCS;
@@ -505,43 +507,56 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
     float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    u32x4 kn[4], vn[4];
-    auto load_page = [&](int lp, u32x4 (&k)[4], u32x4 (&v)[4]) {
-        const int phys = p.page_table[lp];
-        const size_t base = (static_cast<size_t>(phys) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
+    // all loads of a chunk of pages are issued together
+    auto load_chunk = [&](int c0, u32x4 (&k)[kAttPages][4], u32x4 (&v)[kAttPages][4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            k[i] = *reinterpret_cast<const u32x4 *>(L.kc + base + i * 4 * kHeadDim);
-            v[i] = *reinterpret_cast<const u32x4 *>(L.vc + base + i * 4 * kHeadDim);
+        for (int pg = 0; pg < kAttPages; ++pg) {
+            if (c0 + pg < pe) {
+                const int phys = p.page_table[c0 + pg];
+                const size_t base = (static_cast<size_t>(phys) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    k[pg][i] = *reinterpret_cast<const u32x4 *>(L.kc + base + i * 4 * kHeadDim);
+                    v[pg][i] = *reinterpret_cast<const u32x4 *>(L.vc + base + i * 4 * kHeadDim);
+                }
+            }
         }
     };
-    if (pb < pe) load_page(pb, kn, vn);
-    for (int lp = pb; lp < pe; ++lp) {
-        u32x4 kcur[4], vcur[4];
+    u32x4 kn[kAttPages][4], vn[kAttPages][4];
+    if (pb < pe) load_chunk(pb, kn, vn);
+    for (int c0 = pb; c0 < pe; c0 += kAttPages) {
+        u32x4 kcur[kAttPages][4], vcur[kAttPages][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { kcur[i] = kn[i]; vcur[i] = vn[i]; }
-        if (lp + 1 < pe) load_page(lp + 1, kn, vn);
+        for (int pg = 0; pg < kAttPages; ++pg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float sc = 0.f;
-            sc = __builtin_amdgcn_fdot2(as_h2(qv.x), as_h2(kcur[i].x), sc, false);
-            sc = __builtin_amdgcn_fdot2(as_h2(qv.y), as_h2(kcur[i].y), sc, false);
-            sc = __builtin_amdgcn_fdot2(as_h2(qv.z), as_h2(kcur[i].z), sc, false);
-            sc = __builtin_amdgcn_fdot2(as_h2(qv.w), as_h2(kcur[i].w), sc, false);
-            sc = row16_sum(sc) * p.att_scale_log2;
-            const int tok = lp * kPage + ts + 4 * i;
-            if (tok < ctx) {
-                const float mn = fmaxf(m, sc);
-                const float corr = exp2f(m - mn), pw = exp2f(sc - mn);
-                l = l * corr + pw;
-                const h2 v01 = as_h2(vcur[i].x), v23 = as_h2(vcur[i].y), v45 = as_h2(vcur[i].z), v67 = as_h2(vcur[i].w);
-                const float vf[8] = {static_cast<float>(v01[0]), static_cast<float>(v01[1]),
-                                     static_cast<float>(v23[0]), static_cast<float>(v23[1]),
-                                     static_cast<float>(v45[0]), static_cast<float>(v45[1]),
-                                     static_cast<float>(v67[0]), static_cast<float>(v67[1])};
+            for (int i = 0; i < 4; ++i) { kcur[pg][i] = kn[pg][i]; vcur[pg][i] = vn[pg][i]; }
+        if (c0 + kAttPages < pe) load_chunk(c0 + kAttPages, kn, vn);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = acc[e] * corr + pw * vf[e];
-                m = mn;
+        for (int pg = 0; pg < kAttPages; ++pg) {
+            if (c0 + pg >= pe) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float sc = 0.f;
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.x), as_h2(kcur[pg][i].x), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.y), as_h2(kcur[pg][i].y), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.z), as_h2(kcur[pg][i].z), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.w), as_h2(kcur[pg][i].w), sc, false);
+                sc = row16_sum(sc) * p.att_scale_log2;
+                const int tok = (c0 + pg) * kPage + ts + 4 * i;
+                if (tok < ctx) {
+                    const float mn = fmaxf(m, sc);
+                    const float corr = exp2f(m - mn), pw = exp2f(sc - mn);
+                    l = l * corr + pw;
+                    const h2 v01 = as_h2(vcur[pg][i].x), v23 = as_h2(vcur[pg][i].y);
+                    const h2 v45 = as_h2(vcur[pg][i].z), v67 = as_h2(vcur[pg][i].w);
+                    const float vf[8] = {static_cast<float>(v01[0]), static_cast<float>(v01[1]),
+                                         static_cast<float>(v23[0]), static_cast<float>(v23[1]),
+                                         static_cast<float>(v45[0]), static_cast<float>(v45[1]),
+                                         static_cast<float>(v67[0]), static_cast<float>(v67[1])};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * corr + pw * vf[e];
+                    m = mn;
+                }
             }
         }
     }
@@ -570,14 +585,14 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
     if (static_cast<int>(old) != n_split - 1) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (lane == 0) store_agent(arr, 0u);
+    // merge the splits of head h in split order; each batch of 16 splits is
+    // loaded with independent loads before any is used
     const float *hb = p.att_part + static_cast<size_t>(h) * p.att_smax * 132;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, load_agent(hb + s * 132));
-    float Ls = 0.f, A0 = 0.f, A1 = 0.f;
-    for (int s0 = 0; s0 < n_split; s0 += 8) {
-        float ms[8], ls[8], a0[8], a1[8];
+    float M = -INFINITY, Ls = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int s0 = 0; s0 < n_split; s0 += 16) {
+        float ms[16], ls[16], a0[16], a1[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
             if (s0 + u < n_split) {
                 const float *pp = hb + (s0 + u) * 132;
                 ms[u] = load_agent(pp);
@@ -586,8 +601,16 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
                 a1[u] = load_agent(pp + 5 + 2 * lane);
             }
         }
+        // running rescale across batches (one batch at the usual contexts)
+        float Mb = M;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u)
+            if (s0 + u < n_split) Mb = fmaxf(Mb, ms[u]);
+        const float fr = M == -INFINITY ? 0.f : exp2f(M - Mb);
+        Ls *= fr; A0 *= fr; A1 *= fr;
+        M = Mb;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
             if (s0 + u < n_split && ms[u] != -INFINITY) {
                 const float f = exp2f(ms[u] - M);
                 Ls += ls[u] * f;
@@ -601,8 +624,6 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
     store_agent(reinterpret_cast<uint32_t *>(L.o + h * 128) + lane, pair);
     pk_complete(p, p.c_grp_att, h, p.n_qh, done_idx);
 }
-
-// -------------------------------------------------------------- kernel ----
 
 // ------------------------------------------------------ phase schedule ----
 // GEMV phases in order: for each layer QKV, O, gate+up, down; then lm_head.
@@ -794,6 +815,9 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
         if (g.kind == kPhO && att_h >= 0 && ok) {
             ok = pk_wait(p, p.c_layer + 5 * g.l + kDQkv, e1 * n_groups(rb_q));
             if (ok) {
+                // the ring holds nothing this wave still needs: clearing it
+                // lets its registers serve the attention loads
+                ring = Ring{};
                 pk_attention(p, p.layers[g.l], att_h, att_s, n_split, ctx, p.c_layer + 5 * g.l + kDAttn);
                 prefetch_phase(ring, p, g);
             }

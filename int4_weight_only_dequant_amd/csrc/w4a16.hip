@@ -494,7 +494,9 @@ static w4_status setup_persistent(w4_model *m) {
                     phase_geometry(rb_d * nf, nf, kGroup, P, pk.slots_d, why) &&
                     phase_geometry(rb_lm * nkc, nkc, 32, P, pk.slots_lm, why);
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
-    pk.att_pps = std::max(4, (c.max_pages + 63) / 64);
+    // pages per attention split: at least 2, and enough that all (head,
+    // split) items fit on half the waves
+    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 2 * P - 1) / (2 * P));
     pk.att_smax = (c.max_pages + pk.att_pps - 1) / pk.att_pps;
     W4_CHECK(c.n_q_heads * pk.att_smax <= 4 * P, W4_EINVAL, "too many attention splits for the grid");
 
