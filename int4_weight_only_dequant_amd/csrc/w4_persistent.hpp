@@ -16,21 +16,23 @@
 // * Before waiting for a phase's input, a wave issues the loads of its first
 //   four tiles of that phase into a register ring; weights do not depend on
 //   activations, so HBM keeps streaming while dependencies resolve.
-// * A phase's input vector (normalised residual, attention output or SwiGLU
-//   output) is staged per work-group in LDS as fp16 and read back with
-//   broadcast 16-byte LDS reads.  The RMSNorm is applied while staging: the scale comes
-//   from per-row-block sums of squares, summed in a fixed order.
-// * Each wave parks its per-row-block sums in LDS; at the end of the phase
-//   the work-group adds its 4 waves (fixed order) and publishes one fp64
-//   partial per row block.  A row block split across work-groups is reduced
-//   by the last one to arrive (partials in fixed slots, summed in slot
-//   order), which then
-//   runs that row block's epilogue (bias + RoPE + KV append, residual + sum of
-//   squares, SwiGLU, or logits + argmax) and bumps the phase's done counter.
-// * Cross-wave data is written with device-scope (sc1) stores.  Activation
-//   buffers are per layer, so each is written once per launch and read only
-//   after its producer signalled: plain (cached) loads cannot see stale lines,
-//   because each launch starts with invalidated caches.
+// * Split-K sums of the decoder GEMVs are combined with 64-bit integer atomic
+//   adds into per-row accumulators in fixed point (2^-32 units).  Integer
+//   addition is associative, so the result does not depend on arrival order
+//   (bitwise reproducible) and no work-group has to collect partials.  After
+//   its adds are acknowledged a work-group bumps one completion counter (one
+//   per group of 8 work-groups, each on its own 128-byte line).
+// * Epilogues run on the consumer side while staging the next phase's input
+//   in LDS as fp16: residual add + RMSNorm (every consumer rebuilds the whole
+//   vector; work-group 0 also stores the residual stream), SwiGLU of the
+//   gate/up rows under its down-projection tiles, bias + RoPE for attention,
+//   and the merge of the attention splits under its O-projection tiles.  So
+//   each phase boundary costs one acknowledged atomic, one counter signal and
+//   one round of loads.
+// * Accumulators and counters are double-buffered by step parity: a step
+//   uses one set and clears the other for the next step.
+// * The lm_head keeps per-row-block partials reduced by the last work-group
+//   to arrive, which also folds its logits into the step's argmax.
 // * Every wait is bounded: past a spin limit the wave records an error and
 //   every wave bails out, so the grid always drains.  The grid is sized so
 //   that all work-groups are resident at once.
@@ -45,6 +47,9 @@ constexpr int kMaxRbPerWg = 8;           // row blocks one work-group's range ma
 constexpr int kRedBytes = kMaxRbPerWg * 4 * 64 * 8;
 constexpr int kStageBytes = 18432;       // staged fp16 input per work-group
 constexpr unsigned kSpinLimit = 1u << 22;
+constexpr int kGW = 8;                   // work-groups per completion counter
+constexpr double kFix = 4294967296.0;    // accumulator units per 1.0
+constexpr double kFixInv = 1.0 / 4294967296.0;
 
 struct StepState {
     int pos;                  // position of the running step
@@ -61,9 +66,7 @@ struct PKLayer {
     const u32x4 *dn_q; const uint16_t *dn_s;
     const uint16_t *ln1; const uint16_t *ln2;
     uint16_t *kc; uint16_t *vc;            // this layer's KV pools
-    uint16_t *q; uint16_t *o; uint16_t *h; // fp16 activations written once per launch
-    double *xo; double *xd;                // residual after O / after down
-    double *sso; double *ssd;              // per-row-block sums of squares
+    double *xo; double *xd;                // residual stream after O / after down (work-group 0 writes)
 };
 
 struct PKParams {
@@ -73,31 +76,56 @@ struct PKParams {
     const int *page_table; int *tokens; float *logits;
     const double *rope;
     StepState *st;
-    double *x0; double *ss0;
+    double *x0;
     double *partial; float *att_part;
-    unsigned *ctr;
+    unsigned *ctr;             // lm_head arrival and completion counters (128-byte lines)
     int *err;
     int P;                     // work-groups (all resident)
-    int slots_q, slots_o, slots_gu, slots_d, slots_lm;  // partial slot strides per phase
+    int slots_lm;              // lm_head partial slot stride
     int att_pps, att_smax;
     float att_scale_log2;
     double eps;
-    // counter indices (each counter on its own 128-byte line): per-row-block
-    // arrivals, completion groups of 8 row blocks (or heads), per-layer done
-    int c_arr_q, c_arr_o, c_arr_gu, c_arr_d, c_arr_lm, c_arr_att, c_layer;
-    int c_grp_q, c_grp_o, c_grp_gu, c_grp_d, c_grp_lm, c_grp_att;
+    int c_arr_lm, c_grp_lm;
+    // step-parity blocks: int64 accumulators of every layer, then counters
+    char *par[2];
+    size_t par_bytes;          // bytes per block (a multiple of 16)
+    size_t acc_layer;          // accumulators per layer
+    int acc_q, acc_o, acc_gu, acc_d;   // row offsets inside a layer
+    size_t cnt_off;            // byte offset of the counters in a block
+    int n_grp;                 // completion groups of kGW work-groups
+    int cnt_layer;             // counters per layer: 4 phases x n_grp, then one per head
 };
 
 // Counters sit 128 bytes apart: atomics on one line are serialised at the
 // memory side, so unrelated counters must not share a line.
 constexpr int kCS = 32;
-constexpr int kGrp = 8;         // row blocks (or heads) per completion group
+constexpr int kGrp = 8;         // lm_head row blocks per completion group
 
-// done counters
-enum { kCEmbed = 0, kCLm = 1 };
+// done counter of the lm_head
+enum { kCLm = 1 };
 
 __host__ __device__ constexpr int n_groups(int n_units) { return (n_units + kGrp - 1) / kGrp; }
-enum { kDQkv = 0, kDAttn = 1, kDO = 2, kDGu = 3, kDDn = 4 };
+
+// GEMV phases in order: for each layer QKV, O, gate+up, down; then lm_head.
+enum { kPhQ = 0, kPhO = 1, kPhGU = 2, kPhD = 3, kPhLM = 4 };
+
+__device__ __forceinline__ long long *pk_acc(const PKParams &p, int par, int l, int off) {
+    return reinterpret_cast<long long *>(p.par[par]) + static_cast<size_t>(l) * p.acc_layer + off;
+}
+// completion counters of (layer, phase kind), one per group; per-head
+// attention counters; the embedding counter
+__device__ __forceinline__ unsigned *pk_cnt(const PKParams &p, int par, int idx) {
+    return reinterpret_cast<unsigned *>(p.par[par] + p.cnt_off) + static_cast<size_t>(idx) * kCS;
+}
+__device__ __forceinline__ unsigned *pk_grp_cnt(const PKParams &p, int par, int l, int kind) {
+    return pk_cnt(p, par, l * p.cnt_layer + kind * p.n_grp);
+}
+__device__ __forceinline__ unsigned *pk_head_cnt(const PKParams &p, int par, int l) {
+    return pk_cnt(p, par, l * p.cnt_layer + 4 * p.n_grp);
+}
+__device__ __forceinline__ unsigned *pk_embed_cnt(const PKParams &p, int par) {
+    return pk_cnt(p, par, p.n_layers * p.cnt_layer);
+}
 
 struct Range { int b, e; };
 
@@ -113,8 +141,34 @@ __device__ __forceinline__ int tile_owner(int t, int T, int P) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Bounded wait until ctr[idx] reaches target (wrap-safe).  Returns false if
+// Bounded wait (one wave) until counter c_u = base[((b + u) % nk) * kCS]
+// reaches its target for every u < n: `want`, or with want == 0 the size of
+// completion group u (kGW work-groups, fewer in the last).  Returns false if
 // any wave recorded an error or this wait exceeded the spin limit.
+__device__ __noinline__ bool pk_wait_cnt(const PKParams &p, const unsigned *base, int n, int b, int nk,
+                                         unsigned want, int code) {
+    const int lane = lane_id();
+    unsigned spins = 0;
+    for (;;) {
+        bool done = true;
+        for (int u = lane; u < n; u += 64) {
+            const unsigned target = want ? want : static_cast<unsigned>(min(kGW, p.P - u * kGW));
+            done = done && load_agent(base + static_cast<size_t>((b + u) % nk) * kCS) >= target;
+        }
+        if (__all(done)) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            return true;
+        }
+        if ((spins & 31u) == 31u && __builtin_amdgcn_readfirstlane(load_agent(p.err)) != 0) return false;
+        if (++spins > kSpinLimit) {
+            if (lane == 0) store_agent(p.err, code);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Bounded wait until ctr[idx] reaches target (wrap-safe), as above.
 __device__ __noinline__ bool pk_wait(const PKParams &p, int idx, unsigned target) {
     unsigned spins = 0;
     for (;;) {
@@ -129,7 +183,7 @@ __device__ __noinline__ bool pk_wait(const PKParams &p, int idx, unsigned target
     }
 }
 
-// Signal: this wave's prior stores are complete, then bump a counter.
+// Signal: this wave's prior stores and atomics are complete, then bump a counter.
 __device__ __forceinline__ unsigned pk_signal(unsigned *ctr) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
@@ -138,10 +192,9 @@ __device__ __forceinline__ unsigned pk_signal(unsigned *ctr) {
     return __builtin_amdgcn_readfirstlane(old);
 }
 
-// A finished unit (row block or head) bumps its group's counter; the last
-// unit of a group bumps the phase's done counter.  Returns the done counter's
-// previous value if this unit completed a group, else 0xFFFFFFFF.  So a done
-// counter receives one atomic per 8 units instead of one per unit.
+// A finished lm_head row block bumps its group's counter; the last unit of a
+// group bumps the done counter.  Returns the done counter's previous value if
+// this unit completed a group, else 0xFFFFFFFF.
 __device__ __forceinline__ unsigned pk_complete(const PKParams &p, int grp_base, int unit, int n_units,
                                                 int done_idx) {
     const int g = unit / kGrp;
@@ -159,12 +212,7 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-// RMSNorm scale sqrt(mean(x^2) + eps) from n_rb per-row-block sums of squares.
-__device__ __forceinline__ double norm_scale(const double *ss, int n_rb, int d, double eps) {
-    double v = 0.0;
-    for (int b = lane_id(); b < n_rb; b += 64) v += ss[b];
-    return sqrt(wave_sum(v) / d + eps);
-}
+__device__ __forceinline__ double fix_to_f64(long long a) { return static_cast<double>(a) * kFixInv; }
 
 // ------------------------------------------------------------- tile ring ----
 
@@ -207,17 +255,13 @@ __device__ __forceinline__ void prefetch_f16(Ring &r, const u32x4 *lm, int nkc, 
 }
 
 // ------------------------------------------------------- input staging ----
-// Tile t of the work-group range reads V consecutive input elements starting
-// at (t % nk) * V.  If the range has at least nk tiles the whole input vector
-// is staged (element k at LDS index k); otherwise only the slices of its
-// tiles (tile t at LDS index (t - rg.b) * V).  Staging is done by the whole
-// work-group, as fp16; the row-block sum area is cleared at the same time.
+// Tile t reads V consecutive input elements starting at (t % nk) * V.  A
+// normalised input is always staged whole (element k at LDS index k); other
+// inputs are staged whole if the range has at least nk tiles, otherwise as
+// the slices of its tiles (tile t at LDS index (t - rg.b) * V).  Staging is
+// done by the whole work-group, as fp16.
 
 __device__ __forceinline__ bool stage_whole(Range rg, int nk) { return rg.e - rg.b >= nk; }
-
-__device__ __forceinline__ int stage_off(Range rg, int nk, int V, int t) {
-    return (stage_whole(rg, nk) ? t % nk : t - rg.b) * V;
-}
 
 __device__ __forceinline__ void stage_begin(double *red, int n_rl) {
     for (int v = threadIdx.x; v < n_rl * 256; v += kThreads) red[v] = 0.0;
@@ -227,58 +271,134 @@ __device__ __forceinline__ void stage_begin(double *red, int n_rl) {
 // inputs sit in L2 or beyond; one round trip instead of one per element).
 constexpr int kStageMax = 16;   // elements per thread (host-checked)
 
-__device__ __forceinline__ void stage_norm(uint16_t *lds, Range rg, int nk, int V, const double *x, double r,
-                                           const uint16_t *w) {
-    const bool whole = stage_whole(rg, nk);
-    const int n = whole ? nk * V : (rg.e - rg.b) * V;
-    const double inv_r = 1.0 / r;
+// x = x_prev + acc (acc may be null), RMSNorm with weight w, whole vector to
+// LDS.  The sum of squares is taken in a fixed order (per thread in element
+// order, then wave butterflies, then waves 0..3).  If x_out is set the
+// residual x is stored there.
+__device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, int d, const double *x_prev,
+                                                 const long long *acc, const uint16_t *w, double eps,
+                                                 double *x_out) {
     double xv[kStageMax];
     uint16_t wv[kStageMax];
+    long long av[kStageMax];
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        if (k < d) {
+            xv[j] = x_prev[k];
+            wv[j] = w[k];
+            av[j] = acc ? load_agent(acc + k) : 0ll;
+        }
+    }
+    double sq = 0.0;
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        if (k < d) {
+            xv[j] += fix_to_f64(av[j]);
+            sq += xv[j] * xv[j];
+        }
+    }
+    sq = wave_sum(sq);
+    if (lane_id() == 0) wsum[wave_id()] = sq;
+    __syncthreads();
+    const double ss = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    const double inv_r = 1.0 / sqrt(ss / d + eps);
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j) {
+        const int k = threadIdx.x + j * kThreads;
+        if (k < d) {
+            if (x_out) store_agent(x_out + k, xv[j]);
+            lds[k] = f64_to_f16(xv[j] * inv_r * static_cast<double>(f16_to_f32(wv[j])));
+        }
+    }
+}
+
+// h = silu(gate) * up from the gate/up accumulators (gate row 2k, up row
+// 2k + 1 for element k), for the tiles of the range.
+__device__ __forceinline__ void stage_swiglu(uint16_t *lds, Range rg, int nk, int V, const long long *acc) {
+    const bool whole = stage_whole(rg, nk);
+    const int n = whole ? nk * V : (rg.e - rg.b) * V;
+    long long gv[kStageMax], uv[kStageMax];
 #pragma unroll
     for (int j = 0; j < kStageMax; ++j) {
         const int v = threadIdx.x + j * kThreads;
         if (v < n) {
             const int i = v / V, e = v - i * V;
             const int k = whole ? v : ((rg.b + i) % nk) * V + e;
-            xv[j] = x[k];
-            wv[j] = w[k];
+            gv[j] = load_agent(acc + 2 * k);
+            uv[j] = load_agent(acc + 2 * k + 1);
         }
     }
-#pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        const int v = threadIdx.x + j * kThreads;
-        if (v < n) lds[v] = f64_to_f16(xv[j] * inv_r * static_cast<double>(f16_to_f32(wv[j])));
-    }
-}
-
-__device__ __forceinline__ void stage_plain(uint16_t *lds, Range rg, int nk, int V, const uint16_t *src) {
-    const bool whole = stage_whole(rg, nk);
-    const int n = whole ? nk * V : (rg.e - rg.b) * V;
-    uint16_t sv[kStageMax];
 #pragma unroll
     for (int j = 0; j < kStageMax; ++j) {
         const int v = threadIdx.x + j * kThreads;
         if (v < n) {
-            const int i = v / V, e = v - i * V;
-            sv[j] = src[whole ? v : ((rg.b + i) % nk) * V + e];
+            // exp in fp32 (relative error ~1e-7, far below the fp16 rounding
+            // of h); a double exp's coefficient table would be hoisted out
+            // of the phase loop and spilled
+            const double g = fix_to_f64(gv[j]), u = fix_to_f64(uv[j]);
+            const double e = static_cast<double>(__expf(static_cast<float>(-g)));
+            lds[v] = f64_to_f16(g / (1.0 + e) * u);
         }
     }
+}
+
+// Attention output of the heads under the range's O-projection tiles (a
+// 128-element K group is one head): each wave merges one head's splits in
+// split order; lane holds dims 2 lane, 2 lane + 1.
+__device__ __forceinline__ void stage_attn(uint16_t *lds, Range rg, int nk, const float *att_part, int att_smax,
+                                           int n_split) {
+    const bool whole = stage_whole(rg, nk);
+    const int n_u = whole ? nk : rg.e - rg.b;
+    const int lane = lane_id();
+    for (int u = wave_id(); u < n_u; u += 4) {
+        const int h = whole ? u : (rg.b + u) % nk;
+        const float *hb = att_part + static_cast<size_t>(h) * att_smax * 132;
+        float M = -INFINITY, Ls = 0.f, A0 = 0.f, A1 = 0.f;
+        for (int s0 = 0; s0 < n_split; s0 += 16) {
+            float ms[16], ls[16], a0[16], a1[16];
 #pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        const int v = threadIdx.x + j * kThreads;
-        if (v < n) lds[v] = sv[j];
+            for (int q = 0; q < 16; ++q) {
+                if (s0 + q < n_split) {
+                    const float *pp = hb + (s0 + q) * 132;
+                    ms[q] = load_agent(pp);
+                    ls[q] = load_agent(pp + 1);
+                    a0[q] = load_agent(pp + 4 + 2 * lane);
+                    a1[q] = load_agent(pp + 5 + 2 * lane);
+                }
+            }
+            // running rescale across batches (one batch at the usual contexts)
+            float Mb = M;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (s0 + q < n_split) Mb = fmaxf(Mb, ms[q]);
+            const float fr = M == -INFINITY ? 0.f : exp2f(M - Mb);
+            Ls *= fr; A0 *= fr; A1 *= fr;
+            M = Mb;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                if (s0 + q < n_split && ms[q] != -INFINITY) {
+                    const float f = exp2f(ms[q] - M);
+                    Ls += ls[q] * f;
+                    A0 += a0[q] * f;
+                    A1 += a1[q] * f;
+                }
+            }
+        }
+        const float inv = 1.0f / Ls;
+        const uint32_t pair =
+            static_cast<uint32_t>(f32_to_f16(A0 * inv)) | (static_cast<uint32_t>(f32_to_f16(A1 * inv)) << 16);
+        reinterpret_cast<uint32_t *>(lds + u * 128)[lane] = pair;
     }
 }
 
 // ---------------------------------------------------- row-block reduction --
 
-// Publish this work-group's sum for row block rb (or finish it alone);
-// returns true with the full sum in `total` if this wave must run the
-// epilogue.  Called by one wave of the work-group.
-// Work-groups contributing to row block rb, and this work-group's slot.
-// With T >= P every work-group owns at least one tile, so the owners of the
-// row block's tiles are consecutive work-groups; with T < P each tile has its
-// own work-group (ranges hold at most one tile).
+// Work-groups contributing to lm_head row block rb, and this work-group's
+// slot.  With T >= P every work-group owns at least one tile, so the owners
+// of the row block's tiles are consecutive work-groups; with T < P each tile
+// has its own work-group (ranges hold at most one tile).
 __device__ __forceinline__ void rb_contrib(int rb, int nk, int T, int P, int B, int &n_contrib, int &slot) {
     const int a = rb * nk;
     if (T >= P) {
@@ -291,6 +411,9 @@ __device__ __forceinline__ void rb_contrib(int rb, int nk, int T, int P, int B, 
     }
 }
 
+// Publish this work-group's lm_head sum for row block rb (or finish it
+// alone); returns true with the full sum in `total` if this wave must run the
+// epilogue.  Called by one wave of the work-group.
 __device__ __forceinline__ bool pk_reduce(const PKParams &p, int rb, int nk, int T, int slots, double v,
                                           int arr_base, double &total) {
     unsigned *arr = p.ctr + (arr_base + rb) * kCS;
@@ -325,7 +448,7 @@ __device__ __forceinline__ bool pk_reduce(const PKParams &p, int rb, int nk, int
 // (already holding the first tiles) and refilling it; per-row-block sums are
 // parked in red[rl][wave][lane].
 __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_t *ws, int ng, Range rg,
-                                         int rb0, const uint16_t *lds, double *red) {
+                                         bool whole, int rb0, const uint16_t *lds, double *red) {
     const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u);
     const int wave = wave_id(), lane = lane_id();
     const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + 3) / 4 : 0;
@@ -344,7 +467,7 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
                     acc = 0.0;
                     cur = rl;
                 }
-                const u32x4 *xl = reinterpret_cast<const u32x4 *>(lds + stage_off(rg, ng, 128, t));
+                const u32x4 *xl = reinterpret_cast<const u32x4 *>(lds + (whole ? t % ng : i) * 128);
                 float a1 = 0.f, a16 = 0.f;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -366,7 +489,8 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
     if (cur >= 0) red[cur * 256 + wave * 64 + lane] = acc;
 }
 
-// fp16 (lm_head) tile loop of one wave: fp32 accumulation per row block.
+// fp16 (lm_head) tile loop of one wave: fp32 accumulation per row block; the
+// normalised input is staged whole.
 __device__ __forceinline__ void f16_tiles(Ring &r, const u32x4 *lm, int nkc, Range rg, int rb0,
                                           const uint16_t *lds, double *red) {
     const int wave = wave_id(), lane = lane_id();
@@ -386,7 +510,7 @@ __device__ __forceinline__ void f16_tiles(Ring &r, const u32x4 *lm, int nkc, Ran
                     acc0 = acc1 = 0.f;
                     cur = rl;
                 }
-                const u32x4 *xl = reinterpret_cast<const u32x4 *>(lds + stage_off(rg, nkc, 32, t));
+                const u32x4 *xl = reinterpret_cast<const u32x4 *>(lds + (t % nkc) * 32);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const u32x4 xv = xl[c];
@@ -402,57 +526,7 @@ __device__ __forceinline__ void f16_tiles(Ring &r, const u32x4 *lm, int nkc, Ran
     if (cur >= 0) red[cur * 256 + wave * 64 + lane] = static_cast<double>(acc0 + acc1);
 }
 
-// ----------------------------------------------------------- epilogues ----
-
-struct PKFinQKV {
-    const PKParams *p; const PKLayer *L; int pos; int phys; int n_units; int done_idx;
-    __device__ void operator()(int rb, double v) const {
-        const int lane = lane_id();
-        const int row = rb * 64 + lane;
-        const int head = row >> 7, i = (row & 127) >> 1, hi = row & 1, dim = i + 64 * hi;
-        const int logical = head * 128 + dim;
-        v += static_cast<double>(f16_to_f32(L->qkv_b[logical]));
-        const double partner = shfl_xor1(v);
-        double out = v;
-        if (head < p->n_qh + p->n_kvh) {
-            const double c = p->rope[(static_cast<size_t>(pos) * 64 + i) * 2];
-            const double s = p->rope[(static_cast<size_t>(pos) * 64 + i) * 2 + 1];
-            out = hi ? partner * s + v * c : v * c - partner * s;
-        }
-        const uint16_t h16 = f64_to_f16(out);
-        if (head < p->n_qh) {
-            store_agent(L->q + logical, h16);
-        } else {
-            const int kv = head - p->n_qh;
-            const int j = kv < p->n_kvh ? kv : kv - p->n_kvh;
-            const size_t off = ((static_cast<size_t>(phys) * p->n_kvh + j) * kPage + (pos & 15)) * kHeadDim + dim;
-            store_agent((kv < p->n_kvh ? L->kc : L->vc) + off, h16);
-        }
-        pk_complete(*p, p->c_grp_q, rb, n_units, done_idx);
-    }
-};
-
-struct PKFinResid {           // x_new = x_old + v; per-row-block sum of squares
-    const PKParams *p; const double *x_old; double *x_new; double *ss; int grp_base; int n_units; int done_idx;
-    __device__ void operator()(int rb, double v) const {
-        const int row = rb * 64 + lane_id();
-        const double xn = x_old[row] + v;
-        store_agent(x_new + row, xn);
-        const double sq = wave_sum(xn * xn);
-        if (lane_id() == 0) store_agent(ss + rb, sq);
-        pk_complete(*p, grp_base, rb, n_units, done_idx);
-    }
-};
-
-struct PKFinSwiGLU {
-    const PKParams *p; uint16_t *h; int n_units; int done_idx;
-    __device__ void operator()(int rb, double v) const {
-        const int lane = lane_id();
-        const double u = shfl_xor1(v);
-        if ((lane & 1) == 0) store_agent(h + rb * 32 + (lane >> 1), f64_to_f16(v / (1.0 + exp(-v)) * u));
-        pk_complete(*p, p->c_grp_gu, rb, n_units, done_idx);
-    }
-};
+// ------------------------------------------------------- lm_head epilogue --
 
 struct PKFinLogits {
     const PKParams *p; int n_units; int pos; unsigned epoch; unsigned target;
@@ -487,22 +561,73 @@ struct PKFinLogits {
 
 // ----------------------------------------------------------- attention ----
 // One wave per (query head, split of pages): lanes = 4 token rows x 16
-// eight-dim chunks; each 16-byte load covers 4 tokens of a page.  Splits
-// publish (max, sum, 128 weighted-V sums); the last split of a head merges in
-// split order and writes fp16 o.
+// eight-dim chunks; each 16-byte load covers 4 tokens of a page.  The query
+// (and, in the split holding the running position, that token's key and
+// value) comes straight from the QKV accumulators: bias, RoPE and the fp16
+// rounding are applied here.  One wave per kv head also writes the new key
+// and value into the cache for later steps.  Each split publishes (max, sum,
+// 128 weighted-V sums) and bumps its head's counter; the O projection merges.
 
 constexpr int kAttPages = 2;   // pages loaded together per wave (8 x 16 B per lane per page)
+// (no prefetch across chunks: at the usual contexts a split is one chunk,
+// and the registers are needed by the ring)
 
-__device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L, int h, int sp, int n_split,
-                                             int ctx, int done_idx) {
-    unsigned *arr = p.ctr + (p.c_arr_att + h) * kCS;
+// Eight dims dc*8 .. dc*8+7 of head `head` (QKV row order: dims i and i + 64
+// are rows 2i and 2i + 1 of the head), as packed fp16, with bias and, if
+// rope, the rotation of position pos.
+__device__ __forceinline__ u32x4 qkv_dims8(const PKParams &p, const long long *acc, const uint16_t *bias, int head,
+                                           int dc, int pos, bool rope) {
+    const int hi = dc >> 3, i0 = (dc * 8) & 63;
+    const long long *a = acc + head * 128 + 2 * i0;
+    long long av[8], pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        av[e] = load_agent(a + 2 * e + hi);
+        if (rope) pv[e] = load_agent(a + 2 * e + (hi ^ 1));
+    }
+    uint32_t out[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int i = i0 + e;
+        const double v = fix_to_f64(av[e]) + static_cast<double>(f16_to_f32(bias[head * 128 + i + 64 * hi]));
+        double r = v;
+        if (rope) {
+            const double partner =
+                fix_to_f64(pv[e]) + static_cast<double>(f16_to_f32(bias[head * 128 + i + 64 * (hi ^ 1)]));
+            const double c = p.rope[(static_cast<size_t>(pos) * 64 + i) * 2];
+            const double s = p.rope[(static_cast<size_t>(pos) * 64 + i) * 2 + 1];
+            r = hi ? partner * s + v * c : v * c - partner * s;
+        }
+        const uint32_t h16 = f64_to_f16(r);
+        if (e & 1) out[e >> 1] |= h16 << 16;
+        else out[e >> 1] = h16;
+    }
+    u32x4 q;
+    q.x = out[0]; q.y = out[1]; q.z = out[2]; q.w = out[3];
+    return q;
+}
+
+__device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L, const long long *acc_q,
+                                             unsigned *head_cnt, int h, int sp, int n_split, int ctx, int phys) {
     const int lane = lane_id();
     const int ts = lane >> 4, dc = lane & 15;
     const int G = p.n_qh / p.n_kvh, j = h / G;
+    const int pos = ctx - 1;
     const int n_pages = (ctx + kPage - 1) / kPage;
     const int pb = sp * p.att_pps;
     const int pe = min(pb + p.att_pps, n_pages);
-    const u32x4 qv = *reinterpret_cast<const u32x4 *>(L.q + h * 128 + dc * 8);
+    const bool has_cur = pe == n_pages;      // the split holding the running position
+    const u32x4 qv = qkv_dims8(p, acc_q, L.qkv_b, h, dc, pos, true);
+    u32x4 knew{}, vnew{};
+    if (has_cur) {
+        knew = qkv_dims8(p, acc_q, L.qkv_b, p.n_qh + j, dc, pos, true);
+        vnew = qkv_dims8(p, acc_q, L.qkv_b, p.n_qh + p.n_kvh + j, dc, pos, false);
+        if (h == j * G && ts == 0) {
+            const size_t off = ((static_cast<size_t>(phys) * p.n_kvh + j) * kPage + (pos & 15)) * kHeadDim + dc * 8;
+            *reinterpret_cast<u32x4 *>(L.kc + off) = knew;
+            *reinterpret_cast<u32x4 *>(L.vc + off) = vnew;
+        }
+    }
     const size_t slice = static_cast<size_t>(kPage) * kHeadDim;
     float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
@@ -512,8 +637,8 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
 #pragma unroll
         for (int pg = 0; pg < kAttPages; ++pg) {
             if (c0 + pg < pe) {
-                const int phys = p.page_table[c0 + pg];
-                const size_t base = (static_cast<size_t>(phys) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
+                const int ph = p.page_table[c0 + pg];
+                const size_t base = (static_cast<size_t>(ph) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     k[pg][i] = *reinterpret_cast<const u32x4 *>(L.kc + base + i * 4 * kHeadDim);
@@ -522,33 +647,30 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
             }
         }
     };
-    u32x4 kn[kAttPages][4], vn[kAttPages][4];
-    if (pb < pe) load_chunk(pb, kn, vn);
     for (int c0 = pb; c0 < pe; c0 += kAttPages) {
         u32x4 kcur[kAttPages][4], vcur[kAttPages][4];
-#pragma unroll
-        for (int pg = 0; pg < kAttPages; ++pg)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { kcur[pg][i] = kn[pg][i]; vcur[pg][i] = vn[pg][i]; }
-        if (c0 + kAttPages < pe) load_chunk(c0 + kAttPages, kn, vn);
+        load_chunk(c0, kcur, vcur);
 #pragma unroll
         for (int pg = 0; pg < kAttPages; ++pg) {
             if (c0 + pg >= pe) break;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float sc = 0.f;
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.x), as_h2(kcur[pg][i].x), sc, false);
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.y), as_h2(kcur[pg][i].y), sc, false);
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.z), as_h2(kcur[pg][i].z), sc, false);
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.w), as_h2(kcur[pg][i].w), sc, false);
-                sc = row16_sum(sc) * p.att_scale_log2;
                 const int tok = (c0 + pg) * kPage + ts + 4 * i;
+                // the running token's key and value are not in the cache yet
+                const u32x4 kk = tok == pos ? knew : kcur[pg][i];
+                const u32x4 vv = tok == pos ? vnew : vcur[pg][i];
+                float sc = 0.f;
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.x), as_h2(kk.x), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.y), as_h2(kk.y), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.z), as_h2(kk.z), sc, false);
+                sc = __builtin_amdgcn_fdot2(as_h2(qv.w), as_h2(kk.w), sc, false);
+                sc = row16_sum(sc) * p.att_scale_log2;
                 if (tok < ctx) {
                     const float mn = fmaxf(m, sc);
                     const float corr = exp2f(m - mn), pw = exp2f(sc - mn);
                     l = l * corr + pw;
-                    const h2 v01 = as_h2(vcur[pg][i].x), v23 = as_h2(vcur[pg][i].y);
-                    const h2 v45 = as_h2(vcur[pg][i].z), v67 = as_h2(vcur[pg][i].w);
+                    const h2 v01 = as_h2(vv.x), v23 = as_h2(vv.y);
+                    const h2 v45 = as_h2(vv.z), v67 = as_h2(vv.w);
                     const float vf[8] = {static_cast<float>(v01[0]), static_cast<float>(v01[1]),
                                          static_cast<float>(v23[0]), static_cast<float>(v23[1]),
                                          static_cast<float>(v45[0]), static_cast<float>(v45[1]),
@@ -581,109 +703,82 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
         store_agent(part, m);
         store_agent(part + 1, l);
     }
-    const unsigned old = pk_signal(arr);
-    if (static_cast<int>(old) != n_split - 1) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (lane == 0) store_agent(arr, 0u);
-    // merge the splits of head h in split order; each batch of 16 splits is
-    // loaded with independent loads before any is used
-    const float *hb = p.att_part + static_cast<size_t>(h) * p.att_smax * 132;
-    float M = -INFINITY, Ls = 0.f, A0 = 0.f, A1 = 0.f;
-    for (int s0 = 0; s0 < n_split; s0 += 16) {
-        float ms[16], ls[16], a0[16], a1[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            if (s0 + u < n_split) {
-                const float *pp = hb + (s0 + u) * 132;
-                ms[u] = load_agent(pp);
-                ls[u] = load_agent(pp + 1);
-                a0[u] = load_agent(pp + 4 + 2 * lane);
-                a1[u] = load_agent(pp + 5 + 2 * lane);
-            }
-        }
-        // running rescale across batches (one batch at the usual contexts)
-        float Mb = M;
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-            if (s0 + u < n_split) Mb = fmaxf(Mb, ms[u]);
-        const float fr = M == -INFINITY ? 0.f : exp2f(M - Mb);
-        Ls *= fr; A0 *= fr; A1 *= fr;
-        M = Mb;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            if (s0 + u < n_split && ms[u] != -INFINITY) {
-                const float f = exp2f(ms[u] - M);
-                Ls += ls[u] * f;
-                A0 += a0[u] * f;
-                A1 += a1[u] * f;
-            }
-        }
-    }
-    const float inv = 1.0f / Ls;
-    const uint32_t pair = static_cast<uint32_t>(f32_to_f16(A0 * inv)) | (static_cast<uint32_t>(f32_to_f16(A1 * inv)) << 16);
-    store_agent(reinterpret_cast<uint32_t *>(L.o + h * 128) + lane, pair);
-    pk_complete(p, p.c_grp_att, h, p.n_qh, done_idx);
+    pk_signal(head_cnt + h * kCS);
 }
 
 // ------------------------------------------------------ phase schedule ----
-// GEMV phases in order: for each layer QKV, O, gate+up, down; then lm_head.
-enum { kPhQ = 0, kPhO = 1, kPhGU = 2, kPhD = 3, kPhLM = 4 };
+
+enum { kStNorm = 0, kStSwiGLU = 1, kStAttn = 2 };
 
 struct PhaseDesc {
     int kind, l;
     const u32x4 *wq; const uint16_t *ws;
-    int nk, V, T, slots, n_rb;
-    int arr;                                 // arrival counter base index
-    int dep_idx; unsigned dep_target;       // counter that must reach target first
-    // staged input: normalised (x, ss, n_ss, w) or plain fp16 (src)
-    const double *x; const double *ss; int n_ss; const uint16_t *w;
-    const uint16_t *src;
+    int nk, V, T, n_rb;
+    // input dependency: counters base[((b + u) % nk) * kCS] for the units u
+    // of the range (per-tile units, dep_all: all dep_n) must reach dep_want
+    // (0: completion-group sizes)
+    const unsigned *dep; int dep_n; unsigned dep_want; bool dep_all;
+    // staging: normalised residual (x_prev + acc_in, weight w, store to
+    // x_out), SwiGLU of acc_in, or merged attention
+    int stage;
+    const double *x_prev; const long long *acc_in; const uint16_t *w; double *x_out;
+    long long *acc_out;       // this phase's accumulators
+    unsigned *done;           // this phase's completion counters
 };
 
-__device__ __forceinline__ PhaseDesc phase_desc(const PKParams &p, int ph, unsigned e1) {
+__device__ __forceinline__ PhaseDesc phase_desc(const PKParams &p, int ph, int par, int n_split) {
     PhaseDesc g{};
     const int d = p.d, nq = d / kGroup, nf = p.f / kGroup, no = p.n_qh * kHeadDim / kGroup;
     const int rb_q = (p.n_qh + 2 * p.n_kvh) * kHeadDim / 64, rb_d = d / 64, rb_gu = 2 * p.f / 64;
     const int L = p.n_layers;
+    g.dep_all = true;
+    g.dep_n = p.n_grp;
+    g.dep_want = 0;
+    g.stage = kStNorm;
     if (ph >= 4 * L) {
         g.kind = kPhLM; g.l = L - 1;
         g.nk = d / 32; g.V = 32; g.n_rb = (p.vocab + 63) / 64; g.T = g.n_rb * g.nk;
-        g.slots = p.slots_lm; g.arr = p.c_arr_lm;
-        g.dep_idx = p.c_layer + 5 * (L - 1) + kDDn; g.dep_target = e1 * n_groups(rb_d);
-        g.x = p.layers[L - 1].xd; g.ss = p.layers[L - 1].ssd; g.n_ss = rb_d; g.w = p.lnf;
+        g.dep = pk_grp_cnt(p, par, L - 1, kPhD);
+        g.x_prev = p.layers[L - 1].xo; g.acc_in = pk_acc(p, par, L - 1, p.acc_d); g.w = p.lnf;
         return g;
     }
     const int l = ph >> 2;
     const PKLayer &Ly = p.layers[l];
     g.kind = ph & 3; g.l = l; g.V = kGroup;
+    g.done = pk_grp_cnt(p, par, l, g.kind);
     switch (g.kind) {
         case kPhQ:
-            g.wq = Ly.qkv_q; g.ws = Ly.qkv_s; g.nk = nq; g.n_rb = rb_q; g.slots = p.slots_q;
-            g.arr = p.c_arr_q;
-            if (l == 0) { g.dep_idx = kCEmbed; g.dep_target = e1; g.x = p.x0; g.ss = p.ss0; g.n_ss = 1; }
-            else {
-                g.dep_idx = p.c_layer + 5 * (l - 1) + kDDn; g.dep_target = e1 * n_groups(rb_d);
-                g.x = p.layers[l - 1].xd; g.ss = p.layers[l - 1].ssd; g.n_ss = rb_d;
+            g.wq = Ly.qkv_q; g.ws = Ly.qkv_s; g.nk = nq; g.n_rb = rb_q;
+            g.acc_out = pk_acc(p, par, l, p.acc_q);
+            if (l == 0) {
+                g.dep = pk_embed_cnt(p, par); g.dep_n = 1; g.dep_want = 1;
+                g.x_prev = p.x0;
+            } else {
+                g.dep = pk_grp_cnt(p, par, l - 1, kPhD);
+                g.x_prev = p.layers[l - 1].xo; g.acc_in = pk_acc(p, par, l - 1, p.acc_d);
+                g.x_out = p.layers[l - 1].xd;
             }
             g.w = Ly.ln1;
             break;
-        case kPhO:
-            g.wq = Ly.o_q; g.ws = Ly.o_s; g.nk = no; g.n_rb = rb_d; g.slots = p.slots_o;
-            g.arr = p.c_arr_o;
-            g.dep_idx = p.c_layer + 5 * l + kDAttn; g.dep_target = e1 * n_groups(p.n_qh);
-            g.src = Ly.o;
+        case kPhO:          // a 128-element K group of the O projection is one head
+            g.wq = Ly.o_q; g.ws = Ly.o_s; g.nk = no; g.n_rb = rb_d;
+            g.acc_out = pk_acc(p, par, l, p.acc_o);
+            g.dep = pk_head_cnt(p, par, l); g.dep_n = p.n_qh; g.dep_want = static_cast<unsigned>(n_split);
+            g.dep_all = false;
+            g.stage = kStAttn;
             break;
         case kPhGU:
-            g.wq = Ly.gu_q; g.ws = Ly.gu_s; g.nk = nq; g.n_rb = rb_gu; g.slots = p.slots_gu;
-            g.arr = p.c_arr_gu;
-            g.dep_idx = p.c_layer + 5 * l + kDO; g.dep_target = e1 * n_groups(rb_d);
-            g.x = Ly.xo; g.ss = Ly.sso; g.n_ss = rb_d; g.w = Ly.ln2;
+            g.wq = Ly.gu_q; g.ws = Ly.gu_s; g.nk = nq; g.n_rb = rb_gu;
+            g.acc_out = pk_acc(p, par, l, p.acc_gu);
+            g.dep = pk_grp_cnt(p, par, l, kPhO);
+            g.x_prev = l == 0 ? p.x0 : p.layers[l - 1].xd; g.acc_in = pk_acc(p, par, l, p.acc_o);
+            g.w = Ly.ln2; g.x_out = Ly.xo;
             break;
         default:
-            g.wq = Ly.dn_q; g.ws = Ly.dn_s; g.nk = nf; g.n_rb = rb_d; g.slots = p.slots_d;
-            g.arr = p.c_arr_d;
-            g.dep_idx = p.c_layer + 5 * l + kDGu; g.dep_target = e1 * n_groups(rb_gu);
-            g.src = Ly.h;
+            g.wq = Ly.dn_q; g.ws = Ly.dn_s; g.nk = nf; g.n_rb = rb_d;
+            g.acc_out = pk_acc(p, par, l, p.acc_d);
+            g.dep = pk_grp_cnt(p, par, l, kPhGU);
+            g.stage = kStSwiGLU; g.acc_in = pk_acc(p, par, l, p.acc_gu);
             break;
     }
     g.T = g.n_rb * g.nk;
@@ -696,51 +791,36 @@ __device__ __forceinline__ void prefetch_phase(Ring &r, const PKParams &p, const
     else prefetch_w4(r, g.wq, g.ws, g.nk, rg);
 }
 
-// Epilogue of a finished row block (one wave), by phase kind.
-__device__ __noinline__ void pk_finish(const PKParams &p, const PhaseDesc &g, int rb, double v, int pos, int phys,
-                                       unsigned epoch) {
-    const PKLayer &Ly = p.layers[g.l];
-    const int dn = p.c_layer + 5 * g.l;
-    switch (g.kind) {
-        case kPhQ: {
-            PKFinQKV fin{&p, &Ly, pos, phys, g.n_rb, dn + kDQkv};
-            fin(rb, v);
-            break;
-        }
-        case kPhO: {
-            PKFinResid fin{&p, g.l == 0 ? p.x0 : p.layers[g.l - 1].xd, Ly.xo, Ly.sso, p.c_grp_o, g.n_rb, dn + kDO};
-            fin(rb, v);
-            break;
-        }
-        case kPhGU: {
-            PKFinSwiGLU fin{&p, Ly.h, g.n_rb, dn + kDGu};
-            fin(rb, v);
-            break;
-        }
-        case kPhD: {
-            PKFinResid fin{&p, Ly.xo, Ly.xd, Ly.ssd, p.c_grp_d, g.n_rb, dn + kDDn};
-            fin(rb, v);
-            break;
-        }
-        default: {
-            PKFinLogits fin{&p, g.n_rb, pos, epoch, (epoch + 1) * static_cast<unsigned>(n_groups(g.n_rb))};
-            fin(rb, v);
-            break;
-        }
-    }
+__device__ __noinline__ void pk_finish_lm(const PKParams &p, const PhaseDesc &g, int rb, double v, int pos,
+                                          unsigned epoch) {
+    PKFinLogits fin{&p, g.n_rb, pos, epoch, (epoch + 1) * static_cast<unsigned>(n_groups(g.n_rb))};
+    fin(rb, v);
 }
 
 // End of a GEMV phase: the 4 waves' parked sums are added per row block (in
-// wave order) and published; finished row blocks run their epilogue.
+// wave order).  Decoder phases add them to the accumulators and bump the
+// work-group's completion counter once every wave's adds are acknowledged;
+// the lm_head reduces per row block and runs its epilogue.
 __device__ __forceinline__ void phase_reduce(const PKParams &p, const PhaseDesc &g, const double *red, int rb0,
-                                             int n_rl, int pos, int phys, unsigned epoch) {
+                                             int n_rl, int pos, unsigned epoch) {
     __syncthreads();
     const int wave = wave_id(), lane = lane_id();
     for (int rl = wave; rl < n_rl; rl += 4) {
         const double *rr = red + rl * 256 + lane;
         const double v = ((rr[0] + rr[64]) + rr[128]) + rr[192];
-        double tot;
-        if (pk_reduce(p, rb0 + rl, g.nk, g.T, g.slots, v, g.arr, tot)) pk_finish(p, g, rb0 + rl, tot, pos, phys, epoch);
+        if (g.kind == kPhLM) {
+            double tot;
+            if (pk_reduce(p, rb0 + rl, g.nk, g.T, p.slots_lm, v, p.c_arr_lm, tot))
+                pk_finish_lm(p, g, rb0 + rl, tot, pos, epoch);
+        } else {
+            __hip_atomic_fetch_add(g.acc_out + (rb0 + rl) * 64 + lane, __double2ll_rn(v * kFix), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (g.kind != kPhLM) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave == 0) pk_signal(g.done + (blockIdx.x / kGW) * kCS);
     }
     // no trailing barrier: the next phase's LDS writes come after its own
     // work-group-wide barrier
@@ -753,6 +833,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     const PKParams &p = *pp;
     __shared__ __attribute__((aligned(16))) double s_red[kRedBytes / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_stage[kStageBytes / 2];
+    __shared__ double s_wsum[4];
     const int wave = wave_id();
     const int B = blockIdx.x;
     const int w = (B << 2) + wave;
@@ -762,12 +843,12 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     const int pos = p.st->pos;
     const unsigned epoch = p.st->step;
     const unsigned e1 = epoch + 1;
+    const int par = static_cast<int>(e1 & 1u);
     const int ctx = pos + 1;
     const int phys = p.page_table[pos >> 4];
     const int L = p.n_layers;
     const int n_pages = (ctx + kPage - 1) / kPage;
     const int n_split = (n_pages + p.att_pps - 1) / p.att_pps;
-    const int rb_q = (p.n_qh + 2 * p.n_kvh) * kHeadDim / 64;
 
     // attention item of this wave (items spread over all waves), if any
     const int n_items_max = p.n_qh * p.att_smax;
@@ -780,72 +861,78 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
         }
     }
 
-    // embedding and its sum of squares (one wave); clears the argmax key
+    Ring ring;
+    prefetch_phase(ring, p, phase_desc(p, 0, par, n_split));
+
+    // embedding (one wave); clears the argmax key
     if (w == W - 1) {
         const int d = p.d;
         const int tok = p.tokens[pos];
         const uint16_t *row = p.embed + static_cast<size_t>(tok) * d;
-        double sq = 0.0;
-        for (int i = lane; i < d; i += 64) {
-            const double v = static_cast<double>(f16_to_f32(row[i]));
-            store_agent(p.x0 + i, v);
-            sq += v * v;
-        }
-        sq = wave_sum(sq);
-        if (lane == 0) {
-            store_agent(p.ss0, sq);
-            store_agent(&p.st->best, 0ull);
-        }
-        pk_signal(p.ctr + kCEmbed * kCS);
+        for (int i = lane; i < d; i += 64) store_agent(p.x0 + i, static_cast<double>(f16_to_f32(row[i])));
+        if (lane == 0) store_agent(&p.st->best, 0ull);
+        pk_signal(pk_embed_cnt(p, par));
     }
 
-    Ring ring;
+    // clear the other parity's accumulators and counters for the next step
     {
-        const PhaseDesc g0 = phase_desc(p, 0, e1);
-        prefetch_phase(ring, p, g0);
+        u32x4 *z = reinterpret_cast<u32x4 *>(p.par[par ^ 1]);
+        const size_t n16 = p.par_bytes / 16;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (size_t i = static_cast<size_t>(B) * kThreads + threadIdx.x; i < n16; i += static_cast<size_t>(p.P) * kThreads)
+            z[i] = zero;
     }
+
     bool ok = true;
     const int n_ph = 4 * L + 1;
     for (int ph = 0; ph < n_ph; ++ph) {
-        const PhaseDesc g = phase_desc(p, ph, e1);
+        const PhaseDesc g = phase_desc(p, ph, par, n_split);
         const Range rg = wg_range(B, g.T, p.P);
         const bool has_next = ph + 1 < n_ph;
         // attention runs between a layer's QKV and O phases; its waves fill
         // their ring for O only afterwards
         if (g.kind == kPhO && att_h >= 0 && ok) {
-            ok = pk_wait(p, p.c_layer + 5 * g.l + kDQkv, e1 * n_groups(rb_q));
+            ok = pk_wait_cnt(p, pk_grp_cnt(p, par, g.l, kPhQ), p.n_grp, 0, p.n_grp, 0, 2000 + g.l);
             if (ok) {
                 // the ring holds nothing this wave still needs: clearing it
                 // lets its registers serve the attention loads
                 ring = Ring{};
-                pk_attention(p, p.layers[g.l], att_h, att_s, n_split, ctx, p.c_layer + 5 * g.l + kDAttn);
+                pk_attention(p, p.layers[g.l], pk_acc(p, par, g.l, p.acc_q), pk_head_cnt(p, par, g.l), att_h,
+                             att_s, n_split, ctx, phys);
                 prefetch_phase(ring, p, g);
             }
         }
         const bool next_after_att = has_next && ((ph + 1) & 3) == kPhO && ph + 1 < 4 * L && att_h >= 0;
         if (rg.e > rg.b) {
-            ok = ok && pk_wait(p, g.dep_idx, g.dep_target);
+            const bool whole = g.stage == kStNorm || stage_whole(rg, g.nk);
+            if (ok && wave == 0) {
+                if (g.dep_all || whole)
+                    ok = pk_wait_cnt(p, g.dep, g.dep_n, 0, g.dep_n, g.dep_want, 3000 + ph);
+                else
+                    ok = pk_wait_cnt(p, g.dep, rg.e - rg.b, rg.b, g.nk, g.dep_want, 3000 + ph);
+            }
             // a failed wait must not strand the other waves at a barrier
             if (__syncthreads_or(!ok)) { ok = false; break; }
             const int rb0 = rg.b / g.nk, n_rl = (rg.e - 1) / g.nk - rb0 + 1;
             stage_begin(s_red, n_rl);
-            if (g.src) {
-                stage_plain(s_stage, rg, g.nk, g.V, g.src);
-            } else {
-                const double r = norm_scale(g.ss, g.n_ss, p.d, p.eps);
-                stage_norm(s_stage, rg, g.nk, g.V, g.x, r, g.w);
-            }
+            if (g.stage == kStNorm)
+                stage_resid_norm(s_stage, s_wsum, p.d, g.x_prev, g.acc_in, g.w, p.eps, B == 0 ? g.x_out : nullptr);
+            else if (g.stage == kStSwiGLU)
+                stage_swiglu(s_stage, rg, g.nk, g.V, g.acc_in);
+            else
+                stage_attn(s_stage, rg, g.nk, p.att_part, p.att_smax, n_split);
             __syncthreads();
             if (g.kind == kPhLM) f16_tiles(ring, p.lm, g.nk, rg, rb0, s_stage, s_red);
-            else w4_tiles(ring, g.wq, g.ws, g.nk, rg, rb0, s_stage, s_red);
-            // publish and finish row blocks before issuing the next phase's
-            // loads: vmcnt is in order, so any wait on the partial store or
-            // the arrival atomic would otherwise also wait for the prefetch
-            phase_reduce(p, g, s_red, rb0, n_rl, pos, phys, epoch);
-            if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, e1));
+            else w4_tiles(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
+            // publish before issuing the next phase's loads: vmcnt is in
+            // order, so waiting for the adds would also wait for the prefetch
+            phase_reduce(p, g, s_red, rb0, n_rl, pos, epoch);
+            if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, par, n_split));
         } else {
             if (!ok) break;
-            if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, e1));
+            // no tiles here: the work-group still counts as done
+            if (g.kind != kPhLM && wave == 0) pk_signal(g.done + (B / kGW) * kCS);
+            if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, par, n_split));
         }
     }
 }

@@ -488,41 +488,50 @@ static w4_status setup_persistent(w4_model *m) {
     pk = PKParams{};
     pk.P = P;
     std::string why;
-    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, pk.slots_q, why) &&
-                    phase_geometry(rb_d * no, no, kGroup, P, pk.slots_o, why) &&
-                    phase_geometry(rb_gu * nq, nq, kGroup, P, pk.slots_gu, why) &&
-                    phase_geometry(rb_d * nf, nf, kGroup, P, pk.slots_d, why) &&
+    int slots_unused = 0;
+    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, slots_unused, why) &&
+                    phase_geometry(rb_d * no, no, kGroup, P, slots_unused, why) &&
+                    phase_geometry(rb_gu * nq, nq, kGroup, P, slots_unused, why) &&
+                    phase_geometry(rb_d * nf, nf, kGroup, P, slots_unused, why) &&
                     phase_geometry(rb_lm * nkc, nkc, 32, P, pk.slots_lm, why);
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
-    // pages per attention split: at least 2, and enough that all (head,
-    // split) items fit on half the waves
-    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 2 * P - 1) / (2 * P));
+    // normalised inputs are staged whole, one element per thread and batch slot
+    W4_CHECK(d <= kStageMax * kThreads && d * 2 <= kStageBytes, W4_EINVAL, "d_model too large for the persistent step");
+    // pages per attention split: at least 2, and enough that every (head,
+    // split) item has a wave of its own
+    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 4 * P - 1) / (4 * P));
     pk.att_smax = (c.max_pages + pk.att_pps - 1) / pk.att_pps;
     W4_CHECK(c.n_q_heads * pk.att_smax <= 4 * P, W4_EINVAL, "too many attention splits for the grid");
 
+    // step-parity blocks: accumulators of every layer, then counters (per
+    // layer: 4 phases x groups, one per head; then the embedding counter)
+    pk.n_grp = (P + kGW - 1) / kGW;
+    pk.cnt_layer = 4 * pk.n_grp + c.n_q_heads;
+    pk.acc_q = 0;
+    pk.acc_o = pk.acc_q + rb_q * 64;
+    pk.acc_gu = pk.acc_o + d;
+    pk.acc_d = pk.acc_gu + 2 * f;
+    pk.acc_layer = static_cast<size_t>(pk.acc_d + d);
+    pk.cnt_off = align256(pk.acc_layer * L * 8);
+    pk.par_bytes = pk.cnt_off + align256((static_cast<size_t>(L) * pk.cnt_layer + 1) * kCS * 4);
+
     // library-owned persistent buffers
-    const size_t part = std::max({static_cast<size_t>(rb_q) * pk.slots_q, static_cast<size_t>(rb_d) * pk.slots_o,
-                                  static_cast<size_t>(rb_gu) * pk.slots_gu, static_cast<size_t>(rb_d) * pk.slots_d,
-                                  static_cast<size_t>(rb_lm) * pk.slots_lm}) * 64 * 8;
-    const int n_ctr = 2 + 5 * L + rb_q + rb_d + rb_gu + rb_d + rb_lm + c.n_q_heads + n_groups(rb_q) + n_groups(rb_d) +
-                      n_groups(rb_gu) + n_groups(rb_d) + n_groups(rb_lm) + n_groups(c.n_q_heads);
-    const size_t qd = static_cast<size_t>(c.n_q_heads) * kHeadDim;
-    const size_t per_layer = align256(qd * 2) * 2 + align256(static_cast<size_t>(f) * 2) +
-                             align256(static_cast<size_t>(d) * 8) * 2 + align256(static_cast<size_t>(rb_d) * 8) * 2;
+    const size_t part = static_cast<size_t>(rb_lm) * pk.slots_lm * 64 * 8;
+    const int n_ctr = 2 + rb_lm + n_groups(rb_lm);
+    const size_t ctr_bytes = align256(static_cast<size_t>(n_ctr) * kCS * 4);
+    const size_t per_layer = align256(static_cast<size_t>(d) * 8) * 2;
     const size_t total = align256(sizeof(PKLayer) * L) + align256(sizeof(PKParams)) +
-                         align256(static_cast<size_t>(d) * 8) + 256 + align256(part) +
-                         align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) +
-                         align256(static_cast<size_t>(n_ctr) * kCS * 4) + 256 + per_layer * L;
+                         align256(static_cast<size_t>(d) * 8) + align256(part) +
+                         align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) + 256 + per_layer * L +
+                         ctr_bytes + 2 * pk.par_bytes;
     W4_HIP(hipMalloc(&m->pk_arena, total));
     W4_HIP(hipMemset(m->pk_arena, 0, total));
     char *b = static_cast<char *>(m->pk_arena);
     m->pk_layers = reinterpret_cast<PKLayer *>(b); b += align256(sizeof(PKLayer) * L);
     m->pk_dev = reinterpret_cast<PKParams *>(b); b += align256(sizeof(PKParams));
     pk.x0 = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
-    pk.ss0 = reinterpret_cast<double *>(b); b += 256;
     pk.partial = reinterpret_cast<double *>(b); b += align256(part);
     pk.att_part = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4);
-    pk.ctr = reinterpret_cast<unsigned *>(b); b += align256(static_cast<size_t>(n_ctr) * kCS * 4);
     pk.err = reinterpret_cast<int *>(b); b += 256;
     std::vector<PKLayer> hl(L);
     const size_t kv_layer = layer_kv_elems(m);
@@ -534,14 +543,13 @@ static w4_status setup_persistent(w4_model *m) {
         y.dn_q = reinterpret_cast<const u32x4 *>(m->down_q[l]); y.dn_s = m->down_s[l];
         y.ln1 = m->ln1[l]; y.ln2 = m->ln2[l];
         y.kc = m->k_cache + l * kv_layer; y.vc = m->v_cache + l * kv_layer;
-        y.q = reinterpret_cast<uint16_t *>(b); b += align256(qd * 2);
-        y.o = reinterpret_cast<uint16_t *>(b); b += align256(qd * 2);
-        y.h = reinterpret_cast<uint16_t *>(b); b += align256(static_cast<size_t>(f) * 2);
         y.xo = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
         y.xd = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
-        y.sso = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(rb_d) * 8);
-        y.ssd = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(rb_d) * 8);
     }
+    // counters and both parity blocks last and contiguous: reset clears them in one sweep
+    pk.ctr = reinterpret_cast<unsigned *>(b); b += ctr_bytes;
+    pk.par[0] = b; b += pk.par_bytes;
+    pk.par[1] = b; b += pk.par_bytes;
     W4_HIP(hipMemcpy(m->pk_layers, hl.data(), sizeof(PKLayer) * L, hipMemcpyHostToDevice));
     pk.layers = m->pk_layers;
     pk.n_layers = L; pk.d = d; pk.f = f; pk.n_qh = c.n_q_heads; pk.n_kvh = c.n_kv_heads; pk.vocab = c.vocab;
@@ -551,22 +559,11 @@ static w4_status setup_persistent(w4_model *m) {
     pk.st = m->state;
     pk.att_scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(double(kHeadDim)));
     pk.eps = static_cast<double>(c.eps);
-    int o = 2;
-    pk.c_layer = o; o += 5 * L;
-    pk.c_arr_q = o; o += rb_q;
-    pk.c_arr_o = o; o += rb_d;
-    pk.c_arr_gu = o; o += rb_gu;
-    pk.c_arr_d = o; o += rb_d;
-    pk.c_arr_lm = o; o += rb_lm;
-    pk.c_arr_att = o; o += c.n_q_heads;
-    pk.c_grp_q = o; o += n_groups(rb_q);
-    pk.c_grp_o = o; o += n_groups(rb_d);
-    pk.c_grp_gu = o; o += n_groups(rb_gu);
-    pk.c_grp_d = o; o += n_groups(rb_d);
-    pk.c_grp_lm = o; o += n_groups(rb_lm);
-    pk.c_grp_att = o; o += n_groups(c.n_q_heads);
-    W4_CHECK(o <= n_ctr, W4_EINVAL, "counter layout overflow");
-    m->n_ctr = o * kCS;
+    pk.c_arr_lm = 2;
+    pk.c_grp_lm = 2 + rb_lm;
+    const size_t zero_bytes = ctr_bytes + 2 * pk.par_bytes;
+    W4_CHECK(zero_bytes / 4 <= static_cast<size_t>(INT32_MAX), W4_EINVAL, "counter region too large");
+    m->n_ctr = static_cast<int>(zero_bytes / 4);
     m->pk_grid = P;
     W4_HIP(hipMemcpy(m->pk_dev, &pk, sizeof(PKParams), hipMemcpyHostToDevice));
     return W4_OK;
