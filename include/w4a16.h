@@ -200,17 +200,18 @@ w4_status w4_model_row_perm(int32_t kind, const w4_model_config *cfg,
 typedef struct {
     const uint8_t *const *qkv_q;      /* packed, W4_PERM_QKV order          */
     const uint16_t *const *qkv_s;
-    const uint16_t *const *qkv_bias;  /* fp16 [qkv rows], logical order     */
+    const uint16_t *const *qkv_bias;  /* fp16 [qkv rows], logical order,
+                                         16-byte aligned                    */
     const uint8_t *const *o_q;        /* packed, identity order             */
     const uint16_t *const *o_s;
     const uint8_t *const *gu_q;       /* packed, W4_PERM_GATE_UP order      */
     const uint16_t *const *gu_s;
     const uint8_t *const *down_q;     /* packed, identity order             */
     const uint16_t *const *down_s;
-    const uint16_t *const *ln1;       /* fp16 [d_model]                     */
-    const uint16_t *const *ln2;       /* fp16 [d_model]                     */
+    const uint16_t *const *ln1;       /* fp16 [d_model], 4-byte aligned     */
+    const uint16_t *const *ln2;       /* fp16 [d_model], 4-byte aligned     */
     const uint16_t *embed;            /* fp16 [vocab][d_model], row-major   */
-    const uint16_t *lnf;              /* fp16 [d_model]                     */
+    const uint16_t *lnf;              /* fp16 [d_model], 4-byte aligned     */
     const uint16_t *lm_head;          /* w4_pack_f16_matrix of [vocab][d]   */
     uint16_t *k_cache;                /* fp16 [n_layers][max_pages][n_kv][16][128] */
     uint16_t *v_cache;                /* same shape                         */

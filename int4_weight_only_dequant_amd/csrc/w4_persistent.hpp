@@ -31,6 +31,13 @@
 //   one round of loads.
 // * Accumulators and counters are double-buffered by step parity: a step
 //   uses one set and clears the other for the next step.
+// * Data read across work-groups (accumulators, attention partials, the
+//   residual stream) is read with plain loads, so the work-groups of an XCD
+//   share one L2 copy: every such buffer is read only after its producers
+//   have signalled, and is written at most once per launch (attention
+//   partials are per layer), so no L2 can hold a stale line; each launch
+//   starts with invalidated caches.  Counters are polled with device-scope
+//   loads.
 // * The lm_head keeps per-row-block partials reduced by the last work-group
 //   to arrive, which also folds its logits into the step's argmax.
 // * Every wait is bounded: past a spin limit the wave records an error and
@@ -77,7 +84,9 @@ struct PKParams {
     const double *rope;
     StepState *st;
     double *x0;
-    double *partial; float *att_part;
+    double *partial;
+    float *att_part;           // attention split partials, per layer
+    size_t att_layer;          // floats per layer of att_part
     unsigned *ctr;             // lm_head arrival and completion counters (128-byte lines)
     int *err;
     int P;                     // work-groups (all resident)
@@ -140,6 +149,16 @@ __device__ __forceinline__ int tile_owner(int t, int T, int P) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// The thread index behind an empty asm: values derived from it inside the
+// phase loop are recomputed where they are used instead of being hoisted out
+// of the loop, where they would be spilled (and every reload from scratch
+// waits for all outstanding loads, the weight prefetch included).
+__device__ __forceinline__ int opaque_tid() {
+    int t = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(t));
+    return t;
+}
 
 // Bounded wait (one wave) until counter c_u = base[((b + u) % nk) * kCS]
 // reaches its target for every u < n: `want`, or with want == 0 the size of
@@ -272,74 +291,99 @@ __device__ __forceinline__ void stage_begin(double *red, int n_rl) {
 constexpr int kStageMax = 16;   // elements per thread (host-checked)
 
 // x = x_prev + acc (acc may be null), RMSNorm with weight w, whole vector to
-// LDS.  The sum of squares is taken in a fixed order (per thread in element
-// order, then wave butterflies, then waves 0..3).  If x_out is set the
-// residual x is stored there.
+// LDS.  Each thread takes element pairs (2-byte global loads are slow: the
+// fp16 weights are read two at a time).  The sum of squares is taken in a
+// fixed order (per thread in pair order, then wave butterflies, then waves
+// 0..3).  If x_out is set the residual x is stored there.
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+constexpr int kPairMax = kStageMax / 2;
+
 __device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, int d, const double *x_prev,
                                                  const long long *acc, const uint16_t *w, double eps,
                                                  double *x_out) {
-    double xv[kStageMax];
-    uint16_t wv[kStageMax];
-    long long av[kStageMax];
+    const int np = d / 2;
+    const int tid = opaque_tid();
+    f64x2 xv[kPairMax];
+    i64x2 av[kPairMax];
+    uint32_t wv[kPairMax];
 #pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        const int k = threadIdx.x + j * kThreads;
-        if (k < d) {
-            xv[j] = x_prev[k];
-            wv[j] = w[k];
-            av[j] = acc ? load_agent(acc + k) : 0ll;
+    for (int j = 0; j < kPairMax; ++j) {
+        const int q = tid + j * kThreads;
+        if (q < np) {
+            xv[j] = reinterpret_cast<const f64x2 *>(x_prev)[q];
+            wv[j] = reinterpret_cast<const uint32_t *>(w)[q];
+            if (acc) av[j] = reinterpret_cast<const i64x2 *>(acc)[q];
+            else av[j] = i64x2{0, 0};
         }
     }
     double sq = 0.0;
 #pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        const int k = threadIdx.x + j * kThreads;
-        if (k < d) {
-            xv[j] += fix_to_f64(av[j]);
-            sq += xv[j] * xv[j];
+    for (int j = 0; j < kPairMax; ++j) {
+        const int q = tid + j * kThreads;
+        if (q < np) {
+            xv[j].x += fix_to_f64(av[j].x);
+            xv[j].y += fix_to_f64(av[j].y);
+            sq += xv[j].x * xv[j].x;
+            sq += xv[j].y * xv[j].y;
         }
     }
     sq = wave_sum(sq);
     if (lane_id() == 0) wsum[wave_id()] = sq;
     __syncthreads();
     const double ss = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-    const double inv_r = 1.0 / sqrt(ss / d + eps);
+    // the scaling itself runs in fp32: its rounding (a few 2^-24) sits far
+    // below the fp16 rounding of the result
+    const float inv_r = static_cast<float>(1.0 / sqrt(ss / d + eps));
 #pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        const int k = threadIdx.x + j * kThreads;
-        if (k < d) {
-            if (x_out) store_agent(x_out + k, xv[j]);
-            lds[k] = f64_to_f16(xv[j] * inv_r * static_cast<double>(f16_to_f32(wv[j])));
+    for (int j = 0; j < kPairMax; ++j) {
+        const int q = tid + j * kThreads;
+        if (q < np) {
+            if (x_out) {   // device-scope stores: read by other XCDs after the next signal
+                store_agent(x_out + 2 * q, xv[j].x);
+                store_agent(x_out + 2 * q + 1, xv[j].y);
+            }
+            const uint32_t lo = f32_to_f16(static_cast<float>(xv[j].x) * inv_r * f16_to_f32(wv[j] & 0xFFFFu));
+            const uint32_t hi = f32_to_f16(static_cast<float>(xv[j].y) * inv_r * f16_to_f32(wv[j] >> 16));
+            reinterpret_cast<uint32_t *>(lds)[q] = lo | (hi << 16);
         }
     }
 }
 
 // h = silu(gate) * up from the gate/up accumulators (gate row 2k, up row
-// 2k + 1 for element k), for the tiles of the range.
+// 2k + 1 for element k; one 16-byte load per element), for the tiles of the
+// range; element pairs per thread so LDS takes 4-byte writes.
 __device__ __forceinline__ void stage_swiglu(uint16_t *lds, Range rg, int nk, int V, const long long *acc) {
     const bool whole = stage_whole(rg, nk);
     const int n = whole ? nk * V : (rg.e - rg.b) * V;
-    long long gv[kStageMax], uv[kStageMax];
+    const int tid = opaque_tid();
+    i64x2 a0[kPairMax], a1[kPairMax];
 #pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        const int v = threadIdx.x + j * kThreads;
+    for (int j = 0; j < kPairMax; ++j) {
+        const int v = 2 * (tid + j * kThreads);
         if (v < n) {
-            const int i = v / V, e = v - i * V;
+            const int i = v / V, e = v - i * V;            // V is even: the pair stays in one tile
             const int k = whole ? v : ((rg.b + i) % nk) * V + e;
-            gv[j] = load_agent(acc + 2 * k);
-            uv[j] = load_agent(acc + 2 * k + 1);
+            a0[j] = reinterpret_cast<const i64x2 *>(acc)[k];
+            a1[j] = reinterpret_cast<const i64x2 *>(acc)[k + 1];
         }
     }
 #pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        const int v = threadIdx.x + j * kThreads;
+    for (int j = 0; j < kPairMax; ++j) {
+        const int v = 2 * (tid + j * kThreads);
         if (v < n) {
             // exp in fp32 (relative error ~1e-7, far below the fp16 rounding
             // of h); a double exp's coefficient table would be hoisted out
             // of the phase loop and spilled
-            const double g = fix_to_f64(gv[j]), u = fix_to_f64(uv[j]);
-            const double e = static_cast<double>(__expf(static_cast<float>(-g)));
-            lds[v] = f64_to_f16(g / (1.0 + e) * u);
+            uint32_t h2v[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const i64x2 a = u ? a1[j] : a0[j];
+                const double g = fix_to_f64(a.x), up = fix_to_f64(a.y);
+                const double ex = static_cast<double>(__expf(static_cast<float>(-g)));
+                h2v[u] = f64_to_f16(g / (1.0 + ex) * up);
+            }
+            reinterpret_cast<uint32_t *>(lds)[v >> 1] = h2v[0] | (h2v[1] << 16);
         }
     }
 }
@@ -351,7 +395,7 @@ __device__ __forceinline__ void stage_attn(uint16_t *lds, Range rg, int nk, cons
                                            int n_split) {
     const bool whole = stage_whole(rg, nk);
     const int n_u = whole ? nk : rg.e - rg.b;
-    const int lane = lane_id();
+    const int lane = opaque_tid() & 63;
     for (int u = wave_id(); u < n_u; u += 4) {
         const int h = whole ? u : (rg.b + u) % nk;
         const float *hb = att_part + static_cast<size_t>(h) * att_smax * 132;
@@ -362,10 +406,12 @@ __device__ __forceinline__ void stage_attn(uint16_t *lds, Range rg, int nk, cons
             for (int q = 0; q < 16; ++q) {
                 if (s0 + q < n_split) {
                     const float *pp = hb + (s0 + q) * 132;
-                    ms[q] = load_agent(pp);
-                    ls[q] = load_agent(pp + 1);
-                    a0[q] = load_agent(pp + 4 + 2 * lane);
-                    a1[q] = load_agent(pp + 5 + 2 * lane);
+                    const float2 ml = *reinterpret_cast<const float2 *>(pp);
+                    const float2 aa = *reinterpret_cast<const float2 *>(pp + 4 + 2 * lane);
+                    ms[q] = ml.x;
+                    ls[q] = ml.y;
+                    a0[q] = aa.x;
+                    a1[q] = aa.y;
                 }
             }
             // running rescale across batches (one batch at the usual contexts)
@@ -560,43 +606,53 @@ struct PKFinLogits {
 };
 
 // ----------------------------------------------------------- attention ----
-// One wave per (query head, split of pages): lanes = 4 token rows x 16
-// eight-dim chunks; each 16-byte load covers 4 tokens of a page.  The query
-// (and, in the split holding the running position, that token's key and
-// value) comes straight from the QKV accumulators: bias, RoPE and the fp16
-// rounding are applied here.  One wave per kv head also writes the new key
-// and value into the cache for later steps.  Each split publishes (max, sum,
-// 128 weighted-V sums) and bumps its head's counter; the O projection merges.
+// A work-group per (query head, chunk of 4 x pps pages); its wave v takes
+// pages [chunk * 4 pps + v pps, + pps).  In a wave, lanes = 4 token rows x 16
+// eight-dim chunks; each 16-byte load covers 4 tokens of a page.  The K/V
+// pages are requested before waiting for the QKV phase (they hold earlier
+// tokens only).  The query (and, for the running position, that token's key
+// and value) comes straight from the QKV accumulators: bias, RoPE and the
+// fp16 rounding are applied here, and the wave holding the running position
+// of the first query head of a kv group writes the new key and value into
+// the cache for later steps.  The 4 waves' online-softmax states are merged
+// through LDS in wave order; the chunk's (max, sum, 128 weighted-V sums) is
+// published and the head's counter bumped; the O projection merges chunks.
 
 constexpr int kAttPages = 2;   // pages loaded together per wave (8 x 16 B per lane per page)
-// (no prefetch across chunks: at the usual contexts a split is one chunk,
-// and the registers are needed by the ring)
 
 // Eight dims dc*8 .. dc*8+7 of head `head` (QKV row order: dims i and i + 64
 // are rows 2i and 2i + 1 of the head), as packed fp16, with bias and, if
-// rope, the rotation of position pos.
+// rope, the rotation of position pos.  All reads are 16-byte loads: the 16
+// accumulator rows 2 i0 .. 2 i0 + 15, the 8 biases of each half and the 8
+// (cos, sin) pairs.
 __device__ __forceinline__ u32x4 qkv_dims8(const PKParams &p, const long long *acc, const uint16_t *bias, int head,
                                            int dc, int pos, bool rope) {
     const int hi = dc >> 3, i0 = (dc * 8) & 63;
-    const long long *a = acc + head * 128 + 2 * i0;
-    long long av[8], pv[8];
+    const i64x2 *a = reinterpret_cast<const i64x2 *>(acc + head * 128 + 2 * i0);
+    i64x2 av[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        av[e] = load_agent(a + 2 * e + hi);
-        if (rope) pv[e] = load_agent(a + 2 * e + (hi ^ 1));
+    for (int e = 0; e < 8; ++e) av[e] = a[e];
+    const u32x4 bo = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * hi + i0);
+    const u32x4 bp = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * (hi ^ 1) + i0);
+    f64x2 cs[8];
+    if (rope) {
+        const f64x2 *rp = reinterpret_cast<const f64x2 *>(p.rope + (static_cast<size_t>(pos) * 64 + i0) * 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] = rp[e];
     }
+    const uint32_t bw[4] = {bo.x, bo.y, bo.z, bo.w}, pw[4] = {bp.x, bp.y, bp.z, bp.w};
     uint32_t out[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int i = i0 + e;
-        const double v = fix_to_f64(av[e]) + static_cast<double>(f16_to_f32(bias[head * 128 + i + 64 * hi]));
+        const uint16_t b16 = static_cast<uint16_t>(bw[e >> 1] >> (16 * (e & 1)));
+        const uint16_t p16 = static_cast<uint16_t>(pw[e >> 1] >> (16 * (e & 1)));
+        const long long own = hi ? av[e].y : av[e].x, other = hi ? av[e].x : av[e].y;
+        const double v = fix_to_f64(own) + static_cast<double>(f16_to_f32(b16));
         double r = v;
         if (rope) {
-            const double partner =
-                fix_to_f64(pv[e]) + static_cast<double>(f16_to_f32(bias[head * 128 + i + 64 * (hi ^ 1)]));
-            const double c = p.rope[(static_cast<size_t>(pos) * 64 + i) * 2];
-            const double s = p.rope[(static_cast<size_t>(pos) * 64 + i) * 2 + 1];
-            r = hi ? partner * s + v * c : v * c - partner * s;
+            const double partner = fix_to_f64(other) + static_cast<double>(f16_to_f32(p16));
+            const double c = cs[e].x, sn = cs[e].y;
+            r = hi ? partner * sn + v * c : v * c - partner * sn;
         }
         const uint32_t h16 = f64_to_f16(r);
         if (e & 1) out[e >> 1] |= h16 << 16;
@@ -607,16 +663,42 @@ __device__ __forceinline__ u32x4 qkv_dims8(const PKParams &p, const long long *a
     return q;
 }
 
-__device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L, const long long *acc_q,
-                                             unsigned *head_cnt, int h, int sp, int n_split, int ctx, int phys) {
-    const int lane = lane_id();
+// K and V of pages [c0, min(c0 + kAttPages, pe)) for this lane
+__device__ __forceinline__ void att_load(const PKParams &p, const PKLayer &L, int j, int c0, int pe, int ts, int dc,
+                                         u32x4 (&k)[kAttPages][4], u32x4 (&v)[kAttPages][4]) {
+    const size_t slice = static_cast<size_t>(kPage) * kHeadDim;
+#pragma unroll
+    for (int pg = 0; pg < kAttPages; ++pg) {
+        if (c0 + pg < pe) {
+            const int ph = p.page_table[c0 + pg];
+            const size_t base = (static_cast<size_t>(ph) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                k[pg][i] = *reinterpret_cast<const u32x4 *>(L.kc + base + i * 4 * kHeadDim);
+                v[pg][i] = *reinterpret_cast<const u32x4 *>(L.vc + base + i * 4 * kHeadDim);
+            }
+        }
+    }
+}
+
+// Returns false if the wait for the QKV phase failed (all waves agree).
+__device__ __forceinline__ bool pk_attention(const PKParams &p, const PKLayer &L, const unsigned *q_done,
+                                             const long long *acc_q, float *att_part, unsigned *head_cnt, int h,
+                                             int c, int ctx, int phys, float *s_att, int code) {
+    const int lane = opaque_tid() & 63, wave = wave_id();
     const int ts = lane >> 4, dc = lane & 15;
     const int G = p.n_qh / p.n_kvh, j = h / G;
     const int pos = ctx - 1;
     const int n_pages = (ctx + kPage - 1) / kPage;
-    const int pb = sp * p.att_pps;
+    const int pb = (c * 4 + wave) * p.att_pps;
     const int pe = min(pb + p.att_pps, n_pages);
-    const bool has_cur = pe == n_pages;      // the split holding the running position
+    u32x4 kc[kAttPages][4], vc[kAttPages][4];
+    if (pb < pe) att_load(p, L, j, pb, pe, ts, dc, kc, vc);
+    bool ok = true;
+    if (wave == 0) ok = pk_wait_cnt(p, q_done, p.n_grp, 0, p.n_grp, 0, code);
+    if (__syncthreads_or(!ok)) return false;
+
+    const bool has_cur = pb < pe && pe == n_pages;   // this wave holds the running position
     const u32x4 qv = qkv_dims8(p, acc_q, L.qkv_b, h, dc, pos, true);
     u32x4 knew{}, vnew{};
     if (has_cur) {
@@ -628,28 +710,11 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
             *reinterpret_cast<u32x4 *>(L.vc + off) = vnew;
         }
     }
-    const size_t slice = static_cast<size_t>(kPage) * kHeadDim;
     float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    // all loads of a chunk of pages are issued together
-    auto load_chunk = [&](int c0, u32x4 (&k)[kAttPages][4], u32x4 (&v)[kAttPages][4]) {
-#pragma unroll
-        for (int pg = 0; pg < kAttPages; ++pg) {
-            if (c0 + pg < pe) {
-                const int ph = p.page_table[c0 + pg];
-                const size_t base = (static_cast<size_t>(ph) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    k[pg][i] = *reinterpret_cast<const u32x4 *>(L.kc + base + i * 4 * kHeadDim);
-                    v[pg][i] = *reinterpret_cast<const u32x4 *>(L.vc + base + i * 4 * kHeadDim);
-                }
-            }
-        }
-    };
     for (int c0 = pb; c0 < pe; c0 += kAttPages) {
-        u32x4 kcur[kAttPages][4], vcur[kAttPages][4];
-        load_chunk(c0, kcur, vcur);
+        if (c0 != pb) att_load(p, L, j, c0, pe, ts, dc, kc, vc);
 #pragma unroll
         for (int pg = 0; pg < kAttPages; ++pg) {
             if (c0 + pg >= pe) break;
@@ -657,8 +722,8 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
             for (int i = 0; i < 4; ++i) {
                 const int tok = (c0 + pg) * kPage + ts + 4 * i;
                 // the running token's key and value are not in the cache yet
-                const u32x4 kk = tok == pos ? knew : kcur[pg][i];
-                const u32x4 vv = tok == pos ? vnew : vcur[pg][i];
+                const u32x4 kk = tok == pos ? knew : kc[pg][i];
+                const u32x4 vv = tok == pos ? vnew : vc[pg][i];
                 float sc = 0.f;
                 sc = __builtin_amdgcn_fdot2(as_h2(qv.x), as_h2(kk.x), sc, false);
                 sc = __builtin_amdgcn_fdot2(as_h2(qv.y), as_h2(kk.y), sc, false);
@@ -694,16 +759,39 @@ __device__ __forceinline__ void pk_attention(const PKParams &p, const PKLayer &L
         for (int e = 0; e < 8; ++e) acc[e] = acc[e] * f0 + __shfl_xor(acc[e], off) * f1;
         m = mn;
     }
-    float *part = p.att_part + (static_cast<size_t>(h) * p.att_smax + sp) * 132;
+    // merge the 4 waves in wave order through LDS: [wave][m, l, 128 dims]
+    float *sw = s_att + wave * 130;
     if (lane < 16) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) store_agent(part + 4 + dc * 8 + e, acc[e]);
+        for (int e = 0; e < 8; ++e) sw[2 + dc * 8 + e] = acc[e];
     }
-    if (lane == 0) {
-        store_agent(part, m);
-        store_agent(part + 1, l);
+    if (lane == 0) { sw[0] = m; sw[1] = l; }
+    __syncthreads();
+    if (wave == 0) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, s_att[v * 130]);
+        float Ls = 0.f, A0 = 0.f, A1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float mv = s_att[v * 130];
+            if (mv != -INFINITY) {
+                const float f = exp2f(mv - M);
+                Ls += s_att[v * 130 + 1] * f;
+                A0 += s_att[v * 130 + 2 + 2 * lane] * f;
+                A1 += s_att[v * 130 + 3 + 2 * lane] * f;
+            }
+        }
+        float *part = att_part + (static_cast<size_t>(h) * p.att_smax + c) * 132;
+        store_agent(part + 4 + 2 * lane, A0);
+        store_agent(part + 5 + 2 * lane, A1);
+        if (lane == 0) {
+            store_agent(part, M);
+            store_agent(part + 1, Ls);
+        }
+        pk_signal(head_cnt + h * kCS);
     }
-    pk_signal(head_cnt + h * kCS);
+    return true;
 }
 
 // ------------------------------------------------------ phase schedule ----
@@ -848,14 +936,16 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     const int phys = p.page_table[pos >> 4];
     const int L = p.n_layers;
     const int n_pages = (ctx + kPage - 1) / kPage;
-    const int n_split = (n_pages + p.att_pps - 1) / p.att_pps;
+    // attention chunks of 4 x att_pps pages per head at this context
+    const int n_split = (n_pages + 4 * p.att_pps - 1) / (4 * p.att_pps);
 
-    // attention item of this wave (items spread over all waves), if any
-    const int n_items_max = p.n_qh * p.att_smax;
+    // attention unit (head, chunk) of this work-group (units spread over all
+    // work-groups), if any
+    const int n_units_max = p.n_qh * p.att_smax;
     int att_h = -1, att_s = 0;
     {
-        const int i0 = static_cast<int>((static_cast<int64_t>(w) * n_items_max + W - 1) / W);
-        if (i0 < n_items_max && tile_owner(i0, n_items_max, W) == w) {
+        const int i0 = static_cast<int>((static_cast<int64_t>(B) * n_units_max + p.P - 1) / p.P);
+        if (i0 < n_units_max && tile_owner(i0, n_units_max, p.P) == B) {
             const int hh = i0 / p.att_smax, ss = i0 - hh * p.att_smax;
             if (ss < n_split) { att_h = hh; att_s = ss; }
         }
@@ -891,16 +981,16 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
         const bool has_next = ph + 1 < n_ph;
         // attention runs between a layer's QKV and O phases; its waves fill
         // their ring for O only afterwards
-        if (g.kind == kPhO && att_h >= 0 && ok) {
-            ok = pk_wait_cnt(p, pk_grp_cnt(p, par, g.l, kPhQ), p.n_grp, 0, p.n_grp, 0, 2000 + g.l);
-            if (ok) {
-                // the ring holds nothing this wave still needs: clearing it
-                // lets its registers serve the attention loads
-                ring = Ring{};
-                pk_attention(p, p.layers[g.l], pk_acc(p, par, g.l, p.acc_q), pk_head_cnt(p, par, g.l), att_h,
-                             att_s, n_split, ctx, phys);
-                prefetch_phase(ring, p, g);
-            }
+        if (g.kind == kPhO && att_h >= 0) {
+            if (!ok) break;
+            // the ring holds nothing this wave still needs: clearing it
+            // lets its registers serve the attention loads
+            ring = Ring{};
+            ok = pk_attention(p, p.layers[g.l], pk_grp_cnt(p, par, g.l, kPhQ), pk_acc(p, par, g.l, p.acc_q),
+                              p.att_part + g.l * p.att_layer, pk_head_cnt(p, par, g.l), att_h, att_s, ctx, phys,
+                              reinterpret_cast<float *>(s_red), 2000 + g.l);
+            if (!ok) break;
+            prefetch_phase(ring, p, g);
         }
         const bool next_after_att = has_next && ((ph + 1) & 3) == kPhO && ph + 1 < 4 * L && att_h >= 0;
         if (rg.e > rg.b) {
@@ -920,7 +1010,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             else if (g.stage == kStSwiGLU)
                 stage_swiglu(s_stage, rg, g.nk, g.V, g.acc_in);
             else
-                stage_attn(s_stage, rg, g.nk, p.att_part, p.att_smax, n_split);
+                stage_attn(s_stage, rg, g.nk, p.att_part + g.l * p.att_layer, p.att_smax, n_split);
             __syncthreads();
             if (g.kind == kPhLM) f16_tiles(ring, p.lm, g.nk, rg, rb0, s_stage, s_red);
             else w4_tiles(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);

@@ -497,11 +497,12 @@ static w4_status setup_persistent(w4_model *m) {
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
     // normalised inputs are staged whole, one element per thread and batch slot
     W4_CHECK(d <= kStageMax * kThreads && d * 2 <= kStageBytes, W4_EINVAL, "d_model too large for the persistent step");
-    // pages per attention split: at least 2, and enough that every (head,
-    // split) item has a wave of its own
+    // attention: a work-group per (head, chunk of 4 x att_pps pages), wave
+    // v of it taking att_pps pages; at least 2 pages per wave, and enough
+    // that every (head, chunk) unit has a work-group of its own
     pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 4 * P - 1) / (4 * P));
-    pk.att_smax = (c.max_pages + pk.att_pps - 1) / pk.att_pps;
-    W4_CHECK(c.n_q_heads * pk.att_smax <= 4 * P, W4_EINVAL, "too many attention splits for the grid");
+    pk.att_smax = (c.max_pages + 4 * pk.att_pps - 1) / (4 * pk.att_pps);
+    W4_CHECK(c.n_q_heads * pk.att_smax <= P, W4_EINVAL, "too many attention chunks for the grid");
 
     // step-parity blocks: accumulators of every layer, then counters (per
     // layer: 4 phases x groups, one per head; then the embedding counter)
@@ -522,7 +523,7 @@ static w4_status setup_persistent(w4_model *m) {
     const size_t per_layer = align256(static_cast<size_t>(d) * 8) * 2;
     const size_t total = align256(sizeof(PKLayer) * L) + align256(sizeof(PKParams)) +
                          align256(static_cast<size_t>(d) * 8) + align256(part) +
-                         align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) + 256 + per_layer * L +
+                         align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) * L + 256 + per_layer * L +
                          ctr_bytes + 2 * pk.par_bytes;
     W4_HIP(hipMalloc(&m->pk_arena, total));
     W4_HIP(hipMemset(m->pk_arena, 0, total));
@@ -531,7 +532,8 @@ static w4_status setup_persistent(w4_model *m) {
     m->pk_dev = reinterpret_cast<PKParams *>(b); b += align256(sizeof(PKParams));
     pk.x0 = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
     pk.partial = reinterpret_cast<double *>(b); b += align256(part);
-    pk.att_part = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4);
+    pk.att_layer = align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) / 4;
+    pk.att_part = reinterpret_cast<float *>(b); b += pk.att_layer * 4 * L;
     pk.err = reinterpret_cast<int *>(b); b += 256;
     std::vector<PKLayer> hl(L);
     const size_t kv_layer = layer_kv_elems(m);
@@ -589,14 +591,20 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
     for (const void *p : ptrs) W4_CHECK(p != nullptr, W4_EALIGN, "a model buffer is NULL");
     W4_CHECK(aligned16(buf->lm_head) && aligned16(buf->k_cache) && aligned16(buf->v_cache), W4_EALIGN,
              "lm_head and KV caches must be 16-byte aligned");
+    W4_CHECK(reinterpret_cast<uintptr_t>(buf->lnf) % 4 == 0, W4_EALIGN, "lnf must be 4-byte aligned");
     for (int l = 0; l < c.n_layers; ++l) {
         W4_CHECK(buf->qkv_q && buf->qkv_s && buf->qkv_bias && buf->o_q && buf->o_s && buf->gu_q && buf->gu_s &&
                      buf->down_q && buf->down_s && buf->ln1 && buf->ln2,
                  W4_EALIGN, "per-layer pointer arrays must not be NULL");
         W4_CHECK(aligned16(buf->qkv_q[l]) && aligned16(buf->o_q[l]) && aligned16(buf->gu_q[l]) &&
                      aligned16(buf->down_q[l]) && buf->qkv_s[l] && buf->o_s[l] && buf->gu_s[l] && buf->down_s[l] &&
-                     buf->qkv_bias[l] && buf->ln1[l] && buf->ln2[l],
-                 W4_EALIGN, "layer %d: packed weights must be 16-byte aligned, others non-NULL", l);
+                     buf->qkv_bias[l] && buf->ln1[l] && buf->ln2[l] &&
+                     reinterpret_cast<uintptr_t>(buf->ln1[l]) % 4 == 0 && reinterpret_cast<uintptr_t>(buf->ln2[l]) % 4 == 0 &&
+                     aligned16(buf->qkv_bias[l]),
+                 W4_EALIGN,
+                 "layer %d: packed weights and QKV bias must be 16-byte aligned, norm weights 4-byte aligned, others "
+                 "non-NULL",
+                 l);
     }
 
     w4_model *m = new w4_model();
