@@ -6,32 +6,68 @@ Workload: the Qwen2.5-7B-shaped decoder (28 layers, hidden 3584, MLP 18944,
 projections with fp16 scales, fp16 embeddings / norms / lm_head.  A 512-token
 seeded prompt is fed through the decode step (teacher-forced, untimed; its
 last W steps are the warmup), then K greedy steps are timed, each one graph
-replay of the whole step.  Prints one JSON line.
+replay of the whole step: one launch of the persistent decode kernel (plus a
+one-thread page-append kernel on the steps that open a KV page).  Prints one
+JSON line.
 
-Also reported: the achieved HBM bandwidth of the dominant kernel (fused
-gate+up GEMV) timed with HIP events on its launch stream, eager-launch
-ms/token, and the CPU oracle timed on a bounded sample on the host cores.
+Also reported: the roofline of the persistent decode kernel (algorithmic
+bytes of a step over its average duration, from HIP events recorded around
+every timed step on the launch stream), its HBM traffic from the committed
+rocprofv3 counter summary when that summary was taken on the current
+kernel sources, eager-launch ms/token, per-kernel times of the kernel-per-op
+variant, and the CPU oracle timed on a bounded sample on the host cores.
+
+Measurement modes (run by hand, results committed under profiles/):
+  --measure-traffic   runs this file twice under `rocprofv3 --pmc` (FETCH_SIZE,
+                      then WRITE_SIZE) with --traffic-probe, calibrates both
+                      counters on a device-to-device copy of known size, and
+                      writes profiles/decode_step_qwen7b_traffic.md
+  --summarize-trace D writes the kernel statistics of a
+                      `rocprofv3 --kernel-trace --stats -d D -o run` run of
+                      this file to profiles/decode_step_qwen7b_persistent_kernel_stats.md
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
 import numpy as np
 
+HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 PAGES_PUBLISHED_TOKS = 60.0    # the pages' runtime on an H100 for this workload (context)
+TRAFFIC_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_traffic.md")
+STATS_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_persistent_kernel_stats.md")
+KERNEL = "decode_persistent_kernel"
+CALIB_BYTES = 256 << 20        # device-to-device copy used to calibrate the byte counters
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def source_hash() -> str:
+    """Hash of the HIP sources the library is built from (a traffic figure
+    is only reported for the sources it was measured on)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(HERE, "int4_weight_only_dequant_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def step_bytes(dims, ctx_lo: int, ctx_hi: int) -> float:
-    """Algorithmic HBM bytes of one decode step, averaged over ctx in [ctx_lo, ctx_hi]."""
+    """Algorithmic HBM bytes of one decode step, averaged over ctx in [ctx_lo, ctx_hi]:
+    every weight byte once (int4 codes + fp16 scales, fp16 bias / norms / lm_head),
+    the embedding row, the KV cache read over the context and the new K/V written."""
     d, f, L = dims.d_model, dims.d_ff, dims.n_layers
     qkv_rows = dims.qkv_dim
 
@@ -46,12 +82,7 @@ def step_bytes(dims, ctx_lo: int, ctx_hi: int) -> float:
     return L * layer + small + lm + kv_per_tok * mean_ctx + kv_per_tok
 
 
-def gate_up_bytes(dims) -> int:
-    n, k = 2 * dims.d_ff, dims.d_model
-    return n * k // 2 + n * (k // 128) * 2 + k * 2 + dims.d_ff * 2
-
-
-def cpu_baseline(dims, glob, seconds_budget: float = 20.0):
+def cpu_baseline(dims, glob_w, seconds_budget: float = 20.0):
     """Oracle decode step on a bounded sample: a few decoder layers at a
     mid-run position plus the final norm and lm_head, extrapolated to 28 layers."""
     import oracle
@@ -69,7 +100,7 @@ def cpu_baseline(dims, glob, seconds_budget: float = 20.0):
         # filled with seeded values; the oracle's cost does not depend on them
         cache.k[l] = (rng.standard_normal(cache.k[l].shape, dtype=np.float32)).astype(np.float16)
         cache.v[l] = cache.k[l]
-    x = glob.embed[123].astype(np.float64)
+    x = glob_w.embed[123].astype(np.float64)
     t_layers = []
     t_start = time.time()
     for l in range(dims.n_layers):
@@ -80,8 +111,8 @@ def cpu_baseline(dims, glob, seconds_budget: float = 20.0):
         if time.time() - t_start > seconds_budget * 0.6 and len(t_layers) >= 2:
             break
     t0 = time.perf_counter()
-    xf = oracle.f16(oracle.rmsnorm(x, glob.lnf, dims.eps))
-    logits = glob.lm_head.astype(np.float64) @ xf.astype(np.float64)
+    xf = oracle.f16(oracle.rmsnorm(x, glob_w.lnf, dims.eps))
+    logits = glob_w.lm_head.astype(np.float64) @ xf.astype(np.float64)
     oracle.argmax_first(logits)
     t_head = time.perf_counter() - t0
     per_tok = dims.n_layers * float(np.mean(t_layers)) + t_head
@@ -97,6 +128,155 @@ def cpu_baseline(dims, glob, seconds_budget: float = 20.0):
     }
 
 
+def read_traffic():
+    """Per-launch HBM bytes of the persistent kernel from the committed
+    counter summary, or None if it was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_MD) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("source_hash") == source_hash():
+                        return rec
+    except OSError:
+        pass
+    return None
+
+
+def build_model(dims, n_prompt, n_steps):
+    import synth
+    import int4_weight_only_dequant_amd as w4
+    total_pos = n_prompt + n_steps
+    max_pages = -(-total_pos // 16)
+    t0 = time.time()
+    log(f"[bench] generating + packing the model ({max_pages} KV pages)")
+    glob_w = synth.global_weights(dims)
+    free = synth.page_free_list(max_pages)
+    model = w4.DecodeModel(dims, lambda l: synth.layer_weights(dims, l), glob_w, free, max_pages,
+                           progress=lambda l: log(f"[bench] layer {l} uploaded ({time.time() - t0:.0f}s)")
+                           if l % 7 == 6 else None)
+    return model, glob_w, max_pages
+
+
+def traffic_probe():
+    """Child of --measure-traffic (runs under rocprofv3 --pmc): the prompt, 16
+    persistent steps, then a device-to-device copy of CALIB_BYTES."""
+    import torch
+    import synth
+    dims = synth.QWEN7B
+    model, _, _ = build_model(dims, 512, 16)
+    model.reset(synth.prompt_ids(dims, 512))
+    for _ in range(512 + 16):
+        model.step()
+    torch.cuda.synchronize()
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    assert model.device_error() == 0
+    model.close()
+    print("traffic probe done", flush=True)
+
+
+def _pmc_rows(path):
+    rows = list(csv.DictReader(open(path)))
+    return rows
+
+
+def measure_traffic(out_dir: str):
+    """Two rocprofv3 --pmc runs of the traffic probe; writes TRAFFIC_MD."""
+    res = {}
+    cmds = []
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(out_dir, f"pmc_{ctr.lower()}")
+        cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "pmc", "--",
+               sys.executable, "-u", os.path.join(HERE, "bench.py"), "--traffic-probe"]
+        cmds.append(" ".join(cmd[:-4] + ["python3", "-u", "bench.py", "--traffic-probe"]))
+        log("[bench] " + " ".join(cmd))
+        env = dict(os.environ, TMPDIR="/tmp")
+        r = subprocess.run(cmd, env=env, timeout=600)
+        if r.returncode != 0:
+            sys.exit(f"rocprofv3 {ctr} run failed ({r.returncode})")
+        files = glob.glob(os.path.join(d, "**", "pmc_counter_collection.csv"), recursive=True)
+        if not files:
+            sys.exit(f"no counter file under {d}")
+        rows = _pmc_rows(files[0])
+        kern = [float(r["Counter_Value"]) for r in rows if KERNEL in r["Kernel_Name"] and r["Counter_Name"] == ctr]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
+        if len(kern) < 16 or not copy:
+            sys.exit(f"{ctr}: {len(kern)} kernel dispatches, {len(copy)} copy dispatches")
+        res[ctr] = {"kernel_kib": float(np.mean(kern[-16:])), "copy_kib": max(copy), "dispatches": len(kern)}
+    f_scale = CALIB_BYTES / (res["FETCH_SIZE"]["copy_kib"] * 1024.0)
+    w_scale = CALIB_BYTES / (res["WRITE_SIZE"]["copy_kib"] * 1024.0)
+    fetch = res["FETCH_SIZE"]["kernel_kib"] * 1024.0 * f_scale
+    write = res["WRITE_SIZE"]["kernel_kib"] * 1024.0 * w_scale
+    import synth
+    algo = step_bytes(synth.QWEN7B, 513, 528)
+    rec = {"source_hash": source_hash(), "fetch_bytes": fetch, "write_bytes": write,
+           "traffic_bytes": fetch + write, "algorithmic_bytes": algo,
+           "fetch_kib_raw": res["FETCH_SIZE"]["kernel_kib"], "write_kib_raw": res["WRITE_SIZE"]["kernel_kib"],
+           "copy_fetch_kib": res["FETCH_SIZE"]["copy_kib"], "copy_write_kib": res["WRITE_SIZE"]["copy_kib"],
+           "fetch_scale": f_scale, "write_scale": w_scale}
+    lines = [
+        "# HBM traffic of the persistent decode kernel (rocprofv3 counters)", "",
+        "Commands (from the repository root on one MI355X; each counter in a run of its own):", "",
+        "```", "export TMPDIR=/tmp", *cmds, "```", "",
+        "Both runs execute `bench.py --traffic-probe`: the Qwen2.5-7B-shaped model, the 512-token prompt",
+        "through the decode step, 16 more steps (context 513-528), then one device-to-device copy of",
+        f"{CALIB_BYTES} bytes (`__amd_rocclr_copyBuffer`) that calibrates the counters: it reads and writes",
+        "exactly that many bytes, so each counter is scaled by copy bytes / counted bytes.", "",
+        "| | FETCH_SIZE | WRITE_SIZE |", "|---|---:|---:|",
+        f"| copy kernel, KiB counted | {res['FETCH_SIZE']['copy_kib']:.0f} | {res['WRITE_SIZE']['copy_kib']:.0f} |",
+        f"| scale (copy bytes / counted bytes) | {f_scale:.4f} | {w_scale:.4f} |",
+        f"| `{KERNEL}`, KiB per launch (mean of the last 16) | {res['FETCH_SIZE']['kernel_kib']:.0f} | "
+        f"{res['WRITE_SIZE']['kernel_kib']:.0f} |",
+        f"| `{KERNEL}`, scaled bytes per launch | {fetch:.4g} | {write:.4g} |", "",
+        f"Traffic per launch {fetch + write:.4g} bytes against {algo:.4g} algorithmic bytes "
+        f"({(fetch + write) / algo:.3f}x).", "",
+        "The line below is read by bench.py, which reports the traffic only while the kernel sources",
+        "still hash to `source_hash`.", "",
+        "traffic-json: " + json.dumps(rec), ""]
+    os.makedirs(os.path.dirname(TRAFFIC_MD), exist_ok=True)
+    with open(TRAFFIC_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(json.dumps(rec), flush=True)
+
+
+def summarize_trace(d: str, steps: int, cmd: str):
+    """Kernel statistics of a --kernel-trace --stats run of this file; the
+    persistent kernel's mean over its last `steps` dispatches (the timed
+    steps) is listed beside its mean over all dispatches."""
+    stats = glob.glob(os.path.join(d, "**", "run_kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "**", "run_kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        sys.exit(f"no rocprofv3 csv files under {d}")
+    rows = list(csv.DictReader(open(stats[0])))
+    tr = [r for r in csv.DictReader(open(trace[0])) if KERNEL in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr], dtype=np.float64) / 1e3
+    lines = ["# rocprofv3 kernel statistics: persistent decode step", "",
+             "Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | total ms | % |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        if float(r["Percentage"]) < 0.01:
+            continue
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.2f} |")
+    lines += ["", f"`{KERNEL}`: {len(dur)} dispatches; mean over all {dur.mean():.1f} us; "
+              f"mean over the last {steps} (the timed steps, context 513-{512 + steps}) "
+              f"{dur[-steps:].mean():.1f} us (min {dur[-steps:].min():.1f}, max {dur[-steps:].max():.1f}).", "",
+              "The earlier dispatches are the teacher-forced prompt (contexts 1-512, 16 of them eager",
+              "launches) and the warmup; the kernel-per-op rows are the timing-hook replays of that variant.", ""]
+    os.makedirs(os.path.dirname(STATS_MD), exist_ok=True)
+    with open(STATS_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,33 +284,37 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=112)
+    ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--measure-traffic", metavar="OUT_DIR")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--trace-command", default="")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_probe:
+        return traffic_probe()
+    if args.measure_traffic:
+        return measure_traffic(args.measure_traffic)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.steps, args.trace_command)
 
     import torch
     import synth
-    import int4_weight_only_dequant_amd as w4
     from int4_weight_only_dequant_amd import _lib as L
 
     dims = synth.QWEN7B
     n_prompt = 512
     if args.warmup > n_prompt - 1:
         sys.exit("warmup must be below the prompt length")
-    total_pos = n_prompt + args.steps
-    max_pages = -(-total_pos // 16)
     t0 = time.time()
-    log(f"[bench] generating + packing the model ({max_pages} KV pages)")
-    glob = synth.global_weights(dims)
-    free = synth.page_free_list(max_pages)
+    model, glob_w, max_pages = build_model(dims, n_prompt, args.steps)
     prompt = synth.prompt_ids(dims, n_prompt)
-    model = w4.DecodeModel(dims, lambda l: synth.layer_weights(dims, l), glob, free, max_pages,
-                           progress=lambda l: log(f"[bench] layer {l} uploaded ({time.time() - t0:.0f}s)")
-                           if l % 7 == 6 else None)
     stream = torch.cuda.current_stream()
-    log(f"[bench] model ready in {time.time() - t0:.0f}s; launches/step {model.launches_per_step()}")
+    launches = model.launches_per_step()
+    log(f"[bench] model ready in {time.time() - t0:.0f}s; grid {model.grid()} work-groups, "
+        f"{launches} launch per step (+ page append at page boundaries)")
 
     # prompt through the decode step; eager timing on 16 prompt steps; the last W steps are warmup
     model.reset(prompt)
@@ -149,42 +333,45 @@ def main():
             log(f"[bench] prompt prefilled through decode steps; warmup {args.warmup} steps")
     torch.cuda.synchronize()
 
-    # timed region: K graph replays, positions 512 .. 512+K-1
+    # timed region: K graph replays, positions 512 .. 512+K-1, a HIP event on
+    # the launch stream before every step
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     tstart = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[i].record(stream)
         model.step(L.W4_GRAPH)
+    ev[-1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - tstart
     ms = elapsed * 1e3 / args.steps
     tok_s = args.steps / elapsed
+    step_us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)])
+    boundary = np.array([(n_prompt + i) % 16 == 0 for i in range(args.steps)])
+    kern_us = float(step_us[~boundary].mean())      # steps without the page append: the kernel alone
+    assert model.device_error() == 0, "device error during the timed steps"
     gen = model.tokens[n_prompt: n_prompt + args.steps + 1].cpu().numpy()
-    log(f"[bench] {args.steps} steps: {ms:.3f} ms/token, {tok_s:.1f} tok/s; first tokens {gen[:8]}")
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/token, {tok_s:.1f} tok/s; persistent kernel "
+        f"{kern_us:.1f} us per launch (events); first tokens {gen[:8]}")
 
-    # dominant kernel: fused gate+up GEMV, HIP events on its launch stream
-    reps = args.kernel_reps
-    model.kernel_replay(L.W4_KERNEL_GATE_UP, 28)          # warm
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    model.kernel_replay(L.W4_KERNEL_GATE_UP, reps)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    gu_us = e0.elapsed_time(e1) * 1e3 / reps
-    gu_bytes = gate_up_bytes(dims)
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    # kernel-per-op variant, per-kernel times (timing hook; clobbers the activation scratch)
     kern = {}
-    for name, kind in (("down", L.W4_KERNEL_DOWN), ("o_proj", L.W4_KERNEL_O), ("lm_head", L.W4_KERNEL_LM_HEAD)):
-        r = 28 if kind != L.W4_KERNEL_LM_HEAD else 8
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, kind, r in (("gate_up", L.W4_KERNEL_GATE_UP, args.kernel_reps), ("down", L.W4_KERNEL_DOWN, 28),
+                          ("o_proj", L.W4_KERNEL_O, 28), ("lm_head", L.W4_KERNEL_LM_HEAD, 8)):
+        model.kernel_replay(kind, 4)
         e0.record(stream)
         model.kernel_replay(kind, r)
         e1.record(stream)
         torch.cuda.synchronize()
         kern[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / r, 2)
-    kern["gate_up_us"] = round(gu_us, 2)
-    launches = model.launches_per_step()
+    multi_launches = model.launches_per_step(L.W4_MULTI)
     model.close()
 
-    sb = step_bytes(dims, n_prompt + 1, n_prompt + args.steps)
-    step_frac = (sb / (HBM_PEAK_GBS * 1e9)) / (ms * 1e-3)
+    ctx_lo, ctx_hi = n_prompt + 1, n_prompt + args.steps
+    sb = step_bytes(dims, ctx_lo, ctx_hi)
+    achieved = sb / (kern_us * 1e-6) / 1e9
+    tr = read_traffic()
     line = {
         "metric": "decode ms/token & tok/s (batch 1, 512+128); W4A16 GEMV achieved HBM TB/s",
         "value": round(tok_s, 2),
@@ -202,22 +389,24 @@ def main():
                                "graph-captured steps, int4 group-128 projections with fp16 scales",
                    "layers": dims.n_layers, "hidden": dims.d_model, "mlp": dims.d_ff,
                    "heads": f"{dims.n_q_heads}q/{dims.n_kv_heads}kv x {dims.head_dim}",
-                   "vocab": dims.vocab, "context": f"{n_prompt + 1}-{n_prompt + args.steps}",
+                   "vocab": dims.vocab, "context": f"{ctx_lo}-{ctx_hi}",
                    "kv_pages": max_pages, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "w4_gemv_kernel<EpiSwiGLU> (fused gate+up GEMV, N=37888, K=3584)",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"{KERNEL} (the whole decode step, one launch per token)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3)},
-        "step_roofline": {"bytes_per_token": int(sb), "frac_of_8TBs": round(step_frac, 4),
-                          "achieved_GBs": round(sb / (ms * 1e-3) / 1e9, 1)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": round(tr["traffic_bytes"]) if tr else None,
+                     "bytes_per_launch": int(sb), "avg_launch_us": round(kern_us, 2),
+                     "traffic_source": os.path.relpath(TRAFFIC_MD, HERE) if tr else None},
+        "vs_baseline_note": f"ratio to the pages' {PAGES_PUBLISHED_TOKS:.0f} tok/s on an H100-class GPU (context)",
         "eager_ms_per_step": round(eager_ms, 3),
         "launches_per_step": launches,
-        "kernel_us": kern,
+        "kernel_per_op_variant": {"launches_per_step": multi_launches, **kern},
         "tokens_head": [int(t) for t in gen[:16]],
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(dims, glob)
+        line["cpu_baseline"] = cpu_baseline(dims, glob_w)
     log(f"[bench] done in {time.time() - t0:.0f}s")
     print(json.dumps(line), flush=True)
 

@@ -264,8 +264,10 @@ w4_status w4_model_status(w4_model *m, int32_t *device_error);
 /* Work-groups of the persistent step (all resident at once). */
 int32_t w4_model_grid(const w4_model *m);
 
-/* Number of kernel launches one eager step makes (for the launch-count report). */
-int32_t w4_model_launches_per_step(const w4_model *m);
+/* Number of kernel launches one step of the variant selected by flags
+ * (W4_MULTI or not) makes, not counting the page append that steps at a page
+ * boundary add (for the launch-count report). */
+int32_t w4_model_launches_per_step(const w4_model *m, uint32_t flags);
 
 /* Measurement hook: enqueues `reps` launches of one of the step's kernels,
  * with the step's launch geometry, cycling over the layers' weights (so

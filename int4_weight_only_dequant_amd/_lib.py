@@ -75,7 +75,7 @@ def _declare(lib):
         "w4_model_reset": (i32, [vp, i32, vp]),
         "w4_model_pos": (i32, [vp]),
         "decode_step": (i32, [vp, i32, u32, vp]),
-        "w4_model_launches_per_step": (i32, [vp]),
+        "w4_model_launches_per_step": (i32, [vp, u32]),
         "w4_model_kernel_replay": (i32, [vp, i32, i32, vp]),
         "w4_model_status": (i32, [vp, C.POINTER(i32)]),
         "w4_model_grid": (i32, [vp]),

@@ -741,7 +741,10 @@ extern "C" w4_status w4_model_reset(w4_model *m, int32_t n_prompt, void *stream)
 
 extern "C" int32_t w4_model_pos(const w4_model *m) { return m ? m->pos : -1; }
 
-extern "C" int32_t w4_model_launches_per_step(const w4_model *m) { return m ? m->launches : 0; }
+extern "C" int32_t w4_model_launches_per_step(const w4_model *m, uint32_t flags) {
+    if (!m) return 0;
+    return (flags & W4_MULTI) ? m->launches : 1;
+}
 
 extern "C" w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream) {
     clear_error();

@@ -110,8 +110,9 @@ class DecodeModel:
     def grid(self) -> int:
         return L.lib().w4_model_grid(self._m)
 
-    def launches_per_step(self) -> int:
-        return L.lib().w4_model_launches_per_step(self._m)
+    def launches_per_step(self, flags: int = 0) -> int:
+        """Kernel launches of one step of the given variant (page append not counted)."""
+        return L.lib().w4_model_launches_per_step(self._m, flags)
 
     def kernel_replay(self, kind: int, reps: int, stream=None) -> None:
         """Enqueue reps launches of one step kernel (timing hook; scratch is clobbered)."""
