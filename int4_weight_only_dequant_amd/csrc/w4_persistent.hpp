@@ -73,7 +73,7 @@ struct PKLayer {
     const u32x4 *dn_q; const uint16_t *dn_s;
     const uint16_t *ln1; const uint16_t *ln2;
     uint16_t *kc; uint16_t *vc;            // this layer's KV pools
-    double *xo; double *xd;                // residual stream after O / after down (work-group 0 writes)
+    float *xo; float *xd;                  // residual stream after O / after down (work-group 0 writes)
 };
 
 struct PKParams {
@@ -83,7 +83,7 @@ struct PKParams {
     const int *page_table; int *tokens; float *logits;
     const double *rope;
     StepState *st;
-    double *x0;
+    float *x0;                 // embedding row (the layer-0 residual)
     double *partial;
     float *att_part;           // attention split partials, per layer
     size_t att_layer;          // floats per layer of att_part
@@ -225,12 +225,6 @@ __device__ __forceinline__ unsigned pk_complete(const PKParams &p, int grp_base,
     return __builtin_amdgcn_readfirstlane(o2);
 }
 
-// Wave sum in a fixed butterfly order (deterministic).
-__device__ __forceinline__ double wave_sum(double v) {
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
-
 __device__ __forceinline__ double fix_to_f64(long long a) { return static_cast<double>(a) * kFixInv; }
 
 // ------------------------------------------------------------- tile ring ----
@@ -290,28 +284,56 @@ __device__ __forceinline__ void stage_begin(double *red, int n_rl) {
 // inputs sit in L2 or beyond; one round trip instead of one per element).
 constexpr int kStageMax = 16;   // elements per thread (host-checked)
 
-// x = x_prev + acc (acc may be null), RMSNorm with weight w, whole vector to
-// LDS.  Each thread takes element pairs (2-byte global loads are slow: the
-// fp16 weights are read two at a time).  The sum of squares is taken in a
-// fixed order (per thread in pair order, then wave butterflies, then waves
-// 0..3).  If x_out is set the residual x is stored there.
+// x = x_prev + acc (acc may be null), rounded to the fp32 residual stream;
+// RMSNorm with weight w, whole vector to LDS.  Each thread takes element
+// pairs (2-byte global loads are slow: the fp16 weights are read two at a
+// time).  The sum of squares is fp64 in a fixed order: per thread in pair
+// order, within each 16-lane row by DPP, then the 16 row sums of the
+// work-group in row order.  If x_out is set the residual is stored there.
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
 constexpr int kPairMax = kStageMax / 2;
 
-__device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, int d, const double *x_prev,
+__device__ __forceinline__ double dpp_f64(double v, int ctrl_q) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    int lo, hi;
+    switch (ctrl_q) {   // the DPP control must be a constant
+        case 0: lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0xB1, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), 0xB1, 0xF, 0xF, false); break;
+        case 1: lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0x4E, 0xF, 0xF, false);
+                hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), 0x4E, 0xF, 0xF, false); break;
+        case 2: lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0x141, 0xF, 0xF, false);   // row_half_mirror
+                hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), 0x141, 0xF, 0xF, false); break;
+        default: lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), 0x140, 0xF, 0xF, false);  // row_mirror
+                 hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), 0x140, 0xF, 0xF, false); break;
+    }
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                          static_cast<uint32_t>(lo));
+}
+
+// Sum over each 16-lane row (every lane of the row gets it): pairs, quads,
+// halves, rows.
+__device__ __forceinline__ double row16_sum_f64(double v) {
+    v += dpp_f64(v, 0);
+    v += dpp_f64(v, 1);
+    v += dpp_f64(v, 2);
+    v += dpp_f64(v, 3);
+    return v;
+}
+
+__device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, int d, const float *x_prev,
                                                  const long long *acc, const uint16_t *w, double eps,
-                                                 double *x_out) {
+                                                 float *x_out) {
     const int np = d / 2;
     const int tid = opaque_tid();
-    f64x2 xv[kPairMax];
+    float2 xv[kPairMax];
     i64x2 av[kPairMax];
     uint32_t wv[kPairMax];
 #pragma unroll
     for (int j = 0; j < kPairMax; ++j) {
         const int q = tid + j * kThreads;
         if (q < np) {
-            xv[j] = reinterpret_cast<const f64x2 *>(x_prev)[q];
+            xv[j] = reinterpret_cast<const float2 *>(x_prev)[q];
             wv[j] = reinterpret_cast<const uint32_t *>(w)[q];
             if (acc) av[j] = reinterpret_cast<const i64x2 *>(acc)[q];
             else av[j] = i64x2{0, 0};
@@ -322,16 +344,18 @@ __device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, in
     for (int j = 0; j < kPairMax; ++j) {
         const int q = tid + j * kThreads;
         if (q < np) {
-            xv[j].x += fix_to_f64(av[j].x);
-            xv[j].y += fix_to_f64(av[j].y);
-            sq += xv[j].x * xv[j].x;
-            sq += xv[j].y * xv[j].y;
+            xv[j].x = static_cast<float>(static_cast<double>(xv[j].x) + fix_to_f64(av[j].x));
+            xv[j].y = static_cast<float>(static_cast<double>(xv[j].y) + fix_to_f64(av[j].y));
+            sq += static_cast<double>(xv[j].x) * xv[j].x;
+            sq += static_cast<double>(xv[j].y) * xv[j].y;
         }
     }
-    sq = wave_sum(sq);
-    if (lane_id() == 0) wsum[wave_id()] = sq;
+    sq = row16_sum_f64(sq);
+    if ((tid & 15) == 0) wsum[tid >> 4] = sq;
     __syncthreads();
-    const double ss = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    double ss = 0.0;
+#pragma unroll
+    for (int r = 0; r < kThreads / 16; ++r) ss += wsum[r];
     // the scaling itself runs in fp32: its rounding (a few 2^-24) sits far
     // below the fp16 rounding of the result
     const float inv_r = static_cast<float>(1.0 / sqrt(ss / d + eps));
@@ -343,8 +367,8 @@ __device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, in
                 store_agent(x_out + 2 * q, xv[j].x);
                 store_agent(x_out + 2 * q + 1, xv[j].y);
             }
-            const uint32_t lo = f32_to_f16(static_cast<float>(xv[j].x) * inv_r * f16_to_f32(wv[j] & 0xFFFFu));
-            const uint32_t hi = f32_to_f16(static_cast<float>(xv[j].y) * inv_r * f16_to_f32(wv[j] >> 16));
+            const uint32_t lo = f32_to_f16(xv[j].x * inv_r * f16_to_f32(wv[j] & 0xFFFFu));
+            const uint32_t hi = f32_to_f16(xv[j].y * inv_r * f16_to_f32(wv[j] >> 16));
             reinterpret_cast<uint32_t *>(lds)[q] = lo | (hi << 16);
         }
     }
@@ -809,7 +833,7 @@ struct PhaseDesc {
     // staging: normalised residual (x_prev + acc_in, weight w, store to
     // x_out), SwiGLU of acc_in, or merged attention
     int stage;
-    const double *x_prev; const long long *acc_in; const uint16_t *w; double *x_out;
+    const float *x_prev; const long long *acc_in; const uint16_t *w; float *x_out;
     long long *acc_out;       // this phase's accumulators
     unsigned *done;           // this phase's completion counters
 };
@@ -921,7 +945,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     const PKParams &p = *pp;
     __shared__ __attribute__((aligned(16))) double s_red[kRedBytes / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_stage[kStageBytes / 2];
-    __shared__ double s_wsum[4];
+    __shared__ double s_wsum[kThreads / 16];
     const int wave = wave_id();
     const int B = blockIdx.x;
     const int w = (B << 2) + wave;
@@ -959,7 +983,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
         const int d = p.d;
         const int tok = p.tokens[pos];
         const uint16_t *row = p.embed + static_cast<size_t>(tok) * d;
-        for (int i = lane; i < d; i += 64) store_agent(p.x0 + i, static_cast<double>(f16_to_f32(row[i])));
+        for (int i = lane; i < d; i += 64) store_agent(p.x0 + i, f16_to_f32(row[i]));
         if (lane == 0) store_agent(&p.st->best, 0ull);
         pk_signal(pk_embed_cnt(p, par));
     }

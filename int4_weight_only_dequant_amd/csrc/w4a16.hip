@@ -530,7 +530,7 @@ static w4_status setup_persistent(w4_model *m) {
     char *b = static_cast<char *>(m->pk_arena);
     m->pk_layers = reinterpret_cast<PKLayer *>(b); b += align256(sizeof(PKLayer) * L);
     m->pk_dev = reinterpret_cast<PKParams *>(b); b += align256(sizeof(PKParams));
-    pk.x0 = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
+    pk.x0 = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(d) * 8);
     pk.partial = reinterpret_cast<double *>(b); b += align256(part);
     pk.att_layer = align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) / 4;
     pk.att_part = reinterpret_cast<float *>(b); b += pk.att_layer * 4 * L;
@@ -545,8 +545,8 @@ static w4_status setup_persistent(w4_model *m) {
         y.dn_q = reinterpret_cast<const u32x4 *>(m->down_q[l]); y.dn_s = m->down_s[l];
         y.ln1 = m->ln1[l]; y.ln2 = m->ln2[l];
         y.kc = m->k_cache + l * kv_layer; y.vc = m->v_cache + l * kv_layer;
-        y.xo = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
-        y.xd = reinterpret_cast<double *>(b); b += align256(static_cast<size_t>(d) * 8);
+        y.xo = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(d) * 8);
+        y.xd = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(d) * 8);
     }
     // counters and both parity blocks last and contiguous: reset clears them in one sweep
     pk.ctr = reinterpret_cast<unsigned *>(b); b += ctr_bytes;
