@@ -118,6 +118,15 @@ __host__ __device__ constexpr int n_groups(int n_units) { return (n_units + kGrp
 // GEMV phases in order: for each layer QKV, O, gate+up, down; then lm_head.
 enum { kPhQ = 0, kPhO = 1, kPhGU = 2, kPhD = 3, kPhLM = 4 };
 
+// The layer table through the constant address space: it is read-only for
+// the kernel and indexed by uniform layer numbers, so its fields come in by
+// scalar loads (a vector load would make the wave wait for every load it has
+// in flight, the weight prefetch included).
+typedef __attribute__((address_space(4))) const PKLayer *const_layer_ptr;
+__device__ __forceinline__ const_layer_ptr pk_layer(const PKParams &p, int l) {
+    return (const_layer_ptr)(p.layers) + l;
+}
+
 __device__ __forceinline__ long long *pk_acc(const PKParams &p, int par, int l, int off) {
     return reinterpret_cast<long long *>(p.par[par]) + static_cast<size_t>(l) * p.acc_layer + off;
 }
@@ -644,41 +653,56 @@ struct PKFinLogits {
 
 constexpr int kAttPages = 2;   // pages loaded together per wave (8 x 16 B per lane per page)
 
-// Eight dims dc*8 .. dc*8+7 of head `head` (QKV row order: dims i and i + 64
-// are rows 2i and 2i + 1 of the head), as packed fp16, with bias and, if
-// rope, the rotation of position pos.  All reads are 16-byte loads: the 16
-// accumulator rows 2 i0 .. 2 i0 + 15, the 8 biases of each half and the 8
-// (cos, sin) pairs.
-__device__ __forceinline__ u32x4 qkv_dims8(const PKParams &p, const long long *acc, const uint16_t *bias, int head,
-                                           int dc, int pos, bool rope) {
+// Eight dims dc*8 .. dc*8+7 of one head of the QKV output (QKV row order:
+// dims i and i + 64 are rows 2i and 2i + 1 of the head): the 16 accumulator
+// rows 2 i0 .. 2 i0 + 15 and the 8 biases of each half, read with 16-byte
+// loads.  Loading and finishing are separate so that every load of the
+// query, key and value is in flight at once.
+struct QkvRaw {
+    i64x2 a[8];
+    u32x4 bo, bp;
+};
+
+__device__ __forceinline__ void qkv_load_bias(QkvRaw &r, const uint16_t *bias, int head, int dc, bool partner) {
     const int hi = dc >> 3, i0 = (dc * 8) & 63;
+    r.bo = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * hi + i0);
+    if (partner) r.bp = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * (hi ^ 1) + i0);
+}
+
+__device__ __forceinline__ void qkv_load_acc(QkvRaw &r, const long long *acc, int head, int dc) {
+    const int i0 = (dc * 8) & 63;
     const i64x2 *a = reinterpret_cast<const i64x2 *>(acc + head * 128 + 2 * i0);
-    i64x2 av[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) av[e] = a[e];
-    const u32x4 bo = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * hi + i0);
-    const u32x4 bp = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * (hi ^ 1) + i0);
-    f64x2 cs[8];
-    if (rope) {
-        const f64x2 *rp = reinterpret_cast<const f64x2 *>(p.rope + (static_cast<size_t>(pos) * 64 + i0) * 2);
+    for (int e = 0; e < 8; ++e) r.a[e] = a[e];
+}
+
+// The 8 (cos, sin) pairs of position pos for dims i0 .. i0 + 7
+__device__ __forceinline__ void rope_load(f64x2 (&cs)[8], const PKParams &p, int dc, int pos) {
+    const int i0 = (dc * 8) & 63;
+    const f64x2 *rp = reinterpret_cast<const f64x2 *>(p.rope + (static_cast<size_t>(pos) * 64 + i0) * 2);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = rp[e];
-    }
-    const uint32_t bw[4] = {bo.x, bo.y, bo.z, bo.w}, pw[4] = {bp.x, bp.y, bp.z, bp.w};
+    for (int e = 0; e < 8; ++e) cs[e] = rp[e];
+}
+
+// bias, then (if cs) the rotation; rounded to packed fp16
+__device__ __forceinline__ u32x4 qkv_finish(const QkvRaw &r, int dc, const f64x2 *cs) {
+    const int hi = dc >> 3;
+    const uint32_t bw[4] = {r.bo.x, r.bo.y, r.bo.z, r.bo.w}, pw[4] = {r.bp.x, r.bp.y, r.bp.z, r.bp.w};
     uint32_t out[4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint16_t b16 = static_cast<uint16_t>(bw[e >> 1] >> (16 * (e & 1)));
-        const uint16_t p16 = static_cast<uint16_t>(pw[e >> 1] >> (16 * (e & 1)));
-        const long long own = hi ? av[e].y : av[e].x, other = hi ? av[e].x : av[e].y;
+        const long long own = hi ? r.a[e].y : r.a[e].x;
         const double v = fix_to_f64(own) + static_cast<double>(f16_to_f32(b16));
-        double r = v;
-        if (rope) {
+        double res = v;
+        if (cs) {
+            const uint16_t p16 = static_cast<uint16_t>(pw[e >> 1] >> (16 * (e & 1)));
+            const long long other = hi ? r.a[e].x : r.a[e].y;
             const double partner = fix_to_f64(other) + static_cast<double>(f16_to_f32(p16));
             const double c = cs[e].x, sn = cs[e].y;
-            r = hi ? partner * sn + v * c : v * c - partner * sn;
+            res = hi ? partner * sn + v * c : v * c - partner * sn;
         }
-        const uint32_t h16 = f64_to_f16(r);
+        const uint32_t h16 = f64_to_f16(res);
         if (e & 1) out[e >> 1] |= h16 << 16;
         else out[e >> 1] = h16;
     }
@@ -688,25 +712,31 @@ __device__ __forceinline__ u32x4 qkv_dims8(const PKParams &p, const long long *a
 }
 
 // K and V of pages [c0, min(c0 + kAttPages, pe)) for this lane
-__device__ __forceinline__ void att_load(const PKParams &p, const PKLayer &L, int j, int c0, int pe, int ts, int dc,
+__device__ __forceinline__ void att_load(const PKParams &p, const_layer_ptr L, int j, int c0, int pe, int ts, int dc,
                                          u32x4 (&k)[kAttPages][4], u32x4 (&v)[kAttPages][4]) {
     const size_t slice = static_cast<size_t>(kPage) * kHeadDim;
+    // the page table is read-only for the step: scalar loads, all issued
+    // before the K/V loads that depend on them
+    const const_u32_ptr pt = as_const(reinterpret_cast<const uint32_t *>(p.page_table));
+    int phy[kAttPages];
+#pragma unroll
+    for (int pg = 0; pg < kAttPages; ++pg)
+        phy[pg] = c0 + pg < pe ? static_cast<int>(pt[__builtin_amdgcn_readfirstlane(c0 + pg)]) : 0;
 #pragma unroll
     for (int pg = 0; pg < kAttPages; ++pg) {
         if (c0 + pg < pe) {
-            const int ph = p.page_table[c0 + pg];
-            const size_t base = (static_cast<size_t>(ph) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
+            const size_t base = (static_cast<size_t>(phy[pg]) * p.n_kvh + j) * slice + ts * kHeadDim + dc * 8;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                k[pg][i] = *reinterpret_cast<const u32x4 *>(L.kc + base + i * 4 * kHeadDim);
-                v[pg][i] = *reinterpret_cast<const u32x4 *>(L.vc + base + i * 4 * kHeadDim);
+                k[pg][i] = *reinterpret_cast<const u32x4 *>(L->kc + base + i * 4 * kHeadDim);
+                v[pg][i] = *reinterpret_cast<const u32x4 *>(L->vc + base + i * 4 * kHeadDim);
             }
         }
     }
 }
 
 // Returns false if the wait for the QKV phase failed (all waves agree).
-__device__ __forceinline__ bool pk_attention(const PKParams &p, const PKLayer &L, const unsigned *q_done,
+__device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr L, const unsigned *q_done,
                                              const long long *acc_q, float *att_part, unsigned *head_cnt, int h,
                                              int c, int ctx, int phys, float *s_att, int code) {
     const int lane = opaque_tid() & 63, wave = wave_id();
@@ -723,15 +753,25 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const PKLayer &L
     if (__syncthreads_or(!ok)) return false;
 
     const bool has_cur = pb < pe && pe == n_pages;   // this wave holds the running position
-    const u32x4 qv = qkv_dims8(p, acc_q, L.qkv_b, h, dc, pos, true);
+    QkvRaw rq;
+    f64x2 cs[8];
+    qkv_load_bias(rq, L->qkv_b, h, dc, true);
+    rope_load(cs, p, dc, pos);
+    qkv_load_acc(rq, acc_q, h, dc);
+    const u32x4 qv = qkv_finish(rq, dc, cs);
     u32x4 knew{}, vnew{};
     if (has_cur) {
-        knew = qkv_dims8(p, acc_q, L.qkv_b, p.n_qh + j, dc, pos, true);
-        vnew = qkv_dims8(p, acc_q, L.qkv_b, p.n_qh + p.n_kvh + j, dc, pos, false);
+        QkvRaw rk, rv;
+        qkv_load_bias(rk, L->qkv_b, p.n_qh + j, dc, true);
+        qkv_load_bias(rv, L->qkv_b, p.n_qh + p.n_kvh + j, dc, false);
+        qkv_load_acc(rk, acc_q, p.n_qh + j, dc);
+        qkv_load_acc(rv, acc_q, p.n_qh + p.n_kvh + j, dc);
+        knew = qkv_finish(rk, dc, cs);
+        vnew = qkv_finish(rv, dc, nullptr);
         if (h == j * G && ts == 0) {
             const size_t off = ((static_cast<size_t>(phys) * p.n_kvh + j) * kPage + (pos & 15)) * kHeadDim + dc * 8;
-            *reinterpret_cast<u32x4 *>(L.kc + off) = knew;
-            *reinterpret_cast<u32x4 *>(L.vc + off) = vnew;
+            *reinterpret_cast<u32x4 *>(L->kc + off) = knew;
+            *reinterpret_cast<u32x4 *>(L->vc + off) = vnew;
         }
     }
     float m = -INFINITY, l = 0.f, acc[8];
@@ -851,43 +891,43 @@ __device__ __forceinline__ PhaseDesc phase_desc(const PKParams &p, int ph, int p
         g.kind = kPhLM; g.l = L - 1;
         g.nk = d / 32; g.V = 32; g.n_rb = (p.vocab + 63) / 64; g.T = g.n_rb * g.nk;
         g.dep = pk_grp_cnt(p, par, L - 1, kPhD);
-        g.x_prev = p.layers[L - 1].xo; g.acc_in = pk_acc(p, par, L - 1, p.acc_d); g.w = p.lnf;
+        g.x_prev = pk_layer(p, L - 1)->xo; g.acc_in = pk_acc(p, par, L - 1, p.acc_d); g.w = p.lnf;
         return g;
     }
     const int l = ph >> 2;
-    const PKLayer &Ly = p.layers[l];
+    const const_layer_ptr Ly = pk_layer(p, l);
     g.kind = ph & 3; g.l = l; g.V = kGroup;
     g.done = pk_grp_cnt(p, par, l, g.kind);
     switch (g.kind) {
         case kPhQ:
-            g.wq = Ly.qkv_q; g.ws = Ly.qkv_s; g.nk = nq; g.n_rb = rb_q;
+            g.wq = Ly->qkv_q; g.ws = Ly->qkv_s; g.nk = nq; g.n_rb = rb_q;
             g.acc_out = pk_acc(p, par, l, p.acc_q);
             if (l == 0) {
                 g.dep = pk_embed_cnt(p, par); g.dep_n = 1; g.dep_want = 1;
                 g.x_prev = p.x0;
             } else {
                 g.dep = pk_grp_cnt(p, par, l - 1, kPhD);
-                g.x_prev = p.layers[l - 1].xo; g.acc_in = pk_acc(p, par, l - 1, p.acc_d);
-                g.x_out = p.layers[l - 1].xd;
+                g.x_prev = pk_layer(p, l - 1)->xo; g.acc_in = pk_acc(p, par, l - 1, p.acc_d);
+                g.x_out = pk_layer(p, l - 1)->xd;
             }
-            g.w = Ly.ln1;
+            g.w = Ly->ln1;
             break;
         case kPhO:          // a 128-element K group of the O projection is one head
-            g.wq = Ly.o_q; g.ws = Ly.o_s; g.nk = no; g.n_rb = rb_d;
+            g.wq = Ly->o_q; g.ws = Ly->o_s; g.nk = no; g.n_rb = rb_d;
             g.acc_out = pk_acc(p, par, l, p.acc_o);
             g.dep = pk_head_cnt(p, par, l); g.dep_n = p.n_qh; g.dep_want = static_cast<unsigned>(n_split);
             g.dep_all = false;
             g.stage = kStAttn;
             break;
         case kPhGU:
-            g.wq = Ly.gu_q; g.ws = Ly.gu_s; g.nk = nq; g.n_rb = rb_gu;
+            g.wq = Ly->gu_q; g.ws = Ly->gu_s; g.nk = nq; g.n_rb = rb_gu;
             g.acc_out = pk_acc(p, par, l, p.acc_gu);
             g.dep = pk_grp_cnt(p, par, l, kPhO);
-            g.x_prev = l == 0 ? p.x0 : p.layers[l - 1].xd; g.acc_in = pk_acc(p, par, l, p.acc_o);
-            g.w = Ly.ln2; g.x_out = Ly.xo;
+            g.x_prev = l == 0 ? p.x0 : pk_layer(p, l - 1)->xd; g.acc_in = pk_acc(p, par, l, p.acc_o);
+            g.w = Ly->ln2; g.x_out = Ly->xo;
             break;
         default:
-            g.wq = Ly.dn_q; g.ws = Ly.dn_s; g.nk = nf; g.n_rb = rb_d;
+            g.wq = Ly->dn_q; g.ws = Ly->dn_s; g.nk = nf; g.n_rb = rb_d;
             g.acc_out = pk_acc(p, par, l, p.acc_d);
             g.dep = pk_grp_cnt(p, par, l, kPhGU);
             g.stage = kStSwiGLU; g.acc_in = pk_acc(p, par, l, p.acc_gu);
@@ -1010,7 +1050,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             // the ring holds nothing this wave still needs: clearing it
             // lets its registers serve the attention loads
             ring = Ring{};
-            ok = pk_attention(p, p.layers[g.l], pk_grp_cnt(p, par, g.l, kPhQ), pk_acc(p, par, g.l, p.acc_q),
+            ok = pk_attention(p, pk_layer(p, g.l), pk_grp_cnt(p, par, g.l, kPhQ), pk_acc(p, par, g.l, p.acc_q),
                               p.att_part + g.l * p.att_layer, pk_head_cnt(p, par, g.l), att_h, att_s, ctx, phys,
                               reinterpret_cast<float *>(s_red), 2000 + g.l);
             if (!ok) break;

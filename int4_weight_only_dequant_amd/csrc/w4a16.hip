@@ -489,6 +489,12 @@ static w4_status setup_persistent(w4_model *m) {
     pk.P = P;
     std::string why;
     int slots_unused = 0;
+    // attention: a work-group per (head, chunk of 4 x att_pps pages), wave
+    // v of it taking att_pps pages; at least 2 pages per wave, and enough
+    // that every (head, chunk) unit has a work-group of its own
+    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 4 * P - 1) / (4 * P));
+    pk.att_smax = (c.max_pages + 4 * pk.att_pps - 1) / (4 * pk.att_pps);
+    W4_CHECK(c.n_q_heads * pk.att_smax <= P, W4_EINVAL, "too many attention chunks for the grid");
     const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, slots_unused, why) &&
                     phase_geometry(rb_d * no, no, kGroup, P, slots_unused, why) &&
                     phase_geometry(rb_gu * nq, nq, kGroup, P, slots_unused, why) &&
@@ -497,12 +503,6 @@ static w4_status setup_persistent(w4_model *m) {
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
     // normalised inputs are staged whole, one element per thread and batch slot
     W4_CHECK(d <= kStageMax * kThreads && d * 2 <= kStageBytes, W4_EINVAL, "d_model too large for the persistent step");
-    // attention: a work-group per (head, chunk of 4 x att_pps pages), wave
-    // v of it taking att_pps pages; at least 2 pages per wave, and enough
-    // that every (head, chunk) unit has a work-group of its own
-    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 4 * P - 1) / (4 * P));
-    pk.att_smax = (c.max_pages + 4 * pk.att_pps - 1) / (4 * pk.att_pps);
-    W4_CHECK(c.n_q_heads * pk.att_smax <= P, W4_EINVAL, "too many attention chunks for the grid");
 
     // step-parity blocks: accumulators of every layer, then counters (per
     // layer: 4 phases x groups, one per head; then the embedding counter)
