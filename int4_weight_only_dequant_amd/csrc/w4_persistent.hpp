@@ -13,9 +13,10 @@
 //   loads per lane, one contiguous KiB per wave load); its 4 waves take every
 //   4th tile of the range.  Phases run in order QKV -> attention -> O ->
 //   gate+up -> down per layer, then the lm_head.
-// * Before waiting for a phase's input, a wave issues the loads of its first
-//   four tiles of that phase into a register ring; weights do not depend on
-//   activations, so HBM keeps streaming while dependencies resolve.
+// * Before waiting for a phase's input, a wave issues the load of its first
+//   tile of that phase; weights do not depend on activations, so HBM keeps
+//   streaming while dependencies resolve.  In the tile loop each wave keeps
+//   one tile in flight while it works on the previous one.
 // * Split-K sums of the decoder GEMVs are combined with 64-bit integer atomic
 //   adds into per-row accumulators in fixed point (2^-32 units).  Integer
 //   addition is associative, so the result does not depend on arrival order
@@ -49,7 +50,12 @@
 
 namespace w4 {
 
-constexpr int kRing = 4;                 // tiles in flight per wave
+// Tiles in flight per wave.  One is best on MI355X: 2048 waves x 4 KiB keep
+// about 8 MiB in flight, enough for ~7 TB/s at the loaded latency (~1.2 us);
+// deeper rings add no bandwidth, only queueing in front of the latency-bound
+// phase hand-overs (measured: 1.70 ms per step at 1, 1.72 at 2, 1.79 at 3,
+// 1.87 at 4).
+constexpr int kRing = 1;
 constexpr int kMaxRbPerWg = 8;           // row blocks one work-group's range may touch
 constexpr int kRedBytes = kMaxRbPerWg * 4 * 64 * 8;
 constexpr int kStageBytes = 18432;       // staged fp16 input per work-group
