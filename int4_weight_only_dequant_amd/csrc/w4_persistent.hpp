@@ -659,62 +659,42 @@ struct PKFinLogits {
 
 constexpr int kAttPages = 2;   // pages loaded together per wave (8 x 16 B per lane per page)
 
-// Eight dims dc*8 .. dc*8+7 of one head of the QKV output (QKV row order:
-// dims i and i + 64 are rows 2i and 2i + 1 of the head): the 16 accumulator
-// rows 2 i0 .. 2 i0 + 15 and the 8 biases of each half, read with 16-byte
-// loads.  Loading and finishing are separate so that every load of the
-// query, key and value is in flight at once.
-struct QkvRaw {
-    i64x2 a[8];
-    u32x4 bo, bp;
-};
-
-__device__ __forceinline__ void qkv_load_bias(QkvRaw &r, const uint16_t *bias, int head, int dc, bool partner) {
-    const int hi = dc >> 3, i0 = (dc * 8) & 63;
-    r.bo = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * hi + i0);
-    if (partner) r.bp = *reinterpret_cast<const u32x4 *>(bias + head * 128 + 64 * (hi ^ 1) + i0);
-}
-
-__device__ __forceinline__ void qkv_load_acc(QkvRaw &r, const long long *acc, int head, int dc) {
-    const int i0 = (dc * 8) & 63;
-    const i64x2 *a = reinterpret_cast<const i64x2 *>(acc + head * 128 + 2 * i0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.a[e] = a[e];
-}
-
-// The 8 (cos, sin) pairs of position pos for dims i0 .. i0 + 7
-__device__ __forceinline__ void rope_load(f64x2 (&cs)[8], const PKParams &p, int dc, int pos) {
-    const int i0 = (dc * 8) & 63;
-    const f64x2 *rp = reinterpret_cast<const f64x2 *>(p.rope + (static_cast<size_t>(pos) * 64 + i0) * 2);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cs[e] = rp[e];
-}
-
-// bias, then (if cs) the rotation; rounded to packed fp16
-__device__ __forceinline__ u32x4 qkv_finish(const QkvRaw &r, int dc, const f64x2 *cs) {
-    const int hi = dc >> 3;
-    const uint32_t bw[4] = {r.bo.x, r.bo.y, r.bo.z, r.bo.w}, pw[4] = {r.bp.x, r.bp.y, r.bp.z, r.bp.w};
-    uint32_t out[4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint16_t b16 = static_cast<uint16_t>(bw[e >> 1] >> (16 * (e & 1)));
-        const long long own = hi ? r.a[e].y : r.a[e].x;
-        const double v = fix_to_f64(own) + static_cast<double>(f16_to_f32(b16));
-        double res = v;
-        if (cs) {
-            const uint16_t p16 = static_cast<uint16_t>(pw[e >> 1] >> (16 * (e & 1)));
-            const long long other = hi ? r.a[e].x : r.a[e].y;
-            const double partner = fix_to_f64(other) + static_cast<double>(f16_to_f32(p16));
-            const double c = cs[e].x, sn = cs[e].y;
-            res = hi ? partner * sn + v * c : v * c - partner * sn;
-        }
-        const uint32_t h16 = f64_to_f16(res);
-        if (e & 1) out[e >> 1] |= h16 << 16;
-        else out[e >> 1] = h16;
+// The query of head h (and, with kv, the running token's key and value of kv
+// head j) from the QKV accumulators, as fp16 into LDS: sq[128], sk[128],
+// sv[128].  Thread t < 128 takes query dim t and value dim t, thread t >= 128
+// key dim t - 128: bias, then RoPE (dims i and i + 64 pair up; in QKV row
+// order they are rows 2i and 2i + 1 of the head), in fp64.  Every load is
+// issued before any is used.
+__device__ __forceinline__ void qkv_to_lds(const PKParams &p, const long long *acc, const uint16_t *bias, int h,
+                                           int j, int pos, bool kv, uint16_t *sq, uint16_t *sk, uint16_t *sv) {
+    const int t = opaque_tid();
+    const int d = t & 127, i = d & 63, hi = d >> 6;
+    const bool first = t < 128;
+    const bool rot = first || kv;                  // q, or k when wanted
+    const int head = first ? h : p.n_qh + j;
+    const int hv = p.n_qh + p.n_kvh + j;
+    long long a_own = 0, a_par = 0, a_v = 0;
+    uint16_t b_own = 0, b_par = 0, b_v = 0;
+    double c = 0.0, sn = 0.0;
+    if (rot) {
+        a_own = acc[head * 128 + 2 * i + hi];
+        a_par = acc[head * 128 + 2 * i + (hi ^ 1)];
+        b_own = bias[head * 128 + d];
+        b_par = bias[head * 128 + (d ^ 64)];
+        c = p.rope[(static_cast<size_t>(pos) * 64 + i) * 2];
+        sn = p.rope[(static_cast<size_t>(pos) * 64 + i) * 2 + 1];
     }
-    u32x4 q;
-    q.x = out[0]; q.y = out[1]; q.z = out[2]; q.w = out[3];
-    return q;
+    if (first && kv) {
+        a_v = acc[hv * 128 + 2 * i + hi];
+        b_v = bias[hv * 128 + d];
+    }
+    if (rot) {
+        const double v = fix_to_f64(a_own) + static_cast<double>(f16_to_f32(b_own));
+        const double pa = fix_to_f64(a_par) + static_cast<double>(f16_to_f32(b_par));
+        const double r = hi ? pa * sn + v * c : v * c - pa * sn;
+        (first ? sq : sk)[d] = f64_to_f16(r);
+    }
+    if (first && kv) sv[d] = f64_to_f16(fix_to_f64(a_v) + static_cast<double>(f16_to_f32(b_v)));
 }
 
 // K and V of pages [c0, min(c0 + kAttPages, pe)) for this lane
@@ -744,7 +724,8 @@ __device__ __forceinline__ void att_load(const PKParams &p, const_layer_ptr L, i
 // Returns false if the wait for the QKV phase failed (all waves agree).
 __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr L, const unsigned *q_done,
                                              const long long *acc_q, float *att_part, unsigned *head_cnt, int h,
-                                             int c, int ctx, int phys, float *s_att, int code) {
+                                             int c, int n_split, int ctx, int phys, float *s_att, uint16_t *s_qkv,
+                                             int code) {
     const int lane = opaque_tid() & 63, wave = wave_id();
     const int ts = lane >> 4, dc = lane & 15;
     const int G = p.n_qh / p.n_kvh, j = h / G;
@@ -759,26 +740,21 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
     if (__syncthreads_or(!ok)) return false;
 
     const bool has_cur = pb < pe && pe == n_pages;   // this wave holds the running position
-    QkvRaw rq;
-    f64x2 cs[8];
-    qkv_load_bias(rq, L->qkv_b, h, dc, true);
-    rope_load(cs, p, dc, pos);
-    qkv_load_acc(rq, acc_q, h, dc);
-    const u32x4 qv = qkv_finish(rq, dc, cs);
+    const bool last_chunk = c == n_split - 1;       // the work-group holding the running position
+    uint16_t *sq = s_qkv, *sk = s_qkv + 128, *sv = s_qkv + 256;
+    qkv_to_lds(p, acc_q, L->qkv_b, h, j, pos, last_chunk, sq, sk, sv);
+    __syncthreads();
+    const u32x4 qv = *reinterpret_cast<const u32x4 *>(sq + dc * 8);
     u32x4 knew{}, vnew{};
     if (has_cur) {
-        QkvRaw rk, rv;
-        qkv_load_bias(rk, L->qkv_b, p.n_qh + j, dc, true);
-        qkv_load_bias(rv, L->qkv_b, p.n_qh + p.n_kvh + j, dc, false);
-        qkv_load_acc(rk, acc_q, p.n_qh + j, dc);
-        qkv_load_acc(rv, acc_q, p.n_qh + p.n_kvh + j, dc);
-        knew = qkv_finish(rk, dc, cs);
-        vnew = qkv_finish(rv, dc, nullptr);
-        if (h == j * G && ts == 0) {
-            const size_t off = ((static_cast<size_t>(phys) * p.n_kvh + j) * kPage + (pos & 15)) * kHeadDim + dc * 8;
-            *reinterpret_cast<u32x4 *>(L->kc + off) = knew;
-            *reinterpret_cast<u32x4 *>(L->vc + off) = vnew;
-        }
+        knew = *reinterpret_cast<const u32x4 *>(sk + dc * 8);
+        vnew = *reinterpret_cast<const u32x4 *>(sv + dc * 8);
+    }
+    // the first query head of a kv group writes the new key and value
+    if (last_chunk && h == j * G && wave == 0 && lane < 32) {
+        const size_t off = ((static_cast<size_t>(phys) * p.n_kvh + j) * kPage + (pos & 15)) * kHeadDim + (lane & 15) * 8;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>((lane < 16 ? sk : sv) + (lane & 15) * 8);
+        *reinterpret_cast<u32x4 *>((lane < 16 ? L->kc : L->vc) + off) = val;
     }
     float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
@@ -1057,8 +1033,8 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             // lets its registers serve the attention loads
             ring = Ring{};
             ok = pk_attention(p, pk_layer(p, g.l), pk_grp_cnt(p, par, g.l, kPhQ), pk_acc(p, par, g.l, p.acc_q),
-                              p.att_part + g.l * p.att_layer, pk_head_cnt(p, par, g.l), att_h, att_s, ctx, phys,
-                              reinterpret_cast<float *>(s_red), 2000 + g.l);
+                              p.att_part + g.l * p.att_layer, pk_head_cnt(p, par, g.l), att_h, att_s, n_split, ctx,
+                              phys, reinterpret_cast<float *>(s_red), s_stage, 2000 + g.l);
             if (!ok) break;
             prefetch_phase(ring, p, g);
         }
