@@ -42,6 +42,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, TFLOP/s
+PAGES_PUBLISHED_TTFT_MS = 128.0  # the pages' runtime, 512-token prompt, H100 (context)
 PAGES_PUBLISHED_TOKS = 60.0    # the pages' runtime on an H100 for this workload (context)
 TRAFFIC_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_traffic.md")
 STATS_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_persistent_kernel_stats.md")
@@ -316,6 +318,25 @@ def main():
     log(f"[bench] model ready in {time.time() - t0:.0f}s; grid {model.grid()} work-groups, "
         f"{launches} launch per step (+ page append at page boundaries)")
 
+    # time to first token: one prefill call over the 512-token prompt (first run warms up)
+    ttft = []
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in range(4):
+        model.reset(prompt)
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        pe0.record(stream)
+        model.prefill(n_prompt)
+        pe1.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            ttft.append(((time.perf_counter() - tp) * 1e3, pe0.elapsed_time(pe1)))
+    assert model.device_error() == 0, "device error during the prefill"
+    prefill_tok = int(model.tokens[n_prompt].item())
+    ttft_ms = float(np.median([t[0] for t in ttft]))
+    ttft_dev_ms = float(np.median([t[1] for t in ttft]))
+    log(f"[bench] prefill of {n_prompt} tokens: TTFT {ttft_ms:.2f} ms (device {ttft_dev_ms:.2f} ms), token {prefill_tok}")
+
     # prompt through the decode step; eager timing on 16 prompt steps; the last W steps are warmup
     model.reset(prompt)
     eager_lo, eager_n = 400, 16
@@ -372,6 +393,10 @@ def main():
     sb = step_bytes(dims, ctx_lo, ctx_hi)
     achieved = sb / (kern_us * 1e-6) / 1e9
     tr = read_traffic()
+    qkv_rows = (dims.n_q_heads + 2 * dims.n_kv_heads) * dims.head_dim
+    qd = dims.n_q_heads * dims.head_dim
+    lin_flop = 2.0 * n_prompt * dims.n_layers * (qkv_rows * dims.d_model + dims.d_model * qd +
+                                                 2 * dims.d_ff * dims.d_model + dims.d_model * dims.d_ff)
     line = {
         "metric": "decode ms/token & tok/s (batch 1, 512+128); W4A16 GEMV achieved HBM TB/s",
         "value": round(tok_s, 2),
@@ -403,6 +428,13 @@ def main():
         "launches_per_step": launches,
         "kernel_per_op_variant": {"launches_per_step": multi_launches, **kern},
         "tokens_head": [int(t) for t in gen[:16]],
+        "prefill": {"ttft_ms": round(ttft_ms, 3), "device_ms": round(ttft_dev_ms, 3), "prompt_tokens": n_prompt,
+                    "linear_tflop": round(lin_flop / 1e12, 3),
+                    "linear_tflops_over_ttft": round(lin_flop / (ttft_dev_ms * 1e-3) / 1e12, 1),
+                    "mfma_fp16_peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                    "frac_of_peak": round(lin_flop / (ttft_dev_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                    "first_token_matches_decode_path": prefill_tok == int(gen[0]),
+                    "pages_ttft_ms": PAGES_PUBLISHED_TTFT_MS},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

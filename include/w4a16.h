@@ -132,6 +132,30 @@ w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *do
                     int64_t D, int64_t F, void *workspace, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * W4A16 GEMM for prompt prefill (the projections of M prompt tokens at once;
+ * the pages time the first token of a 512-token prompt, [SP] "Technical
+ * Specifications and Benchmarking Data", performance comparison table, and
+ * [AI] "Summary", without describing the prefill).  Matrix cores
+ * (MFMA 32x32x16 fp16), fp32 accumulation; within a group of 128 K the
+ * integer codes meet the fp16 activations exactly and the group's scale is
+ * applied in fp32, split-K partials are summed in fp64 in split order.
+ *   y[m][r] = sum_k x[m][k] * W[r][k]     for m < M, packed rows r < N
+ *
+ *   packed_q, packed_s : device, from pack_int4_weights (y is in packed row
+ *                        order)
+ *   x                  : device, fp16 [M][K] row-major, 16-byte aligned
+ *   y                  : device, fp32 [M][N] row-major (written)
+ *   workspace          : device, w4_gemm_ws_bytes(M, N, K) bytes of scratch
+ *                        (split-K partials; no initialisation needed);
+ *                        calls sharing it must be ordered on one stream
+ * Errors: W4_EINVAL (M outside [1, 2^20], N < 1, K not a positive multiple
+ * of 128, workspace too small), W4_EALIGN, W4_EHIP (launch failure). */
+size_t w4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+w4_status w4a16_gemm(const uint8_t *packed_q, const uint16_t *packed_s,
+                     const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Paged decode attention  ([TS] "Technical Specifications…": 16-token pages,
  * one kv-head slice of a page is 4 KiB; [SP] "Three Critical Engineering
  * Challenges" item 1: softmax and weighted-V accumulation over KV pages).
@@ -158,6 +182,28 @@ w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool,
                             int32_t head_dim, int32_t n_pages_max, float scale,
                             uint16_t *out, void *workspace, size_t ws_bytes,
                             void *stream);
+
+/* Causal paged attention of a chunk of prompt tokens (prefill), on matrix
+ * cores.  Query m (m < n_tokens) sits at position pos0 + m and attends to the
+ * cached positions 0 .. pos0 + m, which include the chunk's own keys:
+ *   out[m][h] = sum_{t <= pos0+m} softmax_t(scale * q[m][h] . K[t, kv(h)]) V[t, kv(h)]
+ * with kv(h) = h / (n_qh / n_kvh) and token t in physical page
+ * page_table[t / 16], slot t % 16 (same pools as paged_attn_decode).
+ *   q         : device, fp16 [n_tokens][n_qh][head_dim]
+ *   k_pool,
+ *   v_pool    : device, fp16 [n_phys][n_kvh][16][head_dim], holding every
+ *               position < pos0 + n_tokens
+ *   page_table: device, int32; entries for positions < pos0 + n_tokens are
+ *               trusted to be valid physical pages
+ *   out       : device, fp16 [n_tokens][n_qh][head_dim] (written)
+ * head_dim must be 128 and n_qh a multiple of n_kvh; scale > 0.  The
+ * softmax weights enter the weighted sum of V rounded to fp16.
+ * Errors: W4_EINVAL, W4_EALIGN, W4_EHIP. */
+w4_status paged_attn_prefill(const uint16_t *q, const uint16_t *k_pool,
+                             const uint16_t *v_pool, const int32_t *page_table,
+                             int32_t pos0, int32_t n_tokens, int32_t n_qh,
+                             int32_t n_kvh, int32_t head_dim, float scale,
+                             uint16_t *out, void *stream);
 
 /* ------------------------------------------------------------------------
  * Decoder model and the graph-captured decode step
@@ -255,6 +301,25 @@ int32_t w4_model_pos(const w4_model *m);
 #define W4_MULTI 2u   /* with W4_GRAPH/W4_EAGER: the one-kernel-per-operation
                          step (143 launches) instead of the persistent one    */
 w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream);
+
+/* Prefill of n_tokens (1..512) prompt tokens at positions pos .. pos +
+ * n_tokens - 1 (pos must equal the model's position): appends the pages that
+ * start in that range, runs every layer over all rows with W4A16 GEMMs
+ * (RMSNorm, QKV + bias + RoPE, K/V written into the cache, causal paged
+ * attention over positions 0..p, O + residual, RMSNorm, gate/up + SwiGLU,
+ * down + residual), then the final norm and the fp16 lm_head on the last row:
+ * logits as after a decode step at position pos + n_tokens - 1, and the
+ * greedy token stored into tokens[pos + n_tokens] unless pos + n_tokens <
+ * n_prompt.  The model's position becomes pos + n_tokens; decode_step
+ * continues from there.  Same arithmetic and fp16 storage points as
+ * decode_step; the time to first token of a 512-token prompt is one call
+ * ([SP] "Technical Specifications and Benchmarking Data").  Launched
+ * directly (not graph-captured); uses the model's prefill scratch, so calls
+ * on one model must be ordered on one stream.
+ * Errors: W4_ESTATE (pos mismatch, no reset), W4_EINVAL (n_tokens outside
+ * [1, 512]), W4_ENOSPC (positions beyond the KV pool), W4_EHIP. */
+#define W4_PREFILL_MAX 512
+w4_status w4_model_prefill(w4_model *m, int32_t pos, int32_t n_tokens, void *stream);
 
 /* Synchronises the device and reports the persistent step's error word:
  * 0 = no error; otherwise a dependency wait exceeded its spin limit (the step

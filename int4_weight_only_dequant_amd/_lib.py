@@ -67,7 +67,10 @@ def _declare(lib):
         "w4a16_gemv": (i32, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
         "w4_mlp_ws_bytes": (sz, [i64, i64]),
         "w4a16_mlp": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp]),
+        "w4_gemm_ws_bytes": (sz, [i64, i64, i64]),
+        "w4a16_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]),
         "w4_attn_ws_bytes": (sz, [i32, i32, i32]),
+        "paged_attn_prefill": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]),
         "paged_attn_decode": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, sz, vp]),
         "w4_model_row_perm": (i32, [i32, C.POINTER(ModelConfig), vp]),
         "w4_model_create": (i32, [C.POINTER(ModelConfig), C.POINTER(ModelBuffers), C.POINTER(vp)]),
@@ -75,6 +78,7 @@ def _declare(lib):
         "w4_model_reset": (i32, [vp, i32, vp]),
         "w4_model_pos": (i32, [vp]),
         "decode_step": (i32, [vp, i32, u32, vp]),
+        "w4_model_prefill": (i32, [vp, i32, i32, vp]),
         "w4_model_launches_per_step": (i32, [vp, u32]),
         "w4_model_kernel_replay": (i32, [vp, i32, i32, vp]),
         "w4_model_status": (i32, [vp, C.POINTER(i32)]),
@@ -238,6 +242,49 @@ def w4a16_mlp(gu_q: torch.Tensor, gu_s: torch.Tensor, down_q: torch.Tensor, down
     check(L.w4a16_mlp(_ptr(gu_q), _ptr(gu_s), _ptr(down_q), _ptr(down_s), _ptr(x), _ptr(h), _ptr(y),
                       d, f, _ptr(ws), ws.numel(), st))
     return h, y
+
+
+def w4a16_gemm(packed_q: torch.Tensor, packed_s: torch.Tensor, x: torch.Tensor, n: int, k: int,
+               y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X W^T (fp32 [M, N]) for fp16 rows X [M, K] and a packed int4 matrix (rows in packed order)."""
+    _dev(packed_q), _dev(packed_s), _dev(x)
+    if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be fp16 [M, K]")
+    m = x.shape[0]
+    L = lib()
+    if packed_q.numel() * packed_q.element_size() < L.w4_packed_qbytes(n, k):
+        raise ValueError("packed codes too small for N x K")
+    if packed_s.numel() * packed_s.element_size() < L.w4_packed_sbytes(n, k):
+        raise ValueError("packed scales too small for N x K")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(y)
+    st = _stream(stream)
+    need = L.w4_gemm_ws_bytes(m, n, k)
+    ws = _workspace("gemm", need, x.device, st)
+    check(L.w4a16_gemm(_ptr(packed_q), _ptr(packed_s), _ptr(x), _ptr(y), m, n, k, _ptr(ws),
+                       ws.numel(), st))
+    return y
+
+
+def paged_attn_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                       page_table: torch.Tensor, pos0: int, scale: float,
+                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal attention of M prompt tokens at positions pos0.. over the paged cache (fp16 in/out)."""
+    for t in (q, k_pool, v_pool, page_table):
+        _dev(t)
+    m, n_qh, hd = q.shape
+    n_phys, n_kvh, page, hd2 = k_pool.shape
+    if page != 16 or hd2 != hd or v_pool.shape != k_pool.shape:
+        raise ValueError("pools must be [n_phys, n_kvh, 16, head_dim]")
+    if page_table.dtype != torch.int32 or page_table.numel() * 16 < pos0 + m:
+        raise ValueError("page_table must be int32 and cover every position < pos0 + M")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    check(lib().paged_attn_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table), int(pos0),
+                                   m, n_qh, n_kvh, hd, float(scale), _ptr(out), _stream(stream)))
+    return out
 
 
 def paged_attn_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

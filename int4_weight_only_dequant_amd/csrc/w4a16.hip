@@ -14,6 +14,7 @@
 #include "w4_attn.hpp"
 #include "w4_gemv.hpp"
 #include "w4_persistent.hpp"
+#include "w4_prefill.hpp"
 
 namespace w4 {
 
@@ -274,6 +275,142 @@ extern "C" w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool
     return W4_OK;
 }
 
+// ------------------------------------------------------------ W4A16 GEMM --
+
+namespace w4 {
+
+constexpr int kGemmTarget = 512;   // work-groups a GEMM launch aims for (2 per CU)
+
+struct GemmGeom {
+    int n_rb, n_nb, n_mb, n_groups, n_split, gps, n_cols, grid;
+};
+
+// Launch geometry of w4_gemm_kernel: 64-token x 256-row tiles, the groups
+// split so that the launch has about kGemmTarget work-groups (at most 8
+// splits), the grid padded to a multiple of 8 columns for the XCD mapping.
+static GemmGeom gemm_geom(int M, int N, int K) {
+    GemmGeom g;
+    g.n_rb = (N + kRows - 1) / kRows;
+    g.n_nb = (g.n_rb + 3) / 4;
+    g.n_mb = (M + kGemmBM - 1) / kGemmBM;
+    g.n_groups = K / kGroup;
+    const int base = g.n_mb * g.n_nb;
+    int s = (kGemmTarget + base - 1) / base;
+    s = std::max(1, std::min(std::min(s, 8), g.n_groups));
+    g.gps = (g.n_groups + s - 1) / s;
+    g.n_split = (g.n_groups + g.gps - 1) / g.gps;
+    g.n_cols = g.n_split * g.n_nb;
+    g.grid = g.n_mb * ((g.n_cols + 7) / 8) * 8;
+    return g;
+}
+
+static hipError_t launch_gemm(const GemmGeom &g, const uint8_t *q, const uint16_t *s, const uint16_t *x, int M,
+                              int N, float *out, hipStream_t st) {
+    GemmProblem p;
+    p.wq = reinterpret_cast<const u32x4 *>(q);
+    p.ws = s;
+    p.x = x;
+    p.out = out;
+    p.M = M;
+    p.N = N;
+    p.n_rb = g.n_rb;
+    p.n_chunks = g.n_groups * (kGroup / kChunk);
+    p.n_groups = g.n_groups;
+    p.n_split = g.n_split;
+    p.gps = g.gps;
+    p.n_nb = g.n_nb;
+    p.n_mb = g.n_mb;
+    p.n_cols = g.n_cols;
+    p.split_stride = static_cast<size_t>(M) * N;
+    hipLaunchKernelGGL(w4_gemm_kernel, dim3(g.grid), dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+// Largest split-K partial area (floats) of an M x N x K GEMM over every M in [1, m_max].
+static size_t gemm_part_floats_max(int m_max, int N, int K) {
+    size_t best = 0;
+    for (int mb = 1; mb * kGemmBM - (kGemmBM - 1) <= m_max; ++mb) {
+        const int M = std::min(mb * kGemmBM, m_max);
+        const GemmGeom g = gemm_geom(M, N, K);
+        best = std::max(best, static_cast<size_t>(g.n_split) * M * N);
+    }
+    return best;
+}
+
+static hipError_t launch_attn_prefill(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, const int *pt,
+                                      uint16_t *out, int M, int n_qh, int n_kvh, int pos0, float scale,
+                                      hipStream_t st) {
+    PrefillAttnProblem a;
+    a.q = q;
+    a.kpool = kc;
+    a.vpool = vc;
+    a.page_table = pt;
+    a.out = out;
+    a.M = M;
+    a.n_qh = n_qh;
+    a.n_kvh = n_kvh;
+    a.pos0 = pos0;
+    a.n_qb = (M + 31) / 32;
+    a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(n_qh * a.n_qb), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace w4
+
+extern "C" size_t w4_gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > (1 << 20) || N < 1 || N > (int64_t(1) << 30) || K < kGroup || K % kGroup ||
+        K > (int64_t(1) << 24))
+        return 0;
+    const GemmGeom g = gemm_geom(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+    return g.n_split > 1 ? static_cast<size_t>(g.n_split) * M * N * sizeof(float) : 16;
+}
+
+extern "C" w4_status w4a16_gemm(const uint8_t *packed_q, const uint16_t *packed_s, const uint16_t *x, float *y,
+                                int64_t M, int64_t N, int64_t K, void *workspace, size_t ws_bytes, void *stream) {
+    clear_error();
+    W4_CHECK(M >= 1 && M <= (1 << 20), W4_EINVAL, "bad M=%lld", (long long)M);
+    W4_CHECK(N >= 1 && N <= (int64_t(1) << 30) && M * N <= (int64_t(1) << 34), W4_EINVAL, "bad N=%lld",
+             (long long)N);
+    W4_CHECK(K >= kGroup && K % kGroup == 0 && K <= (int64_t(1) << 24), W4_EINVAL,
+             "K=%lld must be a positive multiple of 128", (long long)K);
+    W4_CHECK(aligned16(packed_q) && aligned16(packed_s) && aligned16(x), W4_EALIGN,
+             "packed_q, packed_s and x must be 16-byte aligned device pointers");
+    W4_CHECK(y != nullptr && (reinterpret_cast<uintptr_t>(y) & 3) == 0, W4_EALIGN, "bad y pointer");
+    const GemmGeom g = gemm_geom(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+    const size_t need = w4_gemm_ws_bytes(M, N, K);
+    W4_CHECK(ws_bytes >= need && aligned16(workspace), W4_EINVAL,
+             "workspace of %zu bytes given (16-byte aligned), %zu needed", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *dst = g.n_split > 1 ? static_cast<float *>(workspace) : y;
+    W4_HIP(launch_gemm(g, packed_q, packed_s, x, static_cast<int>(M), static_cast<int>(N), dst, s));
+    if (g.n_split > 1) {
+        const size_t total = static_cast<size_t>(M) * N;
+        const int blocks = static_cast<int>(std::min<size_t>((total + kThreads - 1) / kThreads, 4096));
+        hipLaunchKernelGGL(gemm_reduce_kernel, dim3(blocks), dim3(kThreads), 0, s, dst, g.n_split, total, total, y);
+        W4_HIP(hipGetLastError());
+    }
+    return W4_OK;
+}
+
+extern "C" w4_status paged_attn_prefill(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                                        const int32_t *page_table, int32_t pos0, int32_t n_tokens, int32_t n_qh,
+                                        int32_t n_kvh, int32_t head_dim, float scale, uint16_t *out,
+                                        void *stream) {
+    clear_error();
+    W4_CHECK(head_dim == kHeadDim, W4_EINVAL, "head_dim must be 128");
+    W4_CHECK(n_kvh >= 1 && n_qh >= n_kvh && n_qh % n_kvh == 0 && n_qh <= 1024, W4_EINVAL,
+             "n_qh=%d must be a multiple of n_kvh=%d", n_qh, n_kvh);
+    W4_CHECK(n_tokens >= 1 && n_tokens <= (1 << 20) && pos0 >= 0 && pos0 <= (1 << 24), W4_EINVAL,
+             "bad pos0=%d n_tokens=%d", pos0, n_tokens);
+    W4_CHECK(std::isfinite(scale) && scale > 0.0f, W4_EINVAL, "scale must be positive");
+    W4_CHECK(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(out) && page_table != nullptr,
+             W4_EALIGN, "q, pools and out must be 16-byte aligned device pointers");
+    W4_HIP(launch_attn_prefill(q, k_pool, v_pool, page_table, out, n_tokens, n_qh, n_kvh, pos0, scale,
+                               static_cast<hipStream_t>(stream)));
+    return W4_OK;
+}
+
 // ================================================================== model ==
 
 struct w4_model {
@@ -313,6 +450,16 @@ struct w4_model {
     PKParams *pk_dev;         // device copy of pk
     int pk_grid;              // resident work-groups
     int n_ctr;
+
+    // prefill scratch (kPrefillMax token rows)
+    void *pf_arena;
+    float *pf_x;        // residual [rows][d]
+    uint16_t *pf_a;     // normed input [rows][d]
+    uint16_t *pf_q;     // q after RoPE [rows][n_qh*128]
+    uint16_t *pf_o;     // attention output [rows][n_qh*128]
+    uint16_t *pf_h;     // SwiGLU output [rows][d_ff]
+    float *pf_part;     // GEMM split-K partials
+    size_t pf_part_floats;
 
     hipStream_t cap_stream;
     hipGraphExec_t exec[2];   // persistent step: [0] no page boundary, [1] page boundary
@@ -443,7 +590,91 @@ static void model_free(w4_model *m) {
     if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
     if (m->arena) (void)hipFree(m->arena);
     if (m->pk_arena) (void)hipFree(m->pk_arena);
+    if (m->pf_arena) (void)hipFree(m->pf_arena);
     delete m;
+}
+
+// Prefill scratch for kPrefillMax token rows.
+static w4_status setup_prefill(w4_model *m) {
+    const w4_model_config &c = m->cfg;
+    const int d = c.d_model, f = c.d_ff, qd = c.n_q_heads * kHeadDim;
+    const int qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
+    const size_t R = kPrefillMax;
+    size_t part = gemm_part_floats_max(kPrefillMax, qkv_rows, d);
+    part = std::max(part, gemm_part_floats_max(kPrefillMax, d, qd));
+    part = std::max(part, gemm_part_floats_max(kPrefillMax, 2 * f, d));
+    part = std::max(part, gemm_part_floats_max(kPrefillMax, d, f));
+    const size_t sizes[6] = {align256(R * d * 4), align256(R * d * 2), align256(R * qd * 2),
+                             align256(R * qd * 2), align256(R * f * 2), align256(part * 4)};
+    size_t total = 0;
+    for (size_t s : sizes) total += s;
+    W4_HIP(hipMalloc(&m->pf_arena, total));
+    char *b = static_cast<char *>(m->pf_arena);
+    m->pf_x = reinterpret_cast<float *>(b); b += sizes[0];
+    m->pf_a = reinterpret_cast<uint16_t *>(b); b += sizes[1];
+    m->pf_q = reinterpret_cast<uint16_t *>(b); b += sizes[2];
+    m->pf_o = reinterpret_cast<uint16_t *>(b); b += sizes[3];
+    m->pf_h = reinterpret_cast<uint16_t *>(b); b += sizes[4];
+    m->pf_part = reinterpret_cast<float *>(b);
+    m->pf_part_floats = part;
+    return W4_OK;
+}
+
+// Enqueues the prefill of tokens [pos0, pos0 + M): every layer over the M
+// rows, then the lm_head on the last row and the greedy token.
+static hipError_t enqueue_prefill(w4_model *m, int pos0, int M, hipStream_t s) {
+    const w4_model_config &c = m->cfg;
+    const int d = c.d_model, f = c.d_ff, qd = c.n_q_heads * kHeadDim;
+    const int qkv_rows = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim;
+    const double eps = c.eps;
+    const float scale = static_cast<float>(1.0 / sqrt(double(kHeadDim)));
+    hipError_t e;
+#define W4_PF(call)                     \
+    do {                                \
+        call;                           \
+        e = hipGetLastError();          \
+        if (e != hipSuccess) return e;  \
+    } while (0)
+    W4_PF(hipLaunchKernelGGL(pf_embed_kernel, dim3(M), dim3(kThreads), 0, s, m->embed, m->tokens, pos0, M, d,
+                             m->ln1[0], eps, m->pf_x, m->pf_a, m->page_table, m->free_list, m->state));
+    const GemmGeom g_qkv = gemm_geom(M, qkv_rows, d), g_o = gemm_geom(M, d, qd), g_gu = gemm_geom(M, 2 * f, d),
+                   g_dn = gemm_geom(M, d, f);
+    for (int l = 0; l < c.n_layers; ++l) {
+        uint16_t *kc = m->k_cache + l * layer_kv_elems(m);
+        uint16_t *vc = m->v_cache + l * layer_kv_elems(m);
+        e = launch_gemm(g_qkv, m->qkv_q[l], m->qkv_s[l], m->pf_a, M, qkv_rows, m->pf_part, s);
+        if (e != hipSuccess) return e;
+        W4_PF(hipLaunchKernelGGL(pf_qkv_kernel, dim3(M), dim3(kThreads), 0, s, m->pf_part, g_qkv.n_split,
+                                 static_cast<size_t>(M) * qkv_rows, qkv_rows, m->qkv_bias[l], m->rope, pos0,
+                                 m->page_table, m->pf_q, kc, vc, c.n_q_heads, c.n_kv_heads));
+        e = launch_attn_prefill(m->pf_q, kc, vc, m->page_table, m->pf_o, M, c.n_q_heads, c.n_kv_heads, pos0, scale, s);
+        if (e != hipSuccess) return e;
+        e = launch_gemm(g_o, m->o_q[l], m->o_s[l], m->pf_o, M, d, m->pf_part, s);
+        if (e != hipSuccess) return e;
+        W4_PF(hipLaunchKernelGGL(pf_resid_norm_kernel, dim3(M), dim3(kThreads), 0, s, m->pf_part, g_o.n_split,
+                                 static_cast<size_t>(M) * d, d, m->pf_x, m->ln2[l], eps, m->pf_a));
+        e = launch_gemm(g_gu, m->gu_q[l], m->gu_s[l], m->pf_a, M, 2 * f, m->pf_part, s);
+        if (e != hipSuccess) return e;
+        W4_PF(hipLaunchKernelGGL(pf_swiglu_kernel, dim3(M), dim3(kThreads), 0, s, m->pf_part, g_gu.n_split,
+                                 static_cast<size_t>(M) * 2 * f, f, m->pf_h));
+        e = launch_gemm(g_dn, m->down_q[l], m->down_s[l], m->pf_h, M, d, m->pf_part, s);
+        if (e != hipSuccess) return e;
+        const uint16_t *next_w = l + 1 < c.n_layers ? m->ln1[l + 1] : m->lnf;
+        W4_PF(hipLaunchKernelGGL(pf_resid_norm_kernel, dim3(M), dim3(kThreads), 0, s, m->pf_part, g_dn.n_split,
+                                 static_cast<size_t>(M) * d, d, m->pf_x, next_w, eps, m->pf_a));
+    }
+    F16Problem hp;
+    hp.w = reinterpret_cast<const u32x4 *>(m->lm_head);
+    hp.x = reinterpret_cast<const uint32_t *>(m->pf_a + static_cast<size_t>(M - 1) * d);
+    hp.n_chunks = d / 8;
+    hp.n_rb = m->rb_head;
+    hp.n = c.vocab;
+    hp.out = m->logits;
+    hp.best = &m->state->best;
+    W4_PF(hipLaunchKernelGGL(f16_gemv_kernel, dim3(m->rb_head), dim3(kThreads), 0, s, hp));
+    W4_PF(hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1), 0, s, m->state, m->tokens));
+#undef W4_PF
+    return hipSuccess;
 }
 
 // Largest number of work-groups that split one row block, and the checks
@@ -707,7 +938,8 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
         model_free(m);
         return fail(W4_EHIP, "model setup failed: %s", hipGetErrorString(e));
     }
-    w4_status st = setup_persistent(m);
+    w4_status st = setup_prefill(m);
+    if (st == W4_OK) st = setup_persistent(m);
     if (st == W4_OK) st = capture(m, false, false, &m->exec[0]);
     if (st == W4_OK) st = capture(m, true, false, &m->exec[1]);
     if (st == W4_OK) st = capture(m, false, true, &m->exec_multi[0]);
@@ -763,6 +995,20 @@ extern "C" w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void 
         W4_HIP(hipGraphLaunch((multi ? m->exec_multi : m->exec)[boundary ? 1 : 0], s));
     }
     m->pos = pos + 1;
+    return W4_OK;
+}
+
+extern "C" w4_status w4_model_prefill(w4_model *m, int32_t pos, int32_t n_tokens, void *stream) {
+    clear_error();
+    W4_CHECK(m != nullptr, W4_ESTATE, "no model");
+    W4_CHECK(m->n_prompt >= 1, W4_ESTATE, "w4_model_reset was not called");
+    W4_CHECK(pos == m->pos, W4_ESTATE, "position %d out of sequence (model is at %d)", pos, m->pos);
+    W4_CHECK(n_tokens >= 1 && n_tokens <= kPrefillMax, W4_EINVAL, "n_tokens=%d outside [1, %d]", n_tokens,
+             kPrefillMax);
+    W4_CHECK(pos + n_tokens <= m->cfg.max_pages * kPage, W4_ENOSPC, "positions up to %d beyond the KV pool (%d tokens)",
+             pos + n_tokens - 1, m->cfg.max_pages * kPage);
+    W4_HIP(enqueue_prefill(m, pos, n_tokens, static_cast<hipStream_t>(stream)));
+    m->pos = pos + n_tokens;
     return W4_OK;
 }
 

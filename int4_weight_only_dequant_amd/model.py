@@ -101,6 +101,10 @@ class DecodeModel:
     def step(self, flags: int = L.W4_GRAPH, stream=None) -> None:
         decode_step(self, self.pos, flags, stream)
 
+    def prefill(self, n_tokens: int, stream=None) -> None:
+        """Prefill n_tokens positions from the current one (one call, up to 512 tokens)."""
+        prefill(self, self.pos, n_tokens, stream)
+
     def device_error(self) -> int:
         """Synchronise and return the persistent step's error word (0 = ok)."""
         v = C.c_int32()
@@ -133,3 +137,8 @@ class DecodeModel:
 def decode_step(model: DecodeModel, pos: int, flags: int = L.W4_GRAPH, stream=None) -> None:
     """One decode step at position pos (graph replay by default)."""
     L.check(L.lib().decode_step(model._m, int(pos), int(flags), L._stream(stream)))
+
+
+def prefill(model: DecodeModel, pos: int, n_tokens: int, stream=None) -> None:
+    """Prefill tokens[pos : pos + n_tokens] (logits of the last one, greedy token after it)."""
+    L.check(L.lib().w4_model_prefill(model._m, int(pos), int(n_tokens), L._stream(stream)))

@@ -13,7 +13,8 @@ with ``layer = 1000`` for tensors that do not belong to a decoder layer.
 Tensor ids: 0/1 QKV codes/scales, 2/3 O, 4/5 gate, 6/7 up, 8/9 down,
 10 pre-attention norm, 11 pre-MLP norm, 12 QKV bias, 20 embeddings,
 21 lm_head, 22 final norm, 30 prompt ids, 31 page free list,
-40 activation x, 41 attention q, 42 K pool, 43 V pool.
+40 activation x, 41 attention q, 42 K pool, 43 V pool, 44 prefill
+activation rows X, 45 prefill queries Q.
 
 Distributions (the workloads' recipe):
 
@@ -46,6 +47,7 @@ T_LN1, T_LN2, T_BQKV = 10, 11, 12
 T_EMBED, T_LMHEAD, T_LNF = 20, 21, 22
 T_PROMPT, T_FREELIST = 30, 31
 T_X, T_Q, T_K, T_V = 40, 41, 42, 43
+T_XM, T_QM = 44, 45
 
 
 @dataclass(frozen=True)
@@ -167,6 +169,23 @@ def attn_case(ctx: int, n_qh: int = 28, n_kvh: int = 4, head_dim: int = 128,
     else:
         perm = np.arange(n_pages)
     table = perm[:need].astype(np.int32)
+    return q, kp, vp, table
+
+
+def gemm_case(m: int, n: int, k: int, cfg: int = 4, seed: int = SEED, layer: int = GLOBAL_LAYER):
+    """One prefill GEMM problem: codes [n,k], scales [n,k/128], X fp16 [m,k]."""
+    q, s = int4_matrix(cfg, layer, T_O_Q, T_O_S, n, k, seed)
+    x = normal_f16(rng(cfg, layer, T_XM, seed), (m, k))
+    return q, s, x
+
+
+def prefill_attn_case(pos0: int, m: int, n_qh: int = 28, n_kvh: int = 4, head_dim: int = 128,
+                      n_pages: int | None = None, cfg: int = 4, seed: int = SEED):
+    """Prefill attention inputs: queries fp16 [m, n_qh, head_dim] at positions
+    pos0 .. pos0 + m - 1, and paged K/V (shuffled pages) for positions
+    0 .. pos0 + m - 1, as in attn_case."""
+    _, kp, vp, table = attn_case(pos0 + m, n_qh, n_kvh, head_dim, n_pages, cfg, seed)
+    q = normal_f16(rng(cfg, GLOBAL_LAYER, T_QM, seed), (m, n_qh, head_dim))
     return q, kp, vp, table
 
 

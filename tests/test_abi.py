@@ -44,7 +44,20 @@ def test_host_side_argument_errors():
     assert lib.paged_attn_decode(p, p, p, p, 641, 28, 4, 128, 40, 0.1, p, p, 1 << 16, None) == L.W4_EINVAL
     assert lib.paged_attn_decode(p, p, p, p, 0, 28, 4, 128, 40, 0.1, p, p, 1 << 16, None) == L.W4_EINVAL
     assert lib.w4a16_mlp(p, p, p, p, p, p, p, 100, 256, p, 1 << 16, None) == L.W4_EINVAL
+    # prefill GEMM: K, M range, alignment, workspace
+    assert lib.w4a16_gemm(p, p, p, p, 64, 256, 100, p, 1 << 16, None) == L.W4_EINVAL
+    assert lib.w4a16_gemm(p, p, p, p, 0, 256, 128, p, 1 << 16, None) == L.W4_EINVAL
+    assert lib.w4a16_gemm(p, p, p + 2, p, 64, 256, 128, p, 1 << 16, None) == L.W4_EALIGN
+    assert lib.w4a16_gemm(p, p, p, p, 512, 3584, 3584, p, 16, None) == L.W4_EINVAL
+    assert lib.w4_gemm_ws_bytes(512, 3584, 3584) >= 4 * 512 * 3584 and lib.w4_gemm_ws_bytes(1, 64, 100) == 0
+    # prefill attention: head_dim, head ratio, token count, scale
+    assert lib.paged_attn_prefill(p, p, p, p, 0, 16, 28, 4, 64, 0.1, p, None) == L.W4_EINVAL
+    assert lib.paged_attn_prefill(p, p, p, p, 0, 16, 12, 8, 128, 0.1, p, None) == L.W4_EINVAL
+    assert lib.paged_attn_prefill(p, p, p, p, 0, 0, 28, 4, 128, 0.1, p, None) == L.W4_EINVAL
+    assert lib.paged_attn_prefill(p, p, p, p, 0, 16, 28, 4, 128, 0.0, p, None) == L.W4_EINVAL
+    assert lib.paged_attn_prefill(p, p + 2, p, p, 0, 16, 28, 4, 128, 0.1, p, None) == L.W4_EALIGN
     # model calls without a model
+    assert lib.w4_model_prefill(None, 0, 16, None) == L.W4_ESTATE
     assert lib.decode_step(None, 0, 0, None) == L.W4_ESTATE
     assert lib.w4_model_reset(None, 1, None) == L.W4_ESTATE
     assert lib.w4_model_pos(None) == -1
