@@ -47,6 +47,7 @@ PAGES_PUBLISHED_TTFT_MS = 128.0  # the pages' runtime, 512-token prompt, H100 (c
 PAGES_PUBLISHED_TOKS = 60.0    # the pages' runtime on an H100 for this workload (context)
 TRAFFIC_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_traffic.md")
 STATS_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_persistent_kernel_stats.md")
+PREFILL_MD = os.path.join(HERE, "profiles", "prefill_qwen7b_512_kernel_stats.md")
 KERNEL = "decode_persistent_kernel"
 CALIB_BYTES = 256 << 20        # device-to-device copy used to calibrate the byte counters
 
@@ -279,6 +280,51 @@ def summarize_trace(d: str, steps: int, cmd: str):
     print("\n".join(lines))
 
 
+def summarize_prefill_trace(d: str, cmd: str):
+    """Per-kernel times of the last 512-token prefill in a kernel trace of this
+    file (the bench runs the prefill 4 times before the decode steps)."""
+    import collections
+    path = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if "pf_embed_kernel" in r["Kernel_Name"]]
+    s = starts[-1]
+    e = next(i for i in range(s, len(rows)) if "finalize_kernel" in rows[i]["Kernel_Name"]) + 1
+    agg, cnt = collections.defaultdict(float), collections.Counter()
+    per_layer = collections.defaultdict(list)
+    gemm_kind = ["QKV (N=4608, K=3584)", "O (N=3584, K=3584)", "gate+up + SwiGLU (N=37888, K=3584)",
+                 "down (N=3584, K=18944)"]
+    gi = 0
+    for r in rows[s:e]:
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        k = r["Kernel_Name"].split("(")[0].replace("w4::", "").replace("void ", "")
+        agg[k] += us
+        cnt[k] += 1
+        if "w4_gemm_kernel" in k:
+            per_layer[gemm_kind[gi % 4]].append(us)
+            gi += 1
+    span = (int(rows[e - 1]["End_Timestamp"]) - int(rows[s]["Start_Timestamp"])) / 1e3
+    flops = {"QKV (N=4608, K=3584)": 2 * 512 * 4608 * 3584, "O (N=3584, K=3584)": 2 * 512 * 3584 * 3584,
+             "gate+up + SwiGLU (N=37888, K=3584)": 2 * 512 * 37888 * 3584,
+             "down (N=3584, K=18944)": 2 * 512 * 3584 * 18944}
+    out = ["# Prefill of a 512-token prompt, Qwen2.5-7B shape: kernel times", "",
+           "Command (from the repository root on one MI355X):", "", "```", cmd, "```", "",
+           f"Last of the bench's 4 prefill calls: {e - s} dispatches, first-to-last span {span:.1f} us "
+           f"(kernel time {sum(agg.values()):.1f} us).", "",
+           "| kernel | calls | total us | us/call |", "|---|---|---|---|"]
+    for k, v in sorted(agg.items(), key=lambda x: -x[1]):
+        out.append(f"| `{k}` | {cnt[k]} | {v:.1f} | {v / cnt[k]:.2f} |")
+    out += ["", "W4A16 GEMM per projection (mean over the 28 layers; fp16 MFMA peak 2500 TFLOP/s):", "",
+            "| projection | us | TFLOP/s | fraction of peak |", "|---|---|---|---|"]
+    for k, v in per_layer.items():
+        m = sum(v) / len(v)
+        tf = flops[k] / (m * 1e-6) / 1e12
+        out.append(f"| {k} | {m:.1f} | {tf:.0f} | {tf / MFMA_F16_PEAK_TFLOPS:.3f} |")
+    os.makedirs(os.path.dirname(PREFILL_MD), exist_ok=True)
+    open(PREFILL_MD, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +336,7 @@ def main():
     ap.add_argument("--measure-traffic", metavar="OUT_DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--trace-command", default="")
+    ap.add_argument("--summarize-prefill-trace", metavar="DIR")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -301,6 +348,8 @@ def main():
         return measure_traffic(args.measure_traffic)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args.steps, args.trace_command)
+    if args.summarize_prefill_trace:
+        return summarize_prefill_trace(args.summarize_prefill_trace, args.trace_command)
 
     import torch
     import synth

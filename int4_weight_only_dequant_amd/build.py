@@ -31,7 +31,7 @@ def build(verbose: bool = False) -> str:
     out_tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument",
+           "-Wno-unused-command-line-argument", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            f"-I{INCLUDE}", f"-I{CSRC}", "-o", out_tmp]
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:

@@ -21,18 +21,20 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPrefillMax = W4_PREFILL_MAX;   // tokens per prefill call
-constexpr int kGemmBM = 64;          // tokens per GEMM work-group
-constexpr int kGemmXs = 136;         // LDS row stride of the staged activations (halves, 128 + pad)
+constexpr int kGemmBM = 128;         // tokens per GEMM work-group (and per wave)
 
 // ------------------------------------------------------------ W4A16 GEMM --
 //
 // out[s][m][n] = sum over the groups g of split s of
 //                s[n][g] * sum_{k in g} x[m][k] * q[n][k]
 //
-// A work-group computes 64 tokens x 256 packed rows (4 waves, one 64-row
-// block each) over the groups of its split.  Per group of 128 K:
-//  - the 64 x 128 activation tile is staged in LDS (double-buffered, loaded
-//    one group ahead);
+// A work-group computes 128 tokens x 128 packed rows (4 waves, each all 128
+// tokens x 32 rows, so every dequantised weight operand feeds 4 MFMAs) over
+// the groups of its split.  Per group of 128 K:
+//  - the 128 x 128 activation tile is staged in LDS by direct global->LDS
+//    loads (16 bytes per lane, double-buffered, one group ahead); the 16-byte
+//    chunk c of row r sits at chunk c ^ (r % 16) of its LDS row, so that the
+//    operand reads of 16 consecutive rows at one chunk hit distinct banks;
 //  - each wave loads its row block's codes for the group straight into
 //    registers (one group ahead) in the packer's lane layout, and turns them
 //    into exact small-integer fp16 operands;
@@ -50,11 +52,12 @@ struct GemmProblem {
     const u32x4 *wq;        // packed codes
     const uint16_t *ws;     // packed scales
     const uint16_t *x;      // fp16 [M][K]
-    float *out;             // fp32 [n_split][M][N]
+    float *out;             // fp32 [n_split][M][N]  (plain store)
+    uint16_t *h;            // fp16 [M][N/2]        (SwiGLU epilogue)
     int M, N;               // tokens, valid packed rows
     int n_rb, n_chunks, n_groups;
     int n_split, gps;       // splits of the groups, groups per split
-    int n_nb, n_mb, n_cols; // 256-row blocks, 64-token blocks, n_split * n_nb
+    int n_nb, n_mb, n_cols; // 128-row blocks, 128-token blocks, n_split * n_nb
     size_t split_stride;    // M * N
 };
 
@@ -76,9 +79,13 @@ __device__ __forceinline__ h8 dequant8(uint32_t w, uint32_t m_lo, uint32_t m_hi)
     return r;
 }
 
+// kSwiGLU: the rows are the W4_PERM_GATE_UP interleave (gate i, up i) and the
+// launch has one split; the epilogue writes h[m][i] = fp16(silu(gate) * up)
+// instead of the fp32 products.
+template <bool kSwiGLU>
 __global__ __launch_bounds__(kThreads) void w4_gemm_kernel(GemmProblem p) {
-    __shared__ __attribute__((aligned(16))) uint16_t sx[2][kGemmBM * kGemmXs];
-    // work-group -> (M block, split, 256-row block): the M blocks of one
+    __shared__ __attribute__((aligned(16))) uint16_t sx[2][kGemmBM * kGroup];
+    // work-group -> (M block, split, 128-row block): the M blocks of one
     // weight column run back to back on one XCD (work-groups are dealt to the
     // 8 XCDs round-robin), so its codes are fetched from HBM about once.
     const int b = blockIdx.x;
@@ -93,126 +100,119 @@ __global__ __launch_bounds__(kThreads) void w4_gemm_kernel(GemmProblem p) {
     const int wave = wave_id();
     const int lane = threadIdx.x & 63;
     const int c32 = lane & 31, hf = lane >> 5;
-    const int rb = nb * 4 + wave;
+    // wave -> 32 rows: half (wave & 1) of row block 2 nb + wave / 2
+    const int rb = nb * 2 + (wave >> 1);
+    const int rh = wave & 1;
     const bool wv = rb < p.n_rb;
     const int m0 = mb * kGemmBM;
 
-    // activation staging: thread -> rows xr + 16 r, 16-byte column xc
-    const int xr = threadIdx.x >> 4, xc = threadIdx.x & 15;
-    u32x4 xreg[4];
-    auto load_x = [&](int g) {
+    // activation staging: wave w fills rows 32 w .. 32 w + 31, four rows per
+    // load instruction; lane -> row 32 w + 4 j + lane / 16, LDS chunk lane % 16
+    // holding logical chunk (lane % 16) ^ (row % 16).  Rows past M repeat row
+    // M - 1 (their products are never stored).
+    const size_t ldx = static_cast<size_t>(p.n_groups) * kGroup;
+    const int xrow0 = 32 * wave + (lane >> 4);
+    auto load_x = [&](int g, int buf) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + xr + 16 * r;
-            if (row < p.M)
-                xreg[r] = *reinterpret_cast<const u32x4 *>(p.x + static_cast<size_t>(row) * (p.n_groups * kGroup) +
-                                                           g * kGroup + xc * 8);
-            else
-                xreg[r] = u32x4{0u, 0u, 0u, 0u};
+        for (int jj = 0; jj < 8; ++jj) {
+            const int row = xrow0 + 4 * jj;      // row % 16 = (xrow0 + 4 jj) % 16
+            const int chunk = (lane & 15) ^ (row & 15);
+            const uint16_t *src = p.x + static_cast<size_t>(min(m0 + row, p.M - 1)) * ldx + chunk * 8 + g * kGroup;
+            __builtin_amdgcn_global_load_lds(src, &sx[buf][(32 * wave + 4 * jj) * kGroup], 16, 0, 0);
         }
     };
-    auto store_x = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<u32x4 *>(&sx[buf][(xr + 16 * r) * kGemmXs + xc * 8]) = xreg[r];
-    };
-    // codes: [n-subtile][chunk 0/1], scales: [n-subtile]
-    u32x4 wreg[2][2];
-    uint16_t sreg[2];
-    const u32x4 *wrow = p.wq + static_cast<size_t>(rb) * p.n_chunks * kRows + c32;
-    const uint16_t *srow = p.ws + static_cast<size_t>(rb) * p.n_groups * kRows + c32;
+    // codes of the lane's row for the group: chunks 2 hf and 2 hf + 1
+    u32x4 wreg[2];
+    uint16_t sreg = 0;
+    const u32x4 *wrow = p.wq + static_cast<size_t>(rb) * p.n_chunks * kRows + 32 * rh + c32;
+    const uint16_t *srow = p.ws + static_cast<size_t>(rb) * p.n_groups * kRows + 32 * rh + c32;
     auto load_w = [&](int g) {
         if (!wv) return;
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-#pragma unroll
-            for (int co = 0; co < 2; ++co)
-                wreg[ns][co] = wrow[static_cast<size_t>(4 * g + 2 * hf + co) * kRows + 32 * ns];
-            sreg[ns] = srow[static_cast<size_t>(g) * kRows + 32 * ns];
-        }
+        for (int co = 0; co < 2; ++co) wreg[co] = wrow[static_cast<size_t>(4 * g + 2 * hf + co) * kRows];
+        sreg = srow[static_cast<size_t>(g) * kRows];
     };
 
-    double acc[2][2][16];
+    double acc[4][16];      // [token sub-tile][C register]
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[a][c][i] = 0.0;
+        for (int i = 0; i < 16; ++i) acc[a][i] = 0.0;
 
     const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u);
-    load_x(g0);
+    load_x(g0, 0);
     load_w(g0);
-    store_x(0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int g = g0; g < g1; ++g) {
         const int buf = (g - g0) & 1;
-        u32x4 wc[2][2];
-        uint16_t sc[2];
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-            wc[ns][0] = wreg[ns][0];
-            wc[ns][1] = wreg[ns][1];
-            sc[ns] = sreg[ns];
-        }
+        const u32x4 wc0 = wreg[0], wc1 = wreg[1];
+        const double sc = static_cast<double>(f16_to_f32(sreg));
         const bool more = g + 1 < g1;
         if (more) {
-            load_x(g + 1);
+            load_x(g + 1, buf ^ 1);
             load_w(g + 1);
         }
         if (wv) {
-            f32x16 t[2][2];
-            const uint16_t *xa = &sx[buf][c32 * kGemmXs + 64 * hf];
+            f32x16 t[4];
+            // rows c32 + 32 ms share row % 16, hence one chunk swizzle
+            const uint16_t *xa = &sx[buf][c32 * kGroup];
+            const int sw = c32 & 15;
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
-                h8 a[2];
+                const int ch = ((8 * hf + st) ^ sw) * 8;
+                const uint32_t wword = st < 4 ? wc0[st] : wc1[st - 4];
+                const h8 bq = dequant8(wword, m_lo, m_hi);
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
-                    a[ms] = *reinterpret_cast<const h8 *>(xa + 32 * ms * kGemmXs + 8 * st);
-#pragma unroll
-                for (int ns = 0; ns < 2; ++ns) {
-                    const h8 bq = dequant8(wc[ns][st >> 2][st & 3], m_lo, m_hi);
-#pragma unroll
-                    for (int ms = 0; ms < 2; ++ms) {
-                        if (st == 0) {
-                            f32x16 z;
-                            for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-                            t[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ms], bq, z, 0, 0, 0);
-                        } else {
-                            t[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ms], bq, t[ms][ns], 0, 0, 0);
-                        }
+                for (int ms = 0; ms < 4; ++ms) {
+                    const h8 a = *reinterpret_cast<const h8 *>(xa + 32 * ms * kGroup + ch);
+                    if (st == 0) {
+                        f32x16 z;
+                        for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+                        t[ms] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq, z, 0, 0, 0);
+                    } else {
+                        t[ms] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq, t[ms], 0, 0, 0);
                     }
                 }
             }
 #pragma unroll
-            for (int ns = 0; ns < 2; ++ns) {
-                const double s = static_cast<double>(f16_to_f32(sc[ns]));
+            for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        acc[ms][ns][i] = fma(s, static_cast<double>(t[ms][ns][i]), acc[ms][ns][i]);
-            }
+                for (int i = 0; i < 16; ++i) acc[ms][i] = fma(sc, static_cast<double>(t[ms][i]), acc[ms][i]);
         }
-        if (more) store_x(buf ^ 1);
+        // the next group's tile has landed in LDS (direct loads are counted
+        // by vmcnt) before any wave passes the barrier
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     if (!wv) return;
     // C layout of a 32x32 tile: lane holds column c32 (a packed row) and the
     // 16 rows (tokens) 8 (i / 4) + 4 hf + i % 4.
-    float *out = p.out + static_cast<size_t>(split) * p.split_stride;
+    const int n = rb * kRows + 32 * rh + c32;
+    if constexpr (kSwiGLU) {
+        // gate (even column) and up (odd column) sit in neighbouring lanes
+        const int half_n = p.N / 2;
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-        const int n = rb * kRows + 32 * ns + c32;
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
+        for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+                const double g = acc[ms][i];
+                const double u = shfl_xor1(g);
                 const int m = m0 + 32 * ms + 8 * (i >> 2) + 4 * hf + (i & 3);
-                if (m < p.M) out[static_cast<size_t>(m) * p.N + n] = static_cast<float>(acc[ms][ns][i]);
+                if ((c32 & 1) == 0 && m < p.M && n < p.N)
+                    p.h[static_cast<size_t>(m) * half_n + (n >> 1)] = f64_to_f16(g / (1.0 + exp(-g)) * u);
             }
+        return;
     }
+    if (n >= p.N) return;
+    float *out = p.out + static_cast<size_t>(split) * p.split_stride;
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = m0 + 32 * ms + 8 * (i >> 2) + 4 * hf + (i & 3);
+            if (m < p.M) out[static_cast<size_t>(m) * p.N + n] = static_cast<float>(acc[ms][i]);
+        }
 }
 
 // y[m][n] = sum of the splits in order (fp64), stored as fp32.
@@ -323,38 +323,60 @@ __global__ __launch_bounds__(kThreads) void pf_qkv_kernel(const float *part, int
     }
 }
 
-// x[m] += sum of the GEMM splits (fp64 sum, stored fp32); a[m] = fp16(RMSNorm(x[m]) * w).
+// x[m] += sum of the GEMM splits (fp64 sum in split order, stored fp32);
+// a[m] = fp16(RMSNorm(x[m]) * w).  Four elements per thread step (d % 128 == 0).
 __global__ __launch_bounds__(kThreads) void pf_resid_norm_kernel(const float *part, int n_split, size_t stride,
                                                                  int d, float *x, const uint16_t *w, double eps,
                                                                  uint16_t *a) {
     __shared__ double red[kThreads / 64];
     const int m = blockIdx.x;
-    float *xr = x + static_cast<size_t>(m) * d;
-    const float *row = part + static_cast<size_t>(m) * d;
-    for (int i = threadIdx.x; i < d; i += kThreads) {
-        double v = static_cast<double>(xr[i]);
-        double acc = 0.0;
-        for (int s = 0; s < n_split; ++s) acc += static_cast<double>(row[s * stride + i]);
-        xr[i] = static_cast<float>(v + acc);
-    }
-    __syncthreads();
-    row_norm(xr, w, a + static_cast<size_t>(m) * d, d, eps, red);
-}
-
-// h[m][i] = fp16(silu(g) * u); packed gate/up rows interleave gate i (2i) and up i (2i + 1).
-__global__ __launch_bounds__(kThreads) void pf_swiglu_kernel(const float *part, int n_split, size_t stride, int f,
-                                                             uint16_t *h) {
-    const int m = blockIdx.x;
-    const float *row = part + static_cast<size_t>(m) * 2 * f;
-    uint16_t *hr = h + static_cast<size_t>(m) * f;
-    for (int i = threadIdx.x; i < f; i += kThreads) {
-        double g = 0.0, u = 0.0;
-        for (int s = 0; s < n_split; ++s) {
-            const float2 v = *reinterpret_cast<const float2 *>(row + s * stride + 2 * i);
-            g += static_cast<double>(v.x);
-            u += static_cast<double>(v.y);
+    float4 *xr = reinterpret_cast<float4 *>(x + static_cast<size_t>(m) * d);
+    const float4 *row = reinterpret_cast<const float4 *>(part + static_cast<size_t>(m) * d);
+    const size_t st4 = stride / 4;
+    const int d4 = d / 4;
+    constexpr int kMaxV = 8;                       // d <= 8 * 4 * 256 (the model allows d <= 4096)
+    float4 xv[kMaxV];
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        if (i < d4) {
+            const float4 x0 = xr[i];
+            double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+            for (int s = 0; s < n_split; ++s) {
+                const float4 v = row[s * st4 + i];
+                s0 += static_cast<double>(v.x);
+                s1 += static_cast<double>(v.y);
+                s2 += static_cast<double>(v.z);
+                s3 += static_cast<double>(v.w);
+            }
+            float4 y;
+            y.x = static_cast<float>(static_cast<double>(x0.x) + s0);
+            y.y = static_cast<float>(static_cast<double>(x0.y) + s1);
+            y.z = static_cast<float>(static_cast<double>(x0.z) + s2);
+            y.w = static_cast<float>(static_cast<double>(x0.w) + s3);
+            xr[i] = y;
+            xv[j] = y;
+            ss += static_cast<double>(y.x) * y.x + static_cast<double>(y.y) * y.y +
+                  static_cast<double>(y.z) * y.z + static_cast<double>(y.w) * y.w;
         }
-        hr[i] = f64_to_f16(g / (1.0 + exp(-g)) * u);
+    }
+    ss = block_sum4(ss, red);
+    const double r = sqrt(ss / d + eps);
+    const uint32_t *w2 = reinterpret_cast<const uint32_t *>(w);   // norm weights are 4-byte aligned
+    uint2 *ar = reinterpret_cast<uint2 *>(a + static_cast<size_t>(m) * d);
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        if (i < d4) {
+            const uint2 wv = uint2{w2[2 * i], w2[2 * i + 1]};
+            const float4 y = xv[j];
+            const uint32_t h0 = f64_to_f16(static_cast<double>(y.x) / r * f16_to_f32(static_cast<uint16_t>(wv.x)));
+            const uint32_t h1 = f64_to_f16(static_cast<double>(y.y) / r * f16_to_f32(static_cast<uint16_t>(wv.x >> 16)));
+            const uint32_t h2v = f64_to_f16(static_cast<double>(y.z) / r * f16_to_f32(static_cast<uint16_t>(wv.y)));
+            const uint32_t h3 = f64_to_f16(static_cast<double>(y.w) / r * f16_to_f32(static_cast<uint16_t>(wv.y >> 16)));
+            ar[i] = uint2{h0 | (h1 << 16), h2v | (h3 << 16)};
+        }
     }
 }
 

@@ -285,18 +285,18 @@ struct GemmGeom {
     int n_rb, n_nb, n_mb, n_groups, n_split, gps, n_cols, grid;
 };
 
-// Launch geometry of w4_gemm_kernel: 64-token x 256-row tiles, the groups
+// Launch geometry of w4_gemm_kernel: 128-token x 128-row tiles, the groups
 // split so that the launch has about kGemmTarget work-groups (at most 8
 // splits), the grid padded to a multiple of 8 columns for the XCD mapping.
-static GemmGeom gemm_geom(int M, int N, int K) {
+static GemmGeom gemm_geom(int M, int N, int K, int max_split = 8) {
     GemmGeom g;
     g.n_rb = (N + kRows - 1) / kRows;
-    g.n_nb = (g.n_rb + 3) / 4;
+    g.n_nb = (g.n_rb + 1) / 2;
     g.n_mb = (M + kGemmBM - 1) / kGemmBM;
     g.n_groups = K / kGroup;
     const int base = g.n_mb * g.n_nb;
     int s = (kGemmTarget + base - 1) / base;
-    s = std::max(1, std::min(std::min(s, 8), g.n_groups));
+    s = std::max(1, std::min(std::min(s, max_split), g.n_groups));
     g.gps = (g.n_groups + s - 1) / s;
     g.n_split = (g.n_groups + g.gps - 1) / g.gps;
     g.n_cols = g.n_split * g.n_nb;
@@ -304,13 +304,16 @@ static GemmGeom gemm_geom(int M, int N, int K) {
     return g;
 }
 
+// out != nullptr: fp32 split partials; otherwise (one split) the SwiGLU
+// epilogue writes fp16 h [M][N/2].
 static hipError_t launch_gemm(const GemmGeom &g, const uint8_t *q, const uint16_t *s, const uint16_t *x, int M,
-                              int N, float *out, hipStream_t st) {
+                              int N, float *out, hipStream_t st, uint16_t *h = nullptr) {
     GemmProblem p;
     p.wq = reinterpret_cast<const u32x4 *>(q);
     p.ws = s;
     p.x = x;
     p.out = out;
+    p.h = h;
     p.M = M;
     p.N = N;
     p.n_rb = g.n_rb;
@@ -322,7 +325,12 @@ static hipError_t launch_gemm(const GemmGeom &g, const uint8_t *q, const uint16_
     p.n_mb = g.n_mb;
     p.n_cols = g.n_cols;
     p.split_stride = static_cast<size_t>(M) * N;
-    hipLaunchKernelGGL(w4_gemm_kernel, dim3(g.grid), dim3(kThreads), 0, st, p);
+    if (out != nullptr) {
+        hipLaunchKernelGGL(w4_gemm_kernel<false>, dim3(g.grid), dim3(kThreads), 0, st, p);
+    } else {
+        if (g.n_split != 1 || h == nullptr || N % 2) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(w4_gemm_kernel<true>, dim3(g.grid), dim3(kThreads), 0, st, p);
+    }
     return hipGetLastError();
 }
 
@@ -602,7 +610,6 @@ static w4_status setup_prefill(w4_model *m) {
     const size_t R = kPrefillMax;
     size_t part = gemm_part_floats_max(kPrefillMax, qkv_rows, d);
     part = std::max(part, gemm_part_floats_max(kPrefillMax, d, qd));
-    part = std::max(part, gemm_part_floats_max(kPrefillMax, 2 * f, d));
     part = std::max(part, gemm_part_floats_max(kPrefillMax, d, f));
     const size_t sizes[6] = {align256(R * d * 4), align256(R * d * 2), align256(R * qd * 2),
                              align256(R * qd * 2), align256(R * f * 2), align256(part * 4)};
@@ -637,7 +644,7 @@ static hipError_t enqueue_prefill(w4_model *m, int pos0, int M, hipStream_t s) {
     } while (0)
     W4_PF(hipLaunchKernelGGL(pf_embed_kernel, dim3(M), dim3(kThreads), 0, s, m->embed, m->tokens, pos0, M, d,
                              m->ln1[0], eps, m->pf_x, m->pf_a, m->page_table, m->free_list, m->state));
-    const GemmGeom g_qkv = gemm_geom(M, qkv_rows, d), g_o = gemm_geom(M, d, qd), g_gu = gemm_geom(M, 2 * f, d),
+    const GemmGeom g_qkv = gemm_geom(M, qkv_rows, d), g_o = gemm_geom(M, d, qd), g_gu = gemm_geom(M, 2 * f, d, 1),
                    g_dn = gemm_geom(M, d, f);
     for (int l = 0; l < c.n_layers; ++l) {
         uint16_t *kc = m->k_cache + l * layer_kv_elems(m);
@@ -653,10 +660,8 @@ static hipError_t enqueue_prefill(w4_model *m, int pos0, int M, hipStream_t s) {
         if (e != hipSuccess) return e;
         W4_PF(hipLaunchKernelGGL(pf_resid_norm_kernel, dim3(M), dim3(kThreads), 0, s, m->pf_part, g_o.n_split,
                                  static_cast<size_t>(M) * d, d, m->pf_x, m->ln2[l], eps, m->pf_a));
-        e = launch_gemm(g_gu, m->gu_q[l], m->gu_s[l], m->pf_a, M, 2 * f, m->pf_part, s);
+        e = launch_gemm(g_gu, m->gu_q[l], m->gu_s[l], m->pf_a, M, 2 * f, nullptr, s, m->pf_h);
         if (e != hipSuccess) return e;
-        W4_PF(hipLaunchKernelGGL(pf_swiglu_kernel, dim3(M), dim3(kThreads), 0, s, m->pf_part, g_gu.n_split,
-                                 static_cast<size_t>(M) * 2 * f, f, m->pf_h));
         e = launch_gemm(g_dn, m->down_q[l], m->down_s[l], m->pf_h, M, d, m->pf_part, s);
         if (e != hipSuccess) return e;
         const uint16_t *next_w = l + 1 < c.n_layers ? m->ln1[l + 1] : m->lnf;
