@@ -325,6 +325,78 @@ def summarize_prefill_trace(d: str, cmd: str):
     print("\n".join(out))
 
 
+def long_context(args):
+    """The long-context workload: TTFT of a 512-token prompt (one prefill from
+    an empty cache), then a ctx-token prompt filled by 512-token prefill chunks
+    over a shuffled page table, and args.steps greedy graph steps timed at
+    positions ctx .. ctx + steps - 1.  Prints one JSON line."""
+    import torch
+    import synth
+    from int4_weight_only_dequant_amd import _lib as L
+
+    dims = synth.QWEN7B
+    ctx = args.context
+    t0 = time.time()
+    model, _, max_pages = build_model(dims, ctx, args.steps)
+    prompt = synth.prompt_ids(dims, ctx)
+    stream = torch.cuda.current_stream()
+    ttft = []
+    for r in range(4):
+        model.reset(prompt[:512])
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        model.prefill(512)
+        torch.cuda.synchronize()
+        if r:
+            ttft.append((time.perf_counter() - tp) * 1e3)
+    model.reset(prompt)
+    fill_to = ctx - args.warmup
+    torch.cuda.synchronize()
+    tf = time.perf_counter()
+    while model.pos < fill_to:
+        model.prefill(min(512, fill_to - model.pos))
+    torch.cuda.synchronize()
+    fill_ms = (time.perf_counter() - tf) * 1e3
+    for _ in range(args.warmup):
+        model.step(L.W4_GRAPH)
+    torch.cuda.synchronize()
+    log(f"[bench] {ctx}-token context filled by prefill chunks in {fill_ms:.1f} ms; warmup {args.warmup} steps")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    tstart = time.perf_counter()
+    for i in range(args.steps):
+        ev[i].record(stream)
+        model.step(L.W4_GRAPH)
+    ev[-1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - tstart
+    assert model.device_error() == 0, "device error during the timed steps"
+    step_us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)])
+    boundary = np.array([(ctx + i) % 16 == 0 for i in range(args.steps)])
+    kern_us = float(step_us[~boundary].mean())
+    gen = model.tokens[ctx: ctx + 8].cpu().numpy()
+    model.close()
+    sb = step_bytes(dims, ctx + 1, ctx + args.steps)
+    achieved = sb / (kern_us * 1e-6) / 1e9
+    line = {
+        "metric": f"decode ms/token & tok/s at {ctx}-token context (batch 1); TTFT of a 512-token prompt",
+        "value": round(args.steps / elapsed, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded random-init weights of the Qwen2.5-7B shapes, uniform random prompt ids)",
+        "config": {"workload": f"Qwen2.5-7B-shaped W4A16 decode step, batch 1, {ctx}-token prompt filled by "
+                               f"512-token prefill chunks, {args.steps} greedy graph-captured steps",
+                   "context": f"{ctx + 1}-{ctx + args.steps}", "kv_pages": max_pages, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": f"{KERNEL} (the whole decode step, one launch per token)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(sb), "avg_launch_us": round(kern_us, 2)},
+        "ttft_ms": round(float(np.median(ttft)), 3), "fill_ms": round(fill_ms, 2),
+        "tokens_head": [int(t) for t in gen],
+    }
+    log(f"[bench] done in {time.time() - t0:.0f}s")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +409,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--trace-command", default="")
     ap.add_argument("--summarize-prefill-trace", metavar="DIR")
+    ap.add_argument("--context", type=int, default=512,
+                    help="prompt length; above 512 runs the long-context workload (prefill-filled cache)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -350,6 +424,11 @@ def main():
         return summarize_trace(args.summarize_trace, args.steps, args.trace_command)
     if args.summarize_prefill_trace:
         return summarize_prefill_trace(args.summarize_prefill_trace, args.trace_command)
+
+    if args.context != 512:
+        if args.context < 512 or args.context % 16:
+            sys.exit("--context must be 512 or a larger multiple of 16")
+        return long_context(args)
 
     import torch
     import synth

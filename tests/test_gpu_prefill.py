@@ -198,3 +198,32 @@ def test_tiny_prefill_errors():
         assert model.device_error() == 0
     finally:
         model.close()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_tiny_long_context_chunked_prefill_then_decode():
+    """The long-context protocol on the small model: an 8192-token prompt
+    filled by 16 chunked 512-token prefills over 520 shuffled pages, then
+    greedy decode steps at positions 8192..; logits vs the oracle's
+    teacher-forced pass over the whole sequence."""
+    dims, layers, glob, free = _tiny(106, 520)
+    n_prompt, n_steps = 8192, 16
+    prompt = synth.prompt_ids(dims, n_prompt, cfg=106)
+    say(f"case: tiny model, {n_prompt}-token prompt in 16 prefill chunks + {n_steps} steps, 520 pages")
+    model = w4.DecodeModel(dims, lambda l: layers[l], glob, free, 520)
+    try:
+        lg, tk = _run(model, prompt, [512] * 16, n_steps)
+        assert model.device_error() == 0
+        pt = model.page_table.cpu().numpy()
+    finally:
+        model.close()
+    n_used = (n_prompt + n_steps + 15) // 16
+    assert np.array_equal(pt[:n_used], free[:n_used])
+    positions = np.arange(n_prompt - 1, n_prompt + n_steps)
+    ref = oracle.forward_teacher_forced(dims, layers, glob, tk[: positions[-1] + 1], positions)
+    err = float(np.max(np.abs(lg - ref)))
+    want = [oracle.argmax_first(r) for r in ref]
+    say(f"  max |logit err| {err:.3e}")
+    assert err <= LOGIT_ATOL
+    assert list(tk[n_prompt:]) == want
