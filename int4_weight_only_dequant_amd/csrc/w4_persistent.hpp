@@ -761,25 +761,43 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     for (int c0 = pb; c0 < pe; c0 += kAttPages) {
         if (c0 != pb) att_load(p, L, j, c0, pe, ts, dc, kc, vc);
+        // all scores of the resident pages first (independent dot products
+        // and row reductions), then one rescale and one accumulation pass
+        float sc[kAttPages][4];
+        float mb = -INFINITY;
 #pragma unroll
         for (int pg = 0; pg < kAttPages; ++pg) {
-            if (c0 + pg >= pe) break;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tok = (c0 + pg) * kPage + ts + 4 * i;
-                // the running token's key and value are not in the cache yet
+                // the running token's key is not in the cache yet
                 const u32x4 kk = tok == pos ? knew : kc[pg][i];
-                const u32x4 vv = tok == pos ? vnew : vc[pg][i];
-                float sc = 0.f;
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.x), as_h2(kk.x), sc, false);
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.y), as_h2(kk.y), sc, false);
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.z), as_h2(kk.z), sc, false);
-                sc = __builtin_amdgcn_fdot2(as_h2(qv.w), as_h2(kk.w), sc, false);
-                sc = row16_sum(sc) * p.att_scale_log2;
-                if (tok < ctx) {
-                    const float mn = fmaxf(m, sc);
-                    const float corr = exp2f(m - mn), pw = exp2f(sc - mn);
-                    l = l * corr + pw;
+                float v = 0.f;
+                v = __builtin_amdgcn_fdot2(as_h2(qv.x), as_h2(kk.x), v, false);
+                v = __builtin_amdgcn_fdot2(as_h2(qv.y), as_h2(kk.y), v, false);
+                v = __builtin_amdgcn_fdot2(as_h2(qv.z), as_h2(kk.z), v, false);
+                v = __builtin_amdgcn_fdot2(as_h2(qv.w), as_h2(kk.w), v, false);
+                v = row16_sum(v) * p.att_scale_log2;
+                const bool valid = c0 + pg < pe && tok < ctx;
+                sc[pg][i] = valid ? v : -INFINITY;
+                mb = fmaxf(mb, sc[pg][i]);
+            }
+        }
+        const float mn = fmaxf(m, mb);
+        if (mn != -INFINITY) {
+            const float corr = exp2f(m - mn);
+            l *= corr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= corr;
+#pragma unroll
+            for (int pg = 0; pg < kAttPages; ++pg) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (sc[pg][i] == -INFINITY) continue;
+                    const int tok = (c0 + pg) * kPage + ts + 4 * i;
+                    const u32x4 vv = tok == pos ? vnew : vc[pg][i];
+                    const float pw = exp2f(sc[pg][i] - mn);
+                    l += pw;
                     const h2 v01 = as_h2(vv.x), v23 = as_h2(vv.y);
                     const h2 v45 = as_h2(vv.z), v67 = as_h2(vv.w);
                     const float vf[8] = {static_cast<float>(v01[0]), static_cast<float>(v01[1]),
@@ -787,10 +805,10 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
                                          static_cast<float>(v45[0]), static_cast<float>(v45[1]),
                                          static_cast<float>(v67[0]), static_cast<float>(v67[1])};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * corr + pw * vf[e];
-                    m = mn;
+                    for (int e = 0; e < 8; ++e) acc[e] += pw * vf[e];
                 }
             }
+            m = mn;
         }
     }
     // merge the 4 token rows of the wave (lanes 16 and 32 apart)
