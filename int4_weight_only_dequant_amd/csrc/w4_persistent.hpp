@@ -1003,15 +1003,31 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     // attention chunks of 4 x att_pps pages per head at this context
     const int n_split = (n_pages + 4 * p.att_pps - 1) / (4 * p.att_pps);
 
-    // attention unit (head, chunk) of this work-group (units spread over all
-    // work-groups), if any
+    // attention unit (head, chunk) of this work-group, if any.  The query
+    // heads of one kv head and chunk read the same K/V pages: they go to
+    // work-groups of one XCD (work-groups are dealt to the 8 XCDs
+    // round-robin, so B % 8 is the XCD), where all but the first read of a
+    // page hit that XCD's L2.  If the XCD slots cannot hold every group, the
+    // units are spread over all work-groups instead.
     const int n_units_max = p.n_qh * p.att_smax;
     int att_h = -1, att_s = 0;
     {
-        const int i0 = static_cast<int>((static_cast<int64_t>(B) * n_units_max + p.P - 1) / p.P);
-        if (i0 < n_units_max && tile_owner(i0, n_units_max, p.P) == B) {
-            const int hh = i0 / p.att_smax, ss = i0 - hh * p.att_smax;
-            if (ss < n_split) { att_h = hh; att_s = ss; }
+        const int G = p.n_qh / p.n_kvh;
+        const int n_grp = p.n_kvh * p.att_smax;              // (kv head, chunk) groups
+        const int slots = p.P / 8;                            // work-groups per XCD
+        if (p.P % 8 == 0 && ((n_grp + 7) / 8) * G <= slots) {
+            const int x = B & 7, slot = B >> 3;
+            const int grp = (slot / G) * 8 + x, k = slot % G;
+            if (grp < n_grp) {
+                const int jj = grp / p.att_smax, ss = grp - jj * p.att_smax;
+                if (ss < n_split) { att_h = jj * G + k; att_s = ss; }
+            }
+        } else {
+            const int i0 = static_cast<int>((static_cast<int64_t>(B) * n_units_max + p.P - 1) / p.P);
+            if (i0 < n_units_max && tile_owner(i0, n_units_max, p.P) == B) {
+                const int hh = i0 / p.att_smax, ss = i0 - hh * p.att_smax;
+                if (ss < n_split) { att_h = hh; att_s = ss; }
+            }
         }
     }
 
