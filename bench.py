@@ -15,7 +15,10 @@ bytes of a step over its average duration, from HIP events recorded around
 every timed step on the launch stream), its HBM traffic from the committed
 rocprofv3 counter summary when that summary was taken on the current
 kernel sources, eager-launch ms/token, per-kernel times of the kernel-per-op
-variant, and the CPU oracle timed on a bounded sample on the host cores.
+variant, the standalone C-ABI calls on the single-GEMV, MLP and attention
+shapes (w4a16_gemv, w4a16_mlp, paged_attn_decode; operands rotated over
+>= 1 GiB of copies so the Infinity Cache cannot serve them), and the CPU
+oracle timed on a bounded sample on the host cores.
 
 Measurement modes (run by hand, results committed under profiles/):
   --measure-traffic   runs this file twice under `rocprofv3 --pmc` (FETCH_SIZE,
@@ -397,6 +400,154 @@ def long_context(args):
     print(json.dumps(line), flush=True)
 
 
+
+# ------------------------------------------------------------------------------------------
+# Standalone calls of configs 0-2 through the C ABI, rotating over distinct copies of the
+# operands (>= 1 GiB in total) so that no call finds its weights or pages in the 256 MB
+# Infinity Cache; R calls are captured in one graph and the graph replayed.
+
+ROTATE_BYTES = 1 << 30
+
+
+def _w4_bytes(n, k):
+    """Algorithmic bytes of one W4A16 GEMV: codes, scales, x and the fp16 output."""
+    return n * k // 2 + n * (k // 128) * 2 + k * 2 + n * 2
+
+
+def _graph_time_us(torch, calls, reps=3):
+    """Mean time per call of a list of launch closures, captured once into a
+    graph and replayed `reps` times (after one warmup replay)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls[:2]:
+            c()          # eager warmup outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+    del g
+    return us
+
+
+def standalone_kernels(attention: bool = True):
+    """Configs 0-2 through w4a16_gemv, w4a16_mlp and paged_attn_decode."""
+    import torch
+    import synth
+    import int4_weight_only_dequant_amd as w4
+    from int4_weight_only_dequant_amd import _lib as L
+
+    lib = L.lib()
+    dev = torch.device("cuda")
+    out = {}
+
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
+
+    def rotated(arr_u8, copies):
+        """[copies, nbytes] device buffer, every row a copy of arr_u8."""
+        t = torch.from_numpy(np.ascontiguousarray(arr_u8).view(np.uint8).reshape(-1)).to(dev)
+        buf = torch.empty((copies, t.numel()), dtype=torch.uint8, device=dev)
+        buf.copy_(t.unsqueeze(0).expand(copies, -1))
+        return buf
+
+    def gemv_entry(name, n, k, pq, ps):
+        nb = pq.nbytes + ps.nbytes
+        R = max(2, -(-ROTATE_BYTES // nb))
+        bq, bs = rotated(pq, R), rotated(ps, R)
+        x = torch.from_numpy(synth.normal_f16(synth.rng(0, synth.GLOBAL_LAYER, synth.T_X), (k,))).to(dev)
+        y = torch.empty(n, dtype=torch.float16, device=dev)
+        ws = torch.empty(max(lib.w4_gemv_ws_bytes(n, k), 256), dtype=torch.uint8, device=dev)
+
+        def mk(r):
+            def c():
+                L.check(lib.w4a16_gemv(bq[r].data_ptr(), bs[r].data_ptr(), x.data_ptr(), y.data_ptr(), n, k,
+                                       ws.data_ptr(), ws.numel(), cur()))
+            return c
+        us = _graph_time_us(torch, [mk(r) for r in range(R)])
+        b = _w4_bytes(n, k)
+        out[name] = {"N": n, "K": k, "us_per_call": round(us, 2), "bytes": b,
+                     "GBps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "copies": R}
+        del bq, bs
+
+    # config 0: one 3584 x 3584 GEMV
+    q, s, _ = synth.gemv_cfg0()
+    pq, ps = w4.pack_int4_weights(q, s)
+    gemv_entry("gemv_3584x3584", 3584, 3584, pq, ps)
+    # config 1 shapes as single GEMVs (fp16 output), then the MLP call
+    m = synth.mlp_cfg1()
+    d, f = 3584, 18944
+    cfg = L.ModelConfig(d_model=d, d_ff=f, n_layers=1, n_q_heads=28, n_kv_heads=4, head_dim=128,
+                        vocab=1, max_pages=1, eps=1e-6, theta=1e6)
+    perm = w4.model_row_perm(L.W4_PERM_GATE_UP, cfg)
+    pgq, pgs = w4.pack_int4_weights(np.concatenate([m["gate"][0], m["up"][0]]),
+                                    np.concatenate([m["gate"][1], m["up"][1]]), row_perm=perm)
+    pdq, pds = w4.pack_int4_weights(*m["down"])
+    gemv_entry("gemv_gate_up_37888x3584", 2 * f, d, pgq, pgs)
+    gemv_entry("gemv_down_3584x18944", d, f, pdq, pds)
+    nb = pgq.nbytes + pgs.nbytes + pdq.nbytes + pds.nbytes
+    R = max(2, -(-ROTATE_BYTES // nb))
+    bgq, bgs, bdq, bds = rotated(pgq, R), rotated(pgs, R), rotated(pdq, R), rotated(pds, R)
+    x = torch.from_numpy(m["x"]).to(dev)
+    h = torch.empty(f, dtype=torch.float16, device=dev)
+    y = torch.empty(d, dtype=torch.float16, device=dev)
+    ws = torch.empty(max(lib.w4_mlp_ws_bytes(d, f), 256), dtype=torch.uint8, device=dev)
+
+    def mk_mlp(r):
+        def c():
+            L.check(lib.w4a16_mlp(bgq[r].data_ptr(), bgs[r].data_ptr(), bdq[r].data_ptr(), bds[r].data_ptr(),
+                                  x.data_ptr(), h.data_ptr(), y.data_ptr(), d, f, ws.data_ptr(), ws.numel(), cur()))
+        return c
+    us = _graph_time_us(torch, [mk_mlp(r) for r in range(R)])
+    b = _w4_bytes(2 * f, d) + _w4_bytes(d, f)
+    out["mlp_cfg1"] = {"D": d, "F": f, "us_per_call": round(us, 2), "bytes": b,
+                       "GBps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "launches": 3, "copies": R}
+    del bgq, bgs, bdq, bds
+
+    # config 2: paged decode attention; every call reads its own 40 pages of one large pool
+    for ctx in ((640, 8192) if attention else ()):
+        n_pg = ctx // 16
+        q, kp, vp, table = synth.attn_case(ctx)
+        page_bytes = kp[0].nbytes
+        R = max(2, -(-ROTATE_BYTES // (2 * n_pg * page_bytes)))
+        kt = torch.from_numpy(kp).to(dev)
+        vt = torch.from_numpy(vp).to(dev)
+        kpool = kt.repeat(R, 1, 1, 1)
+        vpool = vt.repeat(R, 1, 1, 1)
+        tables = torch.from_numpy(np.stack([table + r * n_pg for r in range(R)]).astype(np.int32)).to(dev)
+        qt = torch.from_numpy(q).to(dev)
+        o = torch.empty_like(qt)
+        ws = torch.empty(max(lib.w4_attn_ws_bytes(28, 4, n_pg), 256), dtype=torch.uint8, device=dev)
+
+        def mk_att(r):
+            def c():
+                L.check(lib.paged_attn_decode(qt.data_ptr(), kpool.data_ptr(), vpool.data_ptr(), tables[r].data_ptr(),
+                                              ctx, 28, 4, 128, n_pg, float(1 / np.sqrt(128)), o.data_ptr(),
+                                              ws.data_ptr(), ws.numel(), cur()))
+            return c
+        us = _graph_time_us(torch, [mk_att(r) for r in range(R)])
+        b = 2 * n_pg * page_bytes + 2 * q.nbytes + n_pg * 4
+        out[f"attn_ctx{ctx}"] = {"ctx": ctx, "pages": n_pg, "us_per_call": round(us, 2), "bytes": b,
+                                 "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                                 "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "copies": R}
+        del kpool, vpool
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -404,6 +555,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=112)
+    ap.add_argument("--no-standalone", action="store_true",
+                    help="skip the standalone GEMV / MLP / attention calls of configs 0-2")
+    ap.add_argument("--standalone-only", action="store_true",
+                    help="run only the standalone calls of configs 0-2 (for kernel profiles)")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--measure-traffic", metavar="OUT_DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -425,6 +580,12 @@ def main():
     if args.summarize_prefill_trace:
         return summarize_prefill_trace(args.summarize_prefill_trace, args.trace_command)
 
+    if args.standalone_only:
+        res = standalone_kernels()
+        for k_, v_ in res.items():
+            log(f"[bench]   {k_}: {v_['us_per_call']} us/call, {v_['GBps']} GB/s ({v_['frac']:.3f} of peak)")
+        print(json.dumps({"standalone_calls": res}), flush=True)
+        return None
     if args.context != 512:
         if args.context < 512 or args.context % 16:
             sys.exit("--context must be 512 or a larger multiple of 16")
@@ -516,6 +677,17 @@ def main():
         kern[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / r, 2)
     multi_launches = model.launches_per_step(L.W4_MULTI)
     model.close()
+    d_, f_, qd_ = dims.d_model, dims.d_ff, dims.n_q_heads * dims.head_dim
+    for name, (n_, k_) in (("gate_up", (2 * f_, d_)), ("down", (d_, f_)), ("o_proj", (d_, qd_))):
+        kern[name + "_GBps"] = round(_w4_bytes(n_, k_) / (kern[name + "_us"] * 1e-6) / 1e9, 1)
+    kern["lm_head_GBps"] = round((dims.vocab * d_ * 2 + d_ * 2 + dims.vocab * 4) / (kern["lm_head_us"] * 1e-6) / 1e9, 1)
+    standalone = None
+    if not args.no_standalone:
+        log("[bench] standalone calls of configs 0-2 (rotated operands, graph-replayed)")
+        torch.cuda.empty_cache()
+        standalone = standalone_kernels()
+        for k_, v_ in standalone.items():
+            log(f"[bench]   {k_}: {v_['us_per_call']} us/call, {v_['GBps']} GB/s ({v_['frac']:.3f} of peak)")
 
     ctx_lo, ctx_hi = n_prompt + 1, n_prompt + args.steps
     sb = step_bytes(dims, ctx_lo, ctx_hi)
@@ -555,6 +727,7 @@ def main():
         "eager_ms_per_step": round(eager_ms, 3),
         "launches_per_step": launches,
         "kernel_per_op_variant": {"launches_per_step": multi_launches, **kern},
+        "standalone_calls": standalone,
         "tokens_head": [int(t) for t in gen[:16]],
         "prefill": {"ttft_ms": round(ttft_ms, 3), "device_ms": round(ttft_dev_ms, 3), "prompt_tokens": n_prompt,
                     "linear_tflop": round(lin_flop / 1e12, 3),

@@ -104,10 +104,13 @@ w4_status w4_pack_f16_matrix(const uint16_t *w, int64_t N, int64_t K,
  *   x                  : device, fp16 [K]
  *   y                  : device, fp16 [N] (written)
  *   workspace          : device, w4_gemv_ws_bytes(N, K) bytes of scratch
- *                        (split-K partials and arrival counters); no
- *                        initialisation needed, the call clears its counters
- *                        first.  Calls that share a workspace must be ordered
- *                        on one stream.
+ *                        (partial sums of row blocks shared by work-groups,
+ *                        and their arrival counters).  It must be all zero
+ *                        before its first use (e.g. hipMemset once); every
+ *                        call leaves it all zero again, whatever the shape,
+ *                        so it can be reused across shapes without clearing.
+ *                        Calls that share a workspace must be ordered on one
+ *                        stream.
  * Errors: W4_EINVAL (N < 1, K not a positive multiple of 128, workspace too
  * small), W4_EALIGN, W4_EHIP (launch failure). */
 size_t w4_gemv_ws_bytes(int64_t N, int64_t K);
@@ -115,16 +118,16 @@ w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_s,
                      const uint16_t *x, uint16_t *y, int64_t N, int64_t K,
                      void *workspace, size_t ws_bytes, void *stream);
 
-/* The MLP decode block of one token on the same kernels the decode step
- * uses: the fused gate+up GEMV with its SwiGLU epilogue, then the down GEMV
+/* The MLP decode block of one token, two launches of the w4a16_gemv kernel:
+ * the fused gate+up GEMV with its SwiGLU epilogue, then the down GEMV
  * (SwiGLU MLP of the Qwen2.5-7B decode workload; int4 projections as above).
  *   h = fp16( silu(Wg x) * (Wu x) ),   y = fp16( Wd h )
  *   gu_q, gu_s     : device, the [gate ; up] matrix (2F rows, K = D) packed
  *                    with the W4_PERM_GATE_UP row order (see below)
  *   down_q, down_s : device, Wd (D rows, K = F) packed in identity order
  *   x              : device, fp16 [D];  h : fp16 [F] and y : fp16 [D] (written)
- *   workspace      : device, w4_mlp_ws_bytes(D, F) bytes of scratch (as for
- *                    w4a16_gemv)
+ *   workspace      : device, w4_mlp_ws_bytes(D, F) bytes of scratch, zero
+ *                    before first use and left zero (as for w4a16_gemv)
  * D and F must be positive multiples of 128.  Errors as for w4a16_gemv. */
 size_t w4_mlp_ws_bytes(int64_t D, int64_t F);
 w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *down_q,
@@ -171,10 +174,13 @@ w4_status w4a16_gemm(const uint8_t *packed_q, const uint16_t *packed_s,
  *                 valid physical pages of the pools
  *   out         : device, fp16 [n_qh][head_dim] (written)
  *   workspace   : device, w4_attn_ws_bytes(n_qh, n_kvh, n_pages_max) bytes of
- *                 scratch (per-split partials and arrival counters); no
- *                 initialisation needed; calls sharing it must be ordered
- * head_dim must be 128; n_qh a multiple of n_kvh with n_qh / n_kvh in
- * {1, 2, 4, 7, 8}; 1 <= ctx_len <= 16 * n_pages_max.  Otherwise W4_EINVAL. */
+ *                 scratch (per-split partials and arrival counters).  It must
+ *                 be zero before its first use; each call leaves its counter
+ *                 region zero, so reuse (any shape) needs no clearing; calls
+ *                 sharing it must be ordered on one stream
+ * head_dim must be 128; 1 <= n_kvh <= 256; n_qh a multiple of n_kvh with
+ * n_qh / n_kvh in {1, 2, 4, 7, 8}; 1 <= ctx_len <= 16 * n_pages_max.
+ * Otherwise W4_EINVAL. */
 size_t w4_attn_ws_bytes(int32_t n_qh, int32_t n_kvh, int32_t n_pages_max);
 w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool,
                             const uint16_t *v_pool, const int32_t *page_table,

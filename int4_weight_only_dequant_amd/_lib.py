@@ -189,12 +189,12 @@ _ws_cache: dict = {}
 
 
 def _workspace(kind: str, nbytes: int, device: torch.device, stream: int) -> torch.Tensor:
-    """Scratch buffer per (entry point, device, stream), grown on demand; the
-    library clears what it needs at the start of each call."""
+    """Scratch buffer per (entry point, device, stream), grown on demand.  It
+    starts zeroed: the calls need a zero workspace and leave it zero."""
     key = (kind, device.index, stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 

@@ -1,0 +1,197 @@
+// Streaming W4A16 GEMV for the standalone calls (w4a16_gemv, w4a16_mlp).
+//
+// Same arithmetic as w4_gemv_kernel (the pages' fp16-activation path,
+// "Building a Custom LLM Inference Runtime for Qwen2.5-Coder-7B on NVIDIA H100
+// Hopper Architecture", sections "Technical Specifications and Hardware
+// Alignment" and "Engineering Challenges" item 3): nibbles become exact fp16
+// integers in registers, v_dot2 products are summed in fp32 within a
+// 128-element group, and the scaled group sums are accumulated in fp64.
+//
+// What differs is the mapping, chosen so that one launch streams the matrix
+// at the HBM rate instead of paying a wave start-up per group:
+// * The matrix is a row-major sequence of T tiles (64 packed rows x one
+//   128-element K group = 4 KiB of codes + 128 B of scales).  The launch has
+//   P work-groups (about 2 per CU, all resident); work-group B owns the
+//   contiguous tile range [ceil(B T / P), ceil((B+1) T / P)), and its 4 waves
+//   take every 4th tile of it with two tiles in flight (the next tile's loads
+//   are issued before the current one is consumed).
+// * Activations are read through the scalar cache (wave-uniform s_load), so
+//   the activation operand of every dot product is an SGPR.  (Staging them
+//   in LDS and reading 16-byte broadcasts instead measured 5% slower on the
+//   gate+up shape.)
+// * Per row block the waves' fp64 sums are added in wave order in LDS.  A row
+//   block that lies inside one range gets its epilogue at once; otherwise
+//   each owning work-group (consecutive ones) stores its sum in its own slot,
+//   and the last to arrive adds the slots in slot order, runs the epilogue,
+//   and zeroes the slots and the counter.  The summation order depends only
+//   on the shape, so results are deterministic, and the workspace is all
+//   zero again after every call: no clearing launch is needed.
+#pragma once
+
+#include "w4_gemv.hpp"
+
+namespace w4 {
+
+constexpr int kSgMaxRl = 8;          // row blocks one work-group's range may touch
+#ifndef W4_SG_WG_TARGET
+#define W4_SG_WG_TARGET 512
+#endif
+constexpr int kSgWgTarget = W4_SG_WG_TARGET;   // work-groups per launch (2 per CU)
+#ifndef W4_SG_MIN_TILES
+#define W4_SG_MIN_TILES 4
+#endif
+constexpr int kSgMinTiles = W4_SG_MIN_TILES;   // tiles per work-group below which P shrinks
+
+struct SgProblem {
+    const u32x4 *wq;          // packed codes
+    const uint16_t *ws;       // packed scales
+    const uint32_t *x;        // activations as fp16 pairs, K/2 words
+    int ng;                   // K / 128
+    int T;                    // tiles = row blocks * ng
+    int P;                    // work-groups
+    int slot_stride;          // partial slots per shared row block
+    int key_by_rb;            // shared row blocks keyed by row block (else by first owner)
+    double *slots;            // [n_keys][slot_stride][64], zero between calls
+    unsigned *ctr;            // [n_keys] arrival counters, zero between calls
+};
+
+// A row block shared by several work-groups is keyed by its index or by its
+// first owner, whichever set is smaller (a work-group is the first owner of
+// at most one shared row block: the one holding the end of its range).
+struct SgGeom {
+    int T, P, slot_stride, n_keys, key_by_rb;
+};
+
+// P: about kSgWgTarget work-groups, fewer for small matrices (at least
+// kSgMinTiles tiles, one per wave, each), never more than one per tile, and
+// enough that no range touches more than kSgMaxRl row blocks.  slot_stride bounds the
+// work-groups that share one row block.
+inline SgGeom sg_geom(int n_rb, int ng) {
+    SgGeom g;
+    g.T = n_rb * ng;
+    const int64_t r_max = static_cast<int64_t>(kSgMaxRl - 1) * ng + 1;
+    const int p_min = static_cast<int>((g.T + r_max - 1) / r_max);
+    int P = kSgWgTarget;
+    const int p_fill = (g.T + kSgMinTiles - 1) / kSgMinTiles;
+    if (P > p_fill) P = p_fill;
+    if (P < p_min) P = p_min;
+    if (P > g.T) P = g.T;
+    g.P = P;
+    g.slot_stride = static_cast<int>((static_cast<int64_t>(ng - 1) * P) / g.T) + 2;
+    g.key_by_rb = n_rb <= P;
+    g.n_keys = g.key_by_rb ? n_rb : P;
+    return g;
+}
+
+inline size_t sg_ctr_bytes(const SgGeom &g) { return (static_cast<size_t>(g.n_keys) * 4 + 255) & ~size_t(255); }
+
+// Workspace: counters first, then the slots.
+inline size_t sg_ws_bytes(int n_rb, int ng) {
+    const SgGeom g = sg_geom(n_rb, ng);
+    return sg_ctr_bytes(g) + static_cast<size_t>(g.n_keys) * g.slot_stride * 64 * sizeof(double);
+}
+
+__device__ __forceinline__ int sg_range_begin(int B, int T, int P) {
+    return static_cast<int>((static_cast<int64_t>(B) * T + P - 1) / P);
+}
+__device__ __forceinline__ int sg_owner(int t, int T, int P) {
+    return static_cast<int>((static_cast<int64_t>(t) * P) / T);
+}
+
+__device__ __forceinline__ void sg_load(u32x4 (&w)[4], uint16_t &s, const SgProblem &p, int t) {
+    const u32x4 *src = p.wq + static_cast<size_t>(t) * 256 + (threadIdx.x & 63);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = __builtin_nontemporal_load(src + c * 64);
+    s = p.ws[static_cast<size_t>(t) * 64 + (threadIdx.x & 63)];
+}
+
+// One tile's scaled group sum (fp32 inside the group, as in w4_gemv_kernel).
+__device__ __forceinline__ double sg_tile(const u32x4 (&w)[4], uint16_t s, const_u32_ptr xg, uint32_t m_lo,
+                                          uint32_t m_hi, uint32_t magic) {
+    float acc1 = 0.f, acc16 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        dot8(w[c].x, xg + c * 16 + 0, acc1, acc16, m_lo, m_hi, magic);
+        dot8(w[c].y, xg + c * 16 + 4, acc1, acc16, m_lo, m_hi, magic);
+        dot8(w[c].z, xg + c * 16 + 8, acc1, acc16, m_lo, m_hi, magic);
+        dot8(w[c].w, xg + c * 16 + 12, acc1, acc16, m_lo, m_hi, magic);
+    }
+    return static_cast<double>(__builtin_fmaf(acc16, 0.0625f, acc1)) * static_cast<double>(f16_to_f32(s));
+}
+
+template <class Epi>
+__global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi) {
+    __shared__ double red[kSgMaxRl * 256];
+    const int B = blockIdx.x;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int t_begin = sg_range_begin(B, p.T, p.P), t_end = sg_range_begin(B + 1, p.T, p.P);
+    const int rb0 = t_begin / p.ng;
+    const int n_rl = (t_end - 1) / p.ng - rb0 + 1;
+    // each thread clears the slots it later writes (rl, its wave, its lane)
+    for (int i = threadIdx.x; i < n_rl * 256; i += kThreads) red[i] = 0.0;
+
+    const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u);
+    const const_u32_ptr xc = as_const(p.x);
+    u32x4 wa[4], wb[4];
+    uint16_t sa = 0, sb = 0;
+    int t = t_begin + wave;
+    if (t < t_end) sg_load(wa, sa, p, t);
+    int cur = -1;
+    double acc = 0.0;
+    auto consume = [&](const u32x4 (&w)[4], uint16_t s, int tt) {
+        const int rbt = tt / p.ng;
+        const int g = tt - rbt * p.ng;
+        const int rl = rbt - rb0;
+        if (rl != cur) {
+            if (cur >= 0) red[cur * 256 + wave * 64 + lane] = acc;
+            acc = 0.0;
+            cur = rl;
+        }
+        acc += sg_tile(w, s, xc + g * 64, m_lo, m_hi, magic);
+    };
+    while (t < t_end) {
+        if (t + 4 < t_end) sg_load(wb, sb, p, t + 4);
+        consume(wa, sa, t);
+        t += 4;
+        if (t >= t_end) break;
+        if (t + 4 < t_end) sg_load(wa, sa, p, t + 4);
+        consume(wb, sb, t);
+        t += 4;
+    }
+    if (cur >= 0) red[cur * 256 + wave * 64 + lane] = acc;
+    __syncthreads();
+
+    // one wave per row block of the range
+    for (int rl = wave; rl < n_rl; rl += 4) {
+        const double *rr = red + rl * 256 + lane;
+        const double v = ((rr[0] + rr[64]) + rr[128]) + rr[192];
+        const int rb = rb0 + rl;
+        const int a = rb * p.ng;
+        const int row = rb * 64 + lane;
+        if (a >= t_begin && a + p.ng <= t_end) {
+            epi(row, lane, v);
+            continue;
+        }
+        const int first = sg_owner(a, p.T, p.P);
+        const int n_c = sg_owner(a + p.ng - 1, p.T, p.P) - first + 1;
+        const int key = p.key_by_rb ? rb : first;
+        double *base = p.slots + static_cast<size_t>(key) * p.slot_stride * 64 + lane;
+        store_agent(base + (B - first) * 64, v);
+        if (!arrive_last(p.ctr + key, static_cast<unsigned>(n_c))) continue;
+        // all slots in parallel, summed in slot order, then cleared
+        double tot = 0.0;
+        int k = 0;
+        for (; k + 8 <= n_c; k += 8) {
+            double s8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s8[u] = load_agent(base + (k + u) * 64);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) tot += s8[u];
+        }
+        for (; k < n_c; ++k) tot += load_agent(base + k * 64);
+        for (k = 0; k < n_c; ++k) store_agent(base + k * 64, 0.0);
+        epi(row, lane, tot);
+    }
+}
+
+}  // namespace w4

@@ -13,6 +13,7 @@
 
 #include "w4_attn.hpp"
 #include "w4_gemv.hpp"
+#include "w4_gemv_stream.hpp"
 #include "w4_persistent.hpp"
 #include "w4_prefill.hpp"
 
@@ -56,19 +57,6 @@ __global__ void finalize_kernel(StepState *st, int *tokens) {
     const int tok = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFull));
     if (pos + 1 >= st->n_prompt) tokens[pos + 1] = tok;
     st->pos = pos + 1;
-}
-
-// Clears the counter region of a caller-provided workspace at the start of
-// a standalone call: a workspace may be reused across shapes, and a previous
-// call's partials can occupy this call's counter slots.
-__global__ void zero_u32_kernel(unsigned *p, int n) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
-}
-
-static hipError_t zero_counters(void *ws, int n, hipStream_t s) {
-    const int blocks = std::min((n + 255) / 256, 1024);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, s, static_cast<unsigned *>(ws), n);
-    return hipGetLastError();
 }
 
 __global__ void reset_kernel(StepState *st, int n_prompt, unsigned *ctr, int n_ctr, int *err) {
@@ -124,8 +112,14 @@ static size_t gemv_partials(int n_rb, int n_split) {
     return n_split > 1 ? static_cast<size_t>(n_split) * n_rb * 64 : 0;
 }
 
+// The arrival counters sit in a region of fixed size at the start of the
+// workspace, so partials of an earlier call with another shape never land on
+// them; the last work-group of each kv head resets its counter, so a
+// workspace that starts zero needs no clearing between calls.
+constexpr int kAttnMaxKvh = 256;
+
 static size_t attn_ws_bytes(int n_kvh, int G, int n_split) {
-    return align256(static_cast<size_t>(n_kvh) * 4) +
+    return align256(static_cast<size_t>(kAttnMaxKvh) * 4) +
            align256(static_cast<size_t>(n_kvh) * n_split * G * 2 * 4) +
            static_cast<size_t>(n_kvh) * n_split * G * 128 * 4;
 }
@@ -133,7 +127,7 @@ static size_t attn_ws_bytes(int n_kvh, int G, int n_split) {
 static void attn_ws_carve(void *ws, int n_kvh, int G, int n_split, AttnProblem &a) {
     char *b = static_cast<char *>(ws);
     a.counter = reinterpret_cast<unsigned *>(b);
-    b += align256(static_cast<size_t>(n_kvh) * 4);
+    b += align256(static_cast<size_t>(kAttnMaxKvh) * 4);
     a.part_ml = reinterpret_cast<float *>(b);
     b += align256(static_cast<size_t>(n_kvh) * n_split * G * 2 * 4);
     a.part_acc = reinterpret_cast<float *>(b);
@@ -145,10 +139,35 @@ using namespace w4;
 
 // ============================================================ kernel calls ==
 
+// Tiles of a standalone GEMV must fit an int (far beyond any matrix that fits
+// in device memory: 2^31 tiles are 8 TiB of codes).
+static bool sg_shape_ok(int64_t N, int64_t K) {
+    return N >= 1 && K >= kGroup && K % kGroup == 0 && ((N + 63) / 64) * (K / kGroup) < (int64_t(1) << 31);
+}
+
+template <class Epi>
+static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const uint16_t *x, int64_t N, int64_t K,
+                            void *ws, const Epi &epi, hipStream_t s) {
+    const int n_rb = static_cast<int>((N + 63) / 64), ng = static_cast<int>(K / kGroup);
+    const SgGeom g = sg_geom(n_rb, ng);
+    SgProblem p;
+    p.wq = reinterpret_cast<const u32x4 *>(q);
+    p.ws = sc;
+    p.x = reinterpret_cast<const uint32_t *>(x);
+    p.ng = ng;
+    p.T = g.T;
+    p.P = g.P;
+    p.slot_stride = g.slot_stride;
+    p.key_by_rb = g.key_by_rb;
+    p.ctr = static_cast<unsigned *>(ws);
+    p.slots = reinterpret_cast<double *>(static_cast<char *>(ws) + sg_ctr_bytes(g));
+    hipLaunchKernelGGL(sg_gemv_kernel<Epi>, dim3(g.P), dim3(kThreads), 0, s, p, epi);
+    return hipGetLastError();
+}
+
 extern "C" size_t w4_gemv_ws_bytes(int64_t N, int64_t K) {
-    if (N < 1 || K < kGroup || K % kGroup) return 0;
-    const int n_rb = static_cast<int>((N + 63) / 64);
-    return gemv_ws_bytes(n_rb, gemv_partials(n_rb, gemv_split(n_rb, static_cast<int>(K / kGroup))));
+    if (N > (int64_t(1) << 31) - 64 || !sg_shape_ok(N, K)) return 0;
+    return sg_ws_bytes(static_cast<int>((N + 63) / 64), static_cast<int>(K / kGroup));
 }
 
 extern "C" w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_s, const uint16_t *x,
@@ -161,41 +180,19 @@ extern "C" w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_
     W4_CHECK(aligned16(packed_q) && aligned16(packed_s) && aligned16(x), W4_EALIGN,
              "packed_q, packed_s and x must be 16-byte aligned device pointers");
     W4_CHECK(y != nullptr && (reinterpret_cast<uintptr_t>(y) & 1) == 0, W4_EALIGN, "bad y pointer");
-    const int n_rb = static_cast<int>((N + 63) / 64);
-    const int n_groups = static_cast<int>(K / kGroup);
-    const int n_split = gemv_split(n_rb, n_groups);
-    const size_t need = gemv_ws_bytes(n_rb, gemv_partials(n_rb, n_split));
+    W4_CHECK(sg_shape_ok(N, K), W4_EINVAL, "N=%lld x K=%lld is too large", (long long)N, (long long)K);
+    const size_t need = w4_gemv_ws_bytes(N, K);
     W4_CHECK(ws_bytes >= need && aligned16(workspace), W4_EINVAL,
              "workspace of %zu bytes given (16-byte aligned), %zu needed", ws_bytes, need);
-    W4Problem p;
-    p.wq = reinterpret_cast<const u32x4 *>(packed_q);
-    p.ws = packed_s;
-    p.x = reinterpret_cast<const uint32_t *>(x);
-    p.n_groups = n_groups;
-    p.n_rb = n_rb;
-    p.n_split = n_split;
-    gemv_ws_carve(workspace, n_rb, p);
-    if (n_split > 1) W4_HIP(zero_counters(workspace, n_rb, static_cast<hipStream_t>(stream)));
-    W4_HIP(launch_w4(p, EpiStoreF16{y, static_cast<int>(N)}, static_cast<hipStream_t>(stream)));
+    W4_HIP(launch_sg(packed_q, packed_s, x, N, K, workspace, EpiStoreF16{y, static_cast<int>(N)},
+                     static_cast<hipStream_t>(stream)));
     return W4_OK;
 }
 
-static void mlp_geometry(int64_t D, int64_t F, int &rb_gu, int &sp_gu, int &rb_dn, int &sp_dn, int &ctr,
-                         size_t &parts) {
-    rb_gu = static_cast<int>((2 * F + 63) / 64);
-    sp_gu = gemv_split(rb_gu, static_cast<int>(D / kGroup));
-    rb_dn = static_cast<int>((D + 63) / 64);
-    sp_dn = gemv_split(rb_dn, static_cast<int>(F / kGroup));
-    ctr = std::max(rb_gu, rb_dn);
-    parts = std::max(gemv_partials(rb_gu, sp_gu), gemv_partials(rb_dn, sp_dn));
-}
-
 extern "C" size_t w4_mlp_ws_bytes(int64_t D, int64_t F) {
-    if (D < kGroup || D % kGroup || F < kGroup || F % kGroup) return 0;
-    int rb_gu, sp_gu, rb_dn, sp_dn, ctr;
-    size_t parts;
-    mlp_geometry(D, F, rb_gu, sp_gu, rb_dn, sp_dn, ctr, parts);
-    return gemv_ws_bytes(ctr, parts);
+    if (D < kGroup || D % kGroup || F < kGroup || F % kGroup || D > (1 << 24) || F > (1 << 24)) return 0;
+    if (!sg_shape_ok(2 * F, D) || !sg_shape_ok(D, F)) return 0;
+    return std::max(w4_gemv_ws_bytes(2 * F, D), w4_gemv_ws_bytes(D, F));
 }
 
 extern "C" w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *down_q,
@@ -207,34 +204,18 @@ extern "C" w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const 
     W4_CHECK(aligned16(gu_q) && aligned16(gu_s) && aligned16(down_q) && aligned16(down_s) && aligned16(x) &&
                  aligned16(h) && aligned16(workspace) && y != nullptr,
              W4_EALIGN, "weights, x, h and workspace must be 16-byte aligned device pointers");
-    int rb_gu, sp_gu, rb_dn, sp_dn, ctr;
-    size_t parts;
-    mlp_geometry(D, F, rb_gu, sp_gu, rb_dn, sp_dn, ctr, parts);
-    const size_t need = gemv_ws_bytes(ctr, parts);
+    W4_CHECK(sg_shape_ok(2 * F, D) && sg_shape_ok(D, F), W4_EINVAL, "D=%lld, F=%lld too large", (long long)D,
+             (long long)F);
+    const size_t need = w4_mlp_ws_bytes(D, F);
     W4_CHECK(ws_bytes >= need, W4_EINVAL, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    W4Problem p;
-    p.wq = reinterpret_cast<const u32x4 *>(gu_q);
-    p.ws = gu_s;
-    p.x = reinterpret_cast<const uint32_t *>(x);
-    p.n_groups = static_cast<int>(D / kGroup);
-    p.n_rb = rb_gu;
-    p.n_split = sp_gu;
-    gemv_ws_carve(workspace, ctr, p);
-    W4_HIP(zero_counters(workspace, ctr, s));
-    W4_HIP(launch_w4(p, EpiSwiGLU{h, static_cast<int>(F)}, s));
-    p.wq = reinterpret_cast<const u32x4 *>(down_q);
-    p.ws = down_s;
-    p.x = reinterpret_cast<const uint32_t *>(h);
-    p.n_groups = static_cast<int>(F / kGroup);
-    p.n_rb = rb_dn;
-    p.n_split = sp_dn;
-    W4_HIP(launch_w4(p, EpiStoreF16{y, static_cast<int>(D)}, s));
+    W4_HIP(launch_sg(gu_q, gu_s, x, 2 * F, D, workspace, EpiSwiGLU{h, static_cast<int>(F)}, s));
+    W4_HIP(launch_sg(down_q, down_s, h, D, F, workspace, EpiStoreF16{y, static_cast<int>(D)}, s));
     return W4_OK;
 }
 
 extern "C" size_t w4_attn_ws_bytes(int32_t n_qh, int32_t n_kvh, int32_t n_pages_max) {
-    if (n_kvh < 1 || n_qh < 1 || n_qh % n_kvh || n_pages_max < 1) return 0;
+    if (n_kvh < 1 || n_kvh > kAttnMaxKvh || n_qh < 1 || n_qh % n_kvh || n_pages_max < 1) return 0;
     return attn_ws_bytes(n_kvh, n_qh / n_kvh, attn_n_split(n_pages_max));
 }
 
@@ -244,7 +225,8 @@ extern "C" w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool
                                        uint16_t *out, void *workspace, size_t ws_bytes, void *stream) {
     clear_error();
     W4_CHECK(head_dim == kHeadDim, W4_EINVAL, "head_dim must be 128 (got %d)", head_dim);
-    W4_CHECK(n_kvh >= 1 && n_qh >= 1 && n_qh % n_kvh == 0 && gqa_supported(n_qh / n_kvh), W4_EINVAL,
+    W4_CHECK(n_kvh >= 1 && n_kvh <= kAttnMaxKvh && n_qh >= 1 && n_qh % n_kvh == 0 && gqa_supported(n_qh / n_kvh),
+             W4_EINVAL,
              "n_qh=%d / n_kvh=%d must be one of 1, 2, 4, 7, 8", n_qh, n_kvh);
     W4_CHECK(n_pages_max >= 1 && ctx_len >= 1 && static_cast<int64_t>(ctx_len) <= int64_t(kPage) * n_pages_max,
              W4_EINVAL, "ctx_len=%d outside [1, 16*n_pages_max=%lld]", ctx_len,
@@ -270,7 +252,6 @@ extern "C" w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out = out;
     attn_ws_carve(workspace, n_kvh, G, n_split, a);
-    W4_HIP(zero_counters(workspace, n_kvh, static_cast<hipStream_t>(stream)));
     W4_HIP(launch_attn(G, a, static_cast<hipStream_t>(stream)));
     return W4_OK;
 }

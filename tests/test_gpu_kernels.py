@@ -87,6 +87,32 @@ def test_gemv_deterministic_and_ws_reuse():
     assert torch.equal(first, y)
 
 
+def test_gemv_shared_workspace_across_shapes_left_zero():
+    """One caller-owned workspace, zeroed once, serves GEMVs of different
+    shapes back to back: each result equals the oracle's and the bitwise
+    result of a fresh workspace, and the workspace is all zero after every
+    call (the contract that lets calls skip clearing it)."""
+    lib = L.lib()
+    shapes = [(3584, 18944), (37888, 3584), (100, 384), (3584, 3584), (257, 3584)]
+    need = max(lib.w4_gemv_ws_bytes(n, k) for n, k in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    for i, (n, k) in enumerate(shapes):
+        say(f"case: shared workspace, call {i}: N={n} K={k}")
+        q, s, x = synth.gemv_case(n, k, cfg=97 + i)
+        pq, ps = w4.pack_int4_weights(q, s)
+        dq, ds, dx = _dev(pq), _dev(ps), _dev(x)
+        y = torch.empty(n, dtype=torch.float16, device=DEV)
+        L.check(lib.w4a16_gemv(dq.data_ptr(), ds.data_ptr(), dx.data_ptr(), y.data_ptr(), n, k,
+                               ws.data_ptr(), ws.numel(), st))
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
+        fresh = w4.w4a16_gemv(dq, ds, dx, n, k).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y, fresh)
+        assert_gemv(y.cpu().numpy(), oracle.gemv(q, s, x), f"shared ws N={n} K={k}")
+
+
 # ------------------------------------------------------------------ MLP ----
 
 def test_mlp_cfg1():
