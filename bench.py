@@ -402,6 +402,117 @@ def long_context(args):
 
 
 # ------------------------------------------------------------------------------------------
+# Phase timestamps of the persistent decode kernel (trace build: libw4a16_trace.so, built by
+# `python -m int4_weight_only_dequant_amd.build --trace`).  Runs the 512-token prompt through
+# the step and 8 more steps, then reads the last step's timestamps and summarises, per phase
+# kind and averaged over layers 1-27, where the time goes.
+
+TRACE_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_phase_trace.md")
+
+
+def phase_trace(write_md: bool = True):
+    import ctypes
+    import torch
+    import synth
+    from int4_weight_only_dequant_amd import _lib, build as w4build
+    if not os.path.exists(w4build.TRACE_LIB):
+        sys.exit(f"{w4build.TRACE_LIB} is not built: run `python -m int4_weight_only_dequant_amd.build --trace`")
+    _lib.LIB_PATH = w4build.TRACE_LIB
+    L = _lib
+    lib = L.lib()
+    lib.w4_model_trace_copy.restype = ctypes.c_int
+    lib.w4_model_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+    dims = synth.QWEN7B
+    n_prompt, n_extra = 512, 8
+    model, _, _ = build_model(dims, n_prompt, n_extra)
+    model.reset(synth.prompt_ids(dims, n_prompt))
+    for _ in range(n_prompt + n_extra):
+        model.step(L.W4_GRAPH)
+    torch.cuda.synchronize()
+    assert model.device_error() == 0
+    P, n_ph = model.grid(), 4 * dims.n_layers + 1
+    tr = np.zeros((P, n_ph, 8), dtype=np.uint64)
+    L.check(lib.w4_model_trace_copy(model._m, tr.ctypes.data, tr.nbytes))
+    pos = model.pos - 1
+    model.close()
+    raw_dir = os.path.join(HERE, "gpurun_out")
+    if os.path.isdir(raw_dir):
+        np.save(os.path.join(raw_dir, "pk_trace.npy"), tr)
+    t = tr.astype(np.float64)
+    t0 = t[:, 0, 0].min()
+    t_end = t[:, :, :].max()
+    valid = t >= t0                                  # stale slots (earlier steps / not reached) are older
+    us = np.where(valid, (t - t0) / 100.0, np.nan)   # 100 MHz ticks -> us since the kernel's first stamp
+    kinds = ["QKV", "O", "gate+up", "down"]
+
+    def med(a):
+        a = a[~np.isnan(a)]
+        return float(np.median(a)) if a.size else float("nan")
+
+    def mx(a):
+        a = a[~np.isnan(a)]
+        return float(a.max()) if a.size else float("nan")
+
+    sig_last = np.array([mx(us[:, ph, 4]) for ph in range(n_ph)])
+    rows = {k: [] for k in kinds}
+    att = []
+    for l in range(1, dims.n_layers):
+        for kind in range(4):
+            ph = 4 * l + kind
+            prev = sig_last[ph - 1]
+            # dependency: QKV and gate+up wait for every work-group of the phase before
+            # (down, O); O waits for attention heads; down for gate+up
+            waited, staged, tiles, sig = us[:, ph, 1], us[:, ph, 2], us[:, ph, 3], us[:, ph, 4]
+            dep_ref = prev if kind != 1 else mx(us[:, ph, 6])
+            rows[kinds[kind]].append([
+                med(waited) - dep_ref,              # last producer signal -> median wait passed
+                med(staged - waited),               # staging
+                med(tiles - staged),                # wave 0's tiles
+                med(sig - tiles),                   # reduce + atomics + signal
+                mx(sig) - med(sig),                 # tail: median -> last signal
+                sig_last[ph] - prev,                # phase span (last signal to last signal)
+            ])
+            if kind == 1:
+                a0, a1 = us[:, ph, 5], us[:, ph, 6]
+                att.append([med(a1 - a0), mx(a1) - sig_last[ph - 1], mx(a1) - med(a1)])
+    hdr = ("| phase | producer's last signal -> median wait passed (us) | staging (us) | wave 0 tiles (us) | "
+           "reduce + signal (us) | median -> last signal (us) | span, last signal to last signal (us) |")
+    lines = [hdr, "|---|---:|---:|---:|---:|---:|---:|"]
+    for k in kinds:
+        a = np.nanmean(np.array(rows[k]), axis=0)
+        lines.append(f"| {k} | " + " | ".join(f"{v:.2f}" for v in a) + " |")
+    a = np.nanmean(np.array(att), axis=0)
+    per_layer = (sig_last[4 * dims.n_layers - 1] - sig_last[3]) / (dims.n_layers - 1)
+    lm = sig_last[n_ph - 1] - sig_last[n_ph - 2]
+    first = sig_last[3]
+    summary = {"position": pos, "grid": P, "kernel_us": round((t_end - t0) / 100.0, 1),
+               "layer0_us": round(first, 2), "per_layer_us": round(per_layer, 2), "lm_head_us": round(lm, 2),
+               "attention_unit_us": round(float(a[0]), 2),
+               "attention_last_publish_after_qkv_us": round(float(a[1]), 2)}
+    log(f"[trace] {json.dumps(summary)}")
+    for ln in lines:
+        log(ln)
+    if write_md:
+        with open(TRACE_MD, "w") as fh:
+            fh.write("# Phase timeline of the persistent decode kernel (Qwen2.5-7B shape, context 520)\n\n")
+            fh.write("Command (from the repository root on one MI355X, after `python -m "
+                     "int4_weight_only_dequant_amd.build --trace` on the build host):\n\n")
+            fh.write("```\npython3 -u bench.py --phase-trace\n```\n\n")
+            fh.write("The trace build records, in wave 0 of every work-group, the 100 MHz real-time counter "
+                     "at the top of each phase, when its dependency wait passes, when its input is staged, "
+                     "when wave 0's tiles are done and when the work-group's completion is signalled "
+                     "(attention work-groups also around the attention).  One step at position "
+                     f"{pos}; phases of layers 1-27 averaged per kind; medians and maxima over the work-groups.\n\n")
+            fh.write(f"Kernel {summary['kernel_us']} us (trace build); layer 0 done at {summary['layer0_us']} us; "
+                     f"{summary['per_layer_us']} us per layer; lm_head phase {summary['lm_head_us']} us.\n"
+                     f"Attention: a (head, chunk) unit takes {summary['attention_unit_us']} us from its start "
+                     f"(before its QKV wait) to publishing; the last unit publishes "
+                     f"{summary['attention_last_publish_after_qkv_us']} us after the last QKV signal.\n\n")
+            fh.write("\n".join(lines) + "\n")
+    return summary
+
+
+# ------------------------------------------------------------------------------------------
 # Standalone calls of configs 0-2 through the C ABI, rotating over distinct copies of the
 # operands (>= 1 GiB in total) so that no call finds its weights or pages in the 256 MB
 # Infinity Cache; R calls are captured in one graph and the graph replayed.
@@ -559,6 +670,8 @@ def main():
                     help="skip the standalone GEMV / MLP / attention calls of configs 0-2")
     ap.add_argument("--standalone-only", action="store_true",
                     help="run only the standalone calls of configs 0-2 (for kernel profiles)")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="phase timestamps of the persistent kernel (needs the trace build)")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--measure-traffic", metavar="OUT_DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -580,6 +693,9 @@ def main():
     if args.summarize_prefill_trace:
         return summarize_prefill_trace(args.summarize_prefill_trace, args.trace_command)
 
+    if args.phase_trace:
+        phase_trace()
+        return None
     if args.standalone_only:
         res = standalone_kernels()
         for k_, v_ in res.items():

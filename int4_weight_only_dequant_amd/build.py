@@ -1,7 +1,9 @@
 """Builds libw4a16.so (all HIP kernels + host code) for gfx950 with hipcc.
 
 Run ``python -m int4_weight_only_dequant_amd.build`` (or call ``build()``).
-The library is written next to this file, in-tree.
+The library is written next to this file, in-tree.  ``--trace`` builds
+libw4a16_trace.so instead: the same library with the persistent decode
+kernel's phase timestamps compiled in (read by ``pk_trace.py``).
 """
 from __future__ import annotations
 
@@ -15,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw4a16.so")
+TRACE_LIB = os.path.join(HERE, "libw4a16_trace.so")
 ARCH = os.environ.get("W4_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["w4a16.hip", "pack.cpp"]
@@ -27,12 +30,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libw4a16.so)")
 
 
-def build(verbose: bool = False) -> str:
-    out_tmp = LIB + ".tmp"
+def build(verbose: bool = False, trace: bool = False) -> str:
+    target = TRACE_LIB if trace else LIB
+    out_tmp = target + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           f"-I{INCLUDE}", f"-I{CSRC}", "-o", out_tmp]
+           f"-I{INCLUDE}", f"-I{CSRC}", "-o", out_tmp] + (["-DW4_PK_TRACE"] if trace else [])
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -43,9 +47,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs)
-    os.replace(out_tmp, LIB)
-    return LIB
+    os.replace(out_tmp, target)
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, trace="--trace" in sys.argv))

@@ -109,7 +109,35 @@ struct PKParams {
     size_t cnt_off;            // byte offset of the counters in a block
     int n_grp;                 // completion groups of kGW work-groups
     int cnt_layer;             // counters per layer: 4 phases x n_grp, then one per head
+    unsigned long long *trace; // [P][phases][kTraceSlots] timestamps (trace builds only)
+    int wa, wb;                // tile-range weights of the grid's first and second half
 };
+
+// Phase timestamps for profiling (built with -DW4_PK_TRACE; off in the
+// product build): wave 0 of each work-group records the 100 MHz real-time
+// counter at the points below, per phase.
+enum {
+    kTrStart = 0,      // top of the phase loop
+    kTrWaited = 1,     // dependency wait passed (all waves)
+    kTrStaged = 2,     // input staged in LDS (all waves)
+    kTrTiles = 3,      // wave 0's tiles done
+    kTrSignal = 4,     // accumulators added and completion signalled
+    kTrAttBegin = 5,   // attention work-groups: attention started
+    kTrAttEnd = 6,     // attention work-groups: chunk published
+    kTraceSlots = 8
+};
+#ifdef W4_PK_TRACE
+#define PK_STAMP(ph, k)                                                                                   \
+    do {                                                                                                  \
+        if (threadIdx.x == 0)                                                                             \
+            p.trace[(static_cast<size_t>(blockIdx.x) * (4 * p.n_layers + 1) + (ph)) * kTraceSlots + (k)] = \
+                __builtin_amdgcn_s_memrealtime();                                                         \
+    } while (0)
+#else
+#define PK_STAMP(ph, k) \
+    do {                \
+    } while (0)
+#endif
 
 // Counters sit 128 bytes apart: atomics on one line are serialised at the
 // memory side, so unrelated counters must not share a line.
@@ -154,13 +182,55 @@ __device__ __forceinline__ unsigned *pk_embed_cnt(const PKParams &p, int par) {
 struct Range { int b, e; };
 
 // Work-group B owns tiles [ceil(B T / P), ceil((B+1) T / P)); tile t belongs
-// to work-group floor(t P / T).  Inside the range wave v takes every 4th tile.
+// to work-group floor(t P / T).  Used for the attention units.
 __device__ __forceinline__ Range wg_range(int B, int T, int P) {
     return {static_cast<int>((static_cast<int64_t>(B) * T + P - 1) / P),
             static_cast<int>((static_cast<int64_t>(B + 1) * T + P - 1) / P)};
 }
 __device__ __forceinline__ int tile_owner(int t, int T, int P) {
     return static_cast<int>((static_cast<int64_t>(t) * P) / T);
+}
+
+// Tile ranges of the GEMV phases: contiguous, in work-group order, with
+// weights.  Two work-groups share each CU (work-groups are dealt out one per
+// CU first, so B and B + P/2 share one), and the first-dispatched one, whose
+// waves are older and win instruction and memory issue, gets through a phase
+// measurably faster; so the first half of the grid has weight wa and the
+// second half wb.  Work-group B owns tiles [start(B), start(B+1)) with
+// start(B) = ceil(T cum(B) / W), cum(B) the weight of the work-groups before
+// B and W the total; inside the range wave v takes every 4th tile.  Phases
+// with fewer than 4 tiles per work-group use equal weights.  (The lm_head
+// keeps equal weights: see phase_part.)
+struct Part {
+    int T, P, wa, wb;
+};
+// Measured on the 7B step (ms per step): 1:1 1.591, 53:47 1.563, 56:44
+// 1.551, 59:41 1.537, 62:38 1.510, 66:34 1.506, 70:30 1.522, 75:25 1.595.
+#ifndef W4_PK_WA
+#define W4_PK_WA 2
+#define W4_PK_WB 1
+#endif
+constexpr int kPkWeightFirst = W4_PK_WA, kPkWeightSecond = W4_PK_WB;
+__host__ __device__ inline Part make_part(int T, int P, int wa, int wb) {
+    return T < 4 * P ? Part{T, P, 1, 1} : Part{T, P, wa, wb};
+}
+__host__ __device__ inline int64_t part_cum(const Part &q, int B) {
+    const int H = q.P / 2;
+    return B <= H ? static_cast<int64_t>(q.wa) * B
+                  : static_cast<int64_t>(q.wa) * H + static_cast<int64_t>(q.wb) * (B - H);
+}
+__host__ __device__ inline int part_start(const Part &q, int B) {
+    const int64_t W = part_cum(q, q.P);
+    return static_cast<int>((static_cast<int64_t>(q.T) * part_cum(q, B) + W - 1) / W);
+}
+__host__ __device__ inline Range part_range(const Part &q, int B) { return {part_start(q, B), part_start(q, B + 1)}; }
+// owner of tile t: the last work-group whose cumulative weight is at most t W / T
+__host__ __device__ inline int part_owner(const Part &q, int t) {
+    const int64_t W = part_cum(q, q.P);
+    const int64_t X = (static_cast<int64_t>(t) * W) / q.T;
+    const int H = q.P / 2;
+    const int64_t WH = static_cast<int64_t>(q.wa) * H;
+    return X < WH ? static_cast<int>(X / q.wa) : H + static_cast<int>((X - WH) / q.wb);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -484,15 +554,15 @@ __device__ __forceinline__ void stage_attn(uint16_t *lds, Range rg, int nk, cons
 // slot.  With T >= P every work-group owns at least one tile, so the owners
 // of the row block's tiles are consecutive work-groups; with T < P each tile
 // has its own work-group (ranges hold at most one tile).
-__device__ __forceinline__ void rb_contrib(int rb, int nk, int T, int P, int B, int &n_contrib, int &slot) {
+__device__ __forceinline__ void rb_contrib(int rb, int nk, const Part &q, int B, int &n_contrib, int &slot) {
     const int a = rb * nk;
-    if (T >= P) {
-        const int first = tile_owner(a, T, P);
-        n_contrib = tile_owner(a + nk - 1, T, P) - first + 1;
+    if (q.T >= q.P) {
+        const int first = part_owner(q, a);
+        n_contrib = part_owner(q, a + nk - 1) - first + 1;
         slot = B - first;
     } else {
         n_contrib = nk;
-        slot = static_cast<int>((static_cast<int64_t>(B) * T + P - 1) / P) - a;   // this work-group's tile
+        slot = part_start(q, B) - a;   // this work-group's tile
     }
 }
 
@@ -503,7 +573,7 @@ __device__ __forceinline__ bool pk_reduce(const PKParams &p, int rb, int nk, int
                                           int arr_base, double &total) {
     unsigned *arr = p.ctr + (arr_base + rb) * kCS;
     int n_contrib, slot;
-    rb_contrib(rb, nk, T, p.P, static_cast<int>(blockIdx.x), n_contrib, slot);
+    rb_contrib(rb, nk, make_part(T, p.P, 1, 1), static_cast<int>(blockIdx.x), n_contrib, slot);
     if (n_contrib == 1) {
         total = v;
         return true;
@@ -937,8 +1007,16 @@ __device__ __forceinline__ PhaseDesc phase_desc(const PKParams &p, int ph, int p
     return g;
 }
 
+// Tile ranges of a phase: weighted for the decoder GEMVs; equal for the
+// lm_head, a long phase in which the two work-groups of a CU share it evenly
+// (measured: with the 2:1 weights the first half's lm_head tiles took 167 us
+// against 99 us for the second half).
+__device__ __forceinline__ Part phase_part(const PKParams &p, const PhaseDesc &g) {
+    return g.kind == kPhLM ? make_part(g.T, p.P, 1, 1) : make_part(g.T, p.P, p.wa, p.wb);
+}
+
 __device__ __forceinline__ void prefetch_phase(Ring &r, const PKParams &p, const PhaseDesc &g) {
-    const Range rg = wg_range(blockIdx.x, g.T, p.P);
+    const Range rg = part_range(phase_part(p, g), blockIdx.x);
     if (g.kind == kPhLM) prefetch_f16(r, p.lm, g.nk, rg);
     else prefetch_w4(r, g.wq, g.ws, g.nk, rg);
 }
@@ -1057,8 +1135,9 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     const int n_ph = 4 * L + 1;
     for (int ph = 0; ph < n_ph; ++ph) {
         const PhaseDesc g = phase_desc(p, ph, par, n_split);
-        const Range rg = wg_range(B, g.T, p.P);
+        const Range rg = part_range(phase_part(p, g), B);
         const bool has_next = ph + 1 < n_ph;
+        PK_STAMP(ph, kTrStart);
         // attention runs between a layer's QKV and O phases; its waves fill
         // their ring for O only afterwards
         if (g.kind == kPhO && att_h >= 0) {
@@ -1066,9 +1145,11 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             // the ring holds nothing this wave still needs: clearing it
             // lets its registers serve the attention loads
             ring = Ring{};
+            PK_STAMP(ph, kTrAttBegin);
             ok = pk_attention(p, pk_layer(p, g.l), pk_grp_cnt(p, par, g.l, kPhQ), pk_acc(p, par, g.l, p.acc_q),
                               p.att_part + g.l * p.att_layer, pk_head_cnt(p, par, g.l), att_h, att_s, n_split, ctx,
                               phys, reinterpret_cast<float *>(s_red), s_stage, 2000 + g.l);
+            PK_STAMP(ph, kTrAttEnd);
             if (!ok) break;
             prefetch_phase(ring, p, g);
         }
@@ -1083,6 +1164,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             }
             // a failed wait must not strand the other waves at a barrier
             if (__syncthreads_or(!ok)) { ok = false; break; }
+            PK_STAMP(ph, kTrWaited);
             const int rb0 = rg.b / g.nk, n_rl = (rg.e - 1) / g.nk - rb0 + 1;
             stage_begin(s_red, n_rl);
             if (g.stage == kStNorm)
@@ -1092,11 +1174,14 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             else
                 stage_attn(s_stage, rg, g.nk, p.att_part + g.l * p.att_layer, p.att_smax, n_split);
             __syncthreads();
+            PK_STAMP(ph, kTrStaged);
             if (g.kind == kPhLM) f16_tiles(ring, p.lm, g.nk, rg, rb0, s_stage, s_red);
             else w4_tiles(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
+            PK_STAMP(ph, kTrTiles);
             // publish before issuing the next phase's loads: vmcnt is in
             // order, so waiting for the adds would also wait for the prefetch
             phase_reduce(p, g, s_red, rb0, n_rl, pos, epoch);
+            PK_STAMP(ph, kTrSignal);
             if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, par, n_split));
         } else {
             if (!ok) break;

@@ -437,6 +437,7 @@ struct w4_model {
     PKParams pk;
     PKLayer *pk_layers;       // device array
     PKParams *pk_dev;         // device copy of pk
+    size_t trace_bytes = 0;   // phase-timestamp buffer (trace builds)
     int pk_grid;              // resident work-groups
     int n_ctr;
 
@@ -665,21 +666,25 @@ static hipError_t enqueue_prefill(w4_model *m, int pos0, int M, hipStream_t s) {
 
 // Largest number of work-groups that split one row block, and the checks
 // that every work-group's range fits the kernel's LDS areas.
-static bool phase_geometry(int T, int nk, int V, int P, int &slots, std::string &why) {
+static bool phase_geometry(int T, int nk, int V, int P, int wa, int wb, int &slots, std::string &why) {
     slots = 1;
     const int n_rb = T / nk;
+    const Part q = make_part(T, P, wa, wb);
     if (T < P) {
         slots = nk;                       // one work-group per tile
     } else {
         for (int rb = 0; rb < n_rb; ++rb) {
-            const int first = static_cast<int>((static_cast<int64_t>(rb) * nk * P) / T);
-            const int last = static_cast<int>((static_cast<int64_t>(rb * nk + nk - 1) * P) / T);
+            const int first = part_owner(q, rb * nk);
+            const int last = part_owner(q, rb * nk + nk - 1);
             slots = std::max(slots, last - first + 1);
         }
     }
     for (int B = 0; B < P; ++B) {
-        const int b = static_cast<int>((static_cast<int64_t>(B) * T + P - 1) / P);
-        const int e = static_cast<int>((static_cast<int64_t>(B + 1) * T + P - 1) / P);
+        const int b = part_start(q, B), e = part_start(q, B + 1);
+        if (T >= P && e <= b) { why = "a work-group without tiles"; return false; }
+        for (int t = b; t < e; t += std::max(1, (e - b) / 4)) {
+            if (part_owner(q, t) != B) { why = "tile owner does not match the ranges"; return false; }
+        }
         if (e <= b) continue;
         const int staged = (e - b >= nk ? nk : e - b) * V;   // whole vector or the range's slices
         if (staged * 2 > kStageBytes) { why = "staged input exceeds LDS"; return false; }
@@ -712,11 +717,15 @@ static w4_status setup_persistent(w4_model *m) {
     pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 4 * P - 1) / (4 * P));
     pk.att_smax = (c.max_pages + 4 * pk.att_pps - 1) / (4 * pk.att_pps);
     W4_CHECK(c.n_q_heads * pk.att_smax <= P, W4_EINVAL, "too many attention chunks for the grid");
-    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, slots_unused, why) &&
-                    phase_geometry(rb_d * no, no, kGroup, P, slots_unused, why) &&
-                    phase_geometry(rb_gu * nq, nq, kGroup, P, slots_unused, why) &&
-                    phase_geometry(rb_d * nf, nf, kGroup, P, slots_unused, why) &&
-                    phase_geometry(rb_lm * nkc, nkc, 32, P, pk.slots_lm, why);
+    // two work-groups per CU: the first-dispatched half of the grid gets the
+    // larger share of every phase (measured: it gets through a phase faster)
+    pk.wa = P == 2 * n_cu ? kPkWeightFirst : 1;
+    pk.wb = P == 2 * n_cu ? kPkWeightSecond : 1;
+    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
+                    phase_geometry(rb_d * no, no, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
+                    phase_geometry(rb_gu * nq, nq, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
+                    phase_geometry(rb_d * nf, nf, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
+                    phase_geometry(rb_lm * nkc, nkc, 32, P, 1, 1, pk.slots_lm, why);
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
     // normalised inputs are staged whole, one element per thread and batch slot
     W4_CHECK(d <= kStageMax * kThreads && d * 2 <= kStageBytes, W4_EINVAL, "d_model too large for the persistent step");
@@ -742,7 +751,14 @@ static w4_status setup_persistent(w4_model *m) {
                          align256(static_cast<size_t>(d) * 8) + align256(part) +
                          align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) * L + 256 + per_layer * L +
                          ctr_bytes + 2 * pk.par_bytes;
+#ifdef W4_PK_TRACE
+    const size_t trace_bytes = static_cast<size_t>(P) * (4 * L + 1) * kTraceSlots * 8;
+    W4_HIP(hipMalloc(&m->pk_arena, total + trace_bytes));
+    pk.trace = reinterpret_cast<unsigned long long *>(static_cast<char *>(m->pk_arena) + total);
+    m->trace_bytes = trace_bytes;
+#else
     W4_HIP(hipMalloc(&m->pk_arena, total));
+#endif
     W4_HIP(hipMemset(m->pk_arena, 0, total));
     char *b = static_cast<char *>(m->pk_arena);
     m->pk_layers = reinterpret_cast<PKLayer *>(b); b += align256(sizeof(PKLayer) * L);
@@ -939,6 +955,19 @@ extern "C" w4_status w4_model_create(const w4_model_config *cfg, const w4_model_
     *out = m;
     return W4_OK;
 }
+
+#ifdef W4_PK_TRACE
+// Trace builds only: copies the persistent kernel's phase timestamps of the
+// last step ([grid][4 * n_layers + 1][8] uint64, 100 MHz ticks) to host memory.
+extern "C" w4_status w4_model_trace_copy(w4_model *m, void *host, size_t bytes) {
+    clear_error();
+    W4_CHECK(m != nullptr && host != nullptr && bytes >= m->trace_bytes, W4_EINVAL, "trace needs %zu bytes",
+             m ? m->trace_bytes : size_t(0));
+    W4_HIP(hipDeviceSynchronize());
+    W4_HIP(hipMemcpy(host, m->pk.trace, m->trace_bytes, hipMemcpyDeviceToHost));
+    return W4_OK;
+}
+#endif
 
 extern "C" void w4_model_destroy(w4_model *m) {
     if (m) (void)hipDeviceSynchronize();
