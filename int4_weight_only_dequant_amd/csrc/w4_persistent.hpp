@@ -56,8 +56,18 @@ namespace w4 {
 // phase hand-overs (measured: 1.70 ms per step at 1, 1.72 at 2, 1.79 at 3,
 // 1.87 at 4).
 constexpr int kRing = 1;
-constexpr int kMaxRbPerWg = 8;           // row blocks one work-group's range may touch
-constexpr int kRedBytes = kMaxRbPerWg * 4 * 64 * 8;
+// Waves per work-group: 4 (two work-groups per CU, weighted ranges) or 8 (one
+// per CU).  Measured on the 7B step: 4 waves 1.494 ms, 8 waves 1.499 ms (the
+// phase tails shrink with 8, but the waits and the per-work-group reduce
+// grow, and attention chunks are twice as long).
+#ifndef W4_PK_WAVES
+#define W4_PK_WAVES 4
+#endif
+constexpr int kPkWaves = W4_PK_WAVES;            // waves per work-group
+constexpr int kPkThreads = 64 * kPkWaves;        // work-group size
+constexpr int kPkWgPerCu = kPkWaves == 4 ? 2 : 1;   // resident work-groups per CU
+constexpr int kMaxRbPerWg = kPkWaves == 4 ? 8 : 12;   // row blocks one work-group's range may touch
+constexpr int kRedBytes = kMaxRbPerWg * kPkWaves * 64 * 8;
 constexpr int kStageBytes = 18432;       // staged fp16 input per work-group
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kGW = 8;                   // work-groups per completion counter
@@ -198,7 +208,7 @@ __device__ __forceinline__ int tile_owner(int t, int T, int P) {
 // measurably faster; so the first half of the grid has weight wa and the
 // second half wb.  Work-group B owns tiles [start(B), start(B+1)) with
 // start(B) = ceil(T cum(B) / W), cum(B) the weight of the work-groups before
-// B and W the total; inside the range wave v takes every 4th tile.  Phases
+// B and W the total; inside the range wave v takes every kPkWaves-th tile.  Phases
 // with fewer than 4 tiles per work-group use equal weights.  (The lm_head
 // keeps equal weights: see phase_part.)
 struct Part {
@@ -268,6 +278,9 @@ __device__ __noinline__ bool pk_wait_cnt(const PKParams &p, const unsigned *base
             if (lane == 0) store_agent(p.err, code);
             return false;
         }
+        // (polling more slowly while most counters are short of their
+        // targets measured slower: 1.491 ms per step at s_sleep 1, 1.499-1.512
+        // at 4-16)
         __builtin_amdgcn_s_sleep(1);
     }
 }
@@ -342,14 +355,14 @@ __device__ __forceinline__ void prefetch_w4(Ring &r, const u32x4 *wq, const uint
     const int t0 = rg.b + (static_cast<int>(threadIdx.x) >> 6);
 #pragma unroll
     for (int s = 0; s < kRing; ++s)
-        if (t0 + 4 * s < rg.e) load_w4_tile(r, s, wq, ws, ng, t0 + 4 * s);
+        if (t0 + kPkWaves * s < rg.e) load_w4_tile(r, s, wq, ws, ng, t0 + kPkWaves * s);
 }
 
 __device__ __forceinline__ void prefetch_f16(Ring &r, const u32x4 *lm, int nkc, Range rg) {
     const int t0 = rg.b + (static_cast<int>(threadIdx.x) >> 6);
 #pragma unroll
     for (int s = 0; s < kRing; ++s)
-        if (t0 + 4 * s < rg.e) load_f16_tile(r, s, lm, nkc, t0 + 4 * s);
+        if (t0 + kPkWaves * s < rg.e) load_f16_tile(r, s, lm, nkc, t0 + kPkWaves * s);
 }
 
 // ------------------------------------------------------- input staging ----
@@ -362,12 +375,12 @@ __device__ __forceinline__ void prefetch_f16(Ring &r, const u32x4 *lm, int nkc, 
 __device__ __forceinline__ bool stage_whole(Range rg, int nk) { return rg.e - rg.b >= nk; }
 
 __device__ __forceinline__ void stage_begin(double *red, int n_rl) {
-    for (int v = threadIdx.x; v < n_rl * 256; v += kThreads) red[v] = 0.0;
+    for (int v = threadIdx.x; v < n_rl * kPkThreads; v += kPkThreads) red[v] = 0.0;
 }
 
 // Staging issues all of a thread's loads before using any of them (the
 // inputs sit in L2 or beyond; one round trip instead of one per element).
-constexpr int kStageMax = 16;   // elements per thread (host-checked)
+constexpr int kStageMax = kPkWaves == 4 ? 16 : 10;   // elements per thread (host-checked)
 
 // x = x_prev + acc (acc may be null), rounded to the fp32 residual stream;
 // RMSNorm with weight w, whole vector to LDS.  Each thread takes element
@@ -416,7 +429,7 @@ __device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, in
     uint32_t wv[kPairMax];
 #pragma unroll
     for (int j = 0; j < kPairMax; ++j) {
-        const int q = tid + j * kThreads;
+        const int q = tid + j * kPkThreads;
         if (q < np) {
             xv[j] = reinterpret_cast<const float2 *>(x_prev)[q];
             wv[j] = reinterpret_cast<const uint32_t *>(w)[q];
@@ -427,7 +440,7 @@ __device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, in
     double sq = 0.0;
 #pragma unroll
     for (int j = 0; j < kPairMax; ++j) {
-        const int q = tid + j * kThreads;
+        const int q = tid + j * kPkThreads;
         if (q < np) {
             xv[j].x = static_cast<float>(static_cast<double>(xv[j].x) + fix_to_f64(av[j].x));
             xv[j].y = static_cast<float>(static_cast<double>(xv[j].y) + fix_to_f64(av[j].y));
@@ -440,13 +453,13 @@ __device__ __forceinline__ void stage_resid_norm(uint16_t *lds, double *wsum, in
     __syncthreads();
     double ss = 0.0;
 #pragma unroll
-    for (int r = 0; r < kThreads / 16; ++r) ss += wsum[r];
+    for (int r = 0; r < kPkThreads / 16; ++r) ss += wsum[r];
     // the scaling itself runs in fp32: its rounding (a few 2^-24) sits far
     // below the fp16 rounding of the result
     const float inv_r = static_cast<float>(1.0 / sqrt(ss / d + eps));
 #pragma unroll
     for (int j = 0; j < kPairMax; ++j) {
-        const int q = tid + j * kThreads;
+        const int q = tid + j * kPkThreads;
         if (q < np) {
             if (x_out) {   // device-scope stores: read by other XCDs after the next signal
                 store_agent(x_out + 2 * q, xv[j].x);
@@ -469,7 +482,7 @@ __device__ __forceinline__ void stage_swiglu(uint16_t *lds, Range rg, int nk, in
     i64x2 a0[kPairMax], a1[kPairMax];
 #pragma unroll
     for (int j = 0; j < kPairMax; ++j) {
-        const int v = 2 * (tid + j * kThreads);
+        const int v = 2 * (tid + j * kPkThreads);
         if (v < n) {
             const int i = v / V, e = v - i * V;            // V is even: the pair stays in one tile
             const int k = whole ? v : ((rg.b + i) % nk) * V + e;
@@ -479,7 +492,7 @@ __device__ __forceinline__ void stage_swiglu(uint16_t *lds, Range rg, int nk, in
     }
 #pragma unroll
     for (int j = 0; j < kPairMax; ++j) {
-        const int v = 2 * (tid + j * kThreads);
+        const int v = 2 * (tid + j * kPkThreads);
         if (v < n) {
             // exp in fp32 (relative error ~1e-7, far below the fp16 rounding
             // of h); a double exp's coefficient table would be hoisted out
@@ -505,7 +518,7 @@ __device__ __forceinline__ void stage_attn(uint16_t *lds, Range rg, int nk, cons
     const bool whole = stage_whole(rg, nk);
     const int n_u = whole ? nk : rg.e - rg.b;
     const int lane = opaque_tid() & 63;
-    for (int u = wave_id(); u < n_u; u += 4) {
+    for (int u = wave_id(); u < n_u; u += kPkWaves) {
         const int h = whole ? u : (rg.b + u) % nk;
         const float *hb = att_part + static_cast<size_t>(h) * att_smax * 132;
         float M = -INFINITY, Ls = 0.f, A0 = 0.f, A1 = 0.f;
@@ -606,7 +619,7 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
                                          bool whole, int rb0, const uint16_t *lds, double *red) {
     const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u);
     const int wave = wave_id(), lane = lane_id();
-    const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + 3) / 4 : 0;
+    const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + kPkWaves - 1) / kPkWaves : 0;
     int cur = -1;
     double acc = 0.0;
     for (int k0 = 0; k0 < n; k0 += kRing) {
@@ -614,11 +627,11 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
         for (int s = 0; s < kRing; ++s) {
             const int k = k0 + s;
             if (k < n) {
-                const int i = wave + 4 * k;          // slot in the work-group range
+                const int i = wave + kPkWaves * k;   // slot in the work-group range
                 const int t = rg.b + i;
                 const int rl = t / ng - rb0;
                 if (rl != cur) {
-                    if (cur >= 0) red[cur * 256 + wave * 64 + lane] = acc;
+                    if (cur >= 0) red[cur * kPkThreads + wave * 64 + lane] = acc;
                     acc = 0.0;
                     cur = rl;
                 }
@@ -637,19 +650,21 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
                     dot8v(r.w[s][c].w, xd, a1, a16, m_lo, m_hi, magic);
                 }
                 acc += static_cast<double>(__builtin_fmaf(a16, 0.0625f, a1)) * static_cast<double>(f16_to_f32(r.s[s]));
-                if (k + kRing < n) load_w4_tile(r, s, wq, ws, ng, t + 4 * kRing);
+                if (k + kRing < n) load_w4_tile(r, s, wq, ws, ng, t + kPkWaves * kRing);
             }
         }
     }
-    if (cur >= 0) red[cur * 256 + wave * 64 + lane] = acc;
+    if (cur >= 0) red[cur * kPkThreads + wave * 64 + lane] = acc;
 }
 
 // fp16 (lm_head) tile loop of one wave: fp32 accumulation per row block; the
-// normalised input is staged whole.
+// normalised input is staged whole.  (Two or three tiles in flight per wave
+// instead of one measured the same, 1.495-1.497 ms per step: the phase
+// already streams at about 6.1 TB/s.)
 __device__ __forceinline__ void f16_tiles(Ring &r, const u32x4 *lm, int nkc, Range rg, int rb0,
                                           const uint16_t *lds, double *red) {
     const int wave = wave_id(), lane = lane_id();
-    const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + 3) / 4 : 0;
+    const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + kPkWaves - 1) / kPkWaves : 0;
     int cur = -1;
     float acc0 = 0.f, acc1 = 0.f;
     for (int k0 = 0; k0 < n; k0 += kRing) {
@@ -657,11 +672,11 @@ __device__ __forceinline__ void f16_tiles(Ring &r, const u32x4 *lm, int nkc, Ran
         for (int s = 0; s < kRing; ++s) {
             const int k = k0 + s;
             if (k < n) {
-                const int i = wave + 4 * k;
+                const int i = wave + kPkWaves * k;
                 const int t = rg.b + i;
                 const int rl = t / nkc - rb0;
                 if (rl != cur) {
-                    if (cur >= 0) red[cur * 256 + wave * 64 + lane] = static_cast<double>(acc0 + acc1);
+                    if (cur >= 0) red[cur * kPkThreads + wave * 64 + lane] = static_cast<double>(acc0 + acc1);
                     acc0 = acc1 = 0.f;
                     cur = rl;
                 }
@@ -674,11 +689,11 @@ __device__ __forceinline__ void f16_tiles(Ring &r, const u32x4 *lm, int nkc, Ran
                     acc0 = __builtin_amdgcn_fdot2(as_h2(r.w[s][c].z), as_h2(xv.z), acc0, false);
                     acc1 = __builtin_amdgcn_fdot2(as_h2(r.w[s][c].w), as_h2(xv.w), acc1, false);
                 }
-                if (k + kRing < n) load_f16_tile(r, s, lm, nkc, t + 4 * kRing);
+                if (k + kRing < n) load_f16_tile(r, s, lm, nkc, t + kPkWaves * kRing);
             }
         }
     }
-    if (cur >= 0) red[cur * 256 + wave * 64 + lane] = static_cast<double>(acc0 + acc1);
+    if (cur >= 0) red[cur * kPkThreads + wave * 64 + lane] = static_cast<double>(acc0 + acc1);
 }
 
 // ------------------------------------------------------- lm_head epilogue --
@@ -715,15 +730,15 @@ struct PKFinLogits {
 };
 
 // ----------------------------------------------------------- attention ----
-// A work-group per (query head, chunk of 4 x pps pages); its wave v takes
-// pages [chunk * 4 pps + v pps, + pps).  In a wave, lanes = 4 token rows x 16
+// A work-group per (query head, chunk of W x pps pages, W its waves); its
+// wave v takes pages [chunk * W pps + v pps, + pps).  In a wave, lanes = 4 token rows x 16
 // eight-dim chunks; each 16-byte load covers 4 tokens of a page.  The K/V
 // pages are requested before waiting for the QKV phase (they hold earlier
 // tokens only).  The query (and, for the running position, that token's key
 // and value) comes straight from the QKV accumulators: bias, RoPE and the
 // fp16 rounding are applied here, and the wave holding the running position
 // of the first query head of a kv group writes the new key and value into
-// the cache for later steps.  The 4 waves' online-softmax states are merged
+// the cache for later steps.  The waves' online-softmax states are merged
 // through LDS in wave order; the chunk's (max, sum, 128 weighted-V sums) is
 // published and the head's counter bumped; the O projection merges chunks.
 
@@ -738,6 +753,7 @@ constexpr int kAttPages = 2;   // pages loaded together per wave (8 x 16 B per l
 __device__ __forceinline__ void qkv_to_lds(const PKParams &p, const long long *acc, const uint16_t *bias, int h,
                                            int j, int pos, bool kv, uint16_t *sq, uint16_t *sk, uint16_t *sv) {
     const int t = opaque_tid();
+    if (t >= 256) return;                          // 128 query dims, 128 key (or value) dims
     const int d = t & 127, i = d & 63, hi = d >> 6;
     const bool first = t < 128;
     const bool rot = first || kv;                  // q, or k when wanted
@@ -801,7 +817,7 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
     const int G = p.n_qh / p.n_kvh, j = h / G;
     const int pos = ctx - 1;
     const int n_pages = (ctx + kPage - 1) / kPage;
-    const int pb = (c * 4 + wave) * p.att_pps;
+    const int pb = (c * kPkWaves + wave) * p.att_pps;
     const int pe = min(pb + p.att_pps, n_pages);
     u32x4 kc[kAttPages][4], vc[kAttPages][4];
     if (pb < pe) att_load(p, L, j, pb, pe, ts, dc, kc, vc);
@@ -893,7 +909,7 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
         for (int e = 0; e < 8; ++e) acc[e] = acc[e] * f0 + __shfl_xor(acc[e], off) * f1;
         m = mn;
     }
-    // merge the 4 waves in wave order through LDS: [wave][m, l, 128 dims]
+    // merge the waves in wave order through LDS: [wave][m, l, 128 dims]
     float *sw = s_att + wave * 130;
     if (lane < 16) {
 #pragma unroll
@@ -904,10 +920,10 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
     if (wave == 0) {
         float M = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) M = fmaxf(M, s_att[v * 130]);
+        for (int v = 0; v < kPkWaves; ++v) M = fmaxf(M, s_att[v * 130]);
         float Ls = 0.f, A0 = 0.f, A1 = 0.f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < kPkWaves; ++v) {
             const float mv = s_att[v * 130];
             if (mv != -INFINITY) {
                 const float f = exp2f(mv - M);
@@ -1035,9 +1051,11 @@ __device__ __forceinline__ void phase_reduce(const PKParams &p, const PhaseDesc 
                                              int n_rl, int pos, unsigned epoch) {
     __syncthreads();
     const int wave = wave_id(), lane = lane_id();
-    for (int rl = wave; rl < n_rl; rl += 4) {
-        const double *rr = red + rl * 256 + lane;
-        const double v = ((rr[0] + rr[64]) + rr[128]) + rr[192];
+    for (int rl = wave; rl < n_rl; rl += kPkWaves) {
+        const double *rr = red + rl * kPkThreads + lane;
+        double v = rr[0];
+#pragma unroll
+        for (int u = 1; u < kPkWaves; ++u) v += rr[u * 64];   // wave order
         if (g.kind == kPhLM) {
             double tot;
             if (pk_reduce(p, rb0 + rl, g.nk, g.T, p.slots_lm, v, p.c_arr_lm, tot))
@@ -1056,18 +1074,18 @@ __device__ __forceinline__ void phase_reduce(const PKParams &p, const PhaseDesc 
     // work-group-wide barrier
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kPkThreads, kPkThreads), amdgpu_waves_per_eu(2)))
 void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     // parameters live in device memory: functions below take their address,
     // which for a by-value kernel argument would force a copy to scratch
     const PKParams &p = *pp;
     __shared__ __attribute__((aligned(16))) double s_red[kRedBytes / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_stage[kStageBytes / 2];
-    __shared__ double s_wsum[kThreads / 16];
+    __shared__ double s_wsum[kPkThreads / 16];
     const int wave = wave_id();
     const int B = blockIdx.x;
-    const int w = (B << 2) + wave;
-    const int W = p.P * 4;
+    const int w = B * kPkWaves + wave;
+    const int W = p.P * kPkWaves;
     const int lane = lane_id();
 
     const int pos = p.st->pos;
@@ -1078,8 +1096,8 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     const int phys = p.page_table[pos >> 4];
     const int L = p.n_layers;
     const int n_pages = (ctx + kPage - 1) / kPage;
-    // attention chunks of 4 x att_pps pages per head at this context
-    const int n_split = (n_pages + 4 * p.att_pps - 1) / (4 * p.att_pps);
+    // attention chunks of kPkWaves x att_pps pages per head at this context
+    const int n_split = (n_pages + kPkWaves * p.att_pps - 1) / (kPkWaves * p.att_pps);
 
     // attention unit (head, chunk) of this work-group, if any.  The query
     // heads of one kv head and chunk read the same K/V pages: they go to
@@ -1127,7 +1145,8 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
         u32x4 *z = reinterpret_cast<u32x4 *>(p.par[par ^ 1]);
         const size_t n16 = p.par_bytes / 16;
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (size_t i = static_cast<size_t>(B) * kThreads + threadIdx.x; i < n16; i += static_cast<size_t>(p.P) * kThreads)
+        for (size_t i = static_cast<size_t>(B) * kPkThreads + threadIdx.x; i < n16;
+             i += static_cast<size_t>(p.P) * kPkThreads)
             z[i] = zero;
     }
 

@@ -551,7 +551,7 @@ static hipError_t enqueue_persistent(w4_model *m, bool boundary, hipStream_t s) 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(decode_persistent_kernel, dim3(m->pk_grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(decode_persistent_kernel, dim3(m->pk_grid), dim3(kPkThreads), 0, s,
                        static_cast<const PKParams *>(m->pk_dev));
     return hipGetLastError();
 }
@@ -688,7 +688,7 @@ static bool phase_geometry(int T, int nk, int V, int P, int wa, int wb, int &slo
         if (e <= b) continue;
         const int staged = (e - b >= nk ? nk : e - b) * V;   // whole vector or the range's slices
         if (staged * 2 > kStageBytes) { why = "staged input exceeds LDS"; return false; }
-        if (staged > kStageMax * kThreads) { why = "staged input exceeds the per-thread batch"; return false; }
+        if (staged > kStageMax * kPkThreads) { why = "staged input exceeds the per-thread batch"; return false; }
         if ((e - 1) / nk - b / nk + 1 > kMaxRbPerWg) { why = "range touches too many row blocks"; return false; }
     }
     return true;
@@ -699,9 +699,9 @@ static w4_status setup_persistent(w4_model *m) {
     int dev = 0, n_cu = 0, occ = 0;
     W4_HIP(hipGetDevice(&dev));
     W4_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
-    W4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_persistent_kernel, kThreads, 0));
+    W4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_persistent_kernel, kPkThreads, 0));
     W4_CHECK(occ >= 1 && n_cu >= 1, W4_EHIP, "persistent kernel cannot be resident (occupancy %d)", occ);
-    const int P = n_cu * std::min(occ, 2);
+    const int P = n_cu * std::min(occ, kPkWgPerCu);
     const int L = c.n_layers, d = c.d_model, f = c.d_ff;
     const int nq = d / kGroup, nf = f / kGroup, nkc = d / 32, no = c.n_q_heads * kHeadDim / kGroup;
     const int rb_q = (c.n_q_heads + 2 * c.n_kv_heads) * kHeadDim / 64, rb_d = d / 64, rb_gu = 2 * f / 64;
@@ -711,11 +711,11 @@ static w4_status setup_persistent(w4_model *m) {
     pk.P = P;
     std::string why;
     int slots_unused = 0;
-    // attention: a work-group per (head, chunk of 4 x att_pps pages), wave
+    // attention: a work-group per (head, chunk of kPkWaves x att_pps pages), wave
     // v of it taking att_pps pages; at least 2 pages per wave, and enough
     // that every (head, chunk) unit has a work-group of its own
-    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + 4 * P - 1) / (4 * P));
-    pk.att_smax = (c.max_pages + 4 * pk.att_pps - 1) / (4 * pk.att_pps);
+    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + kPkWaves * P - 1) / (kPkWaves * P));
+    pk.att_smax = (c.max_pages + kPkWaves * pk.att_pps - 1) / (kPkWaves * pk.att_pps);
     W4_CHECK(c.n_q_heads * pk.att_smax <= P, W4_EINVAL, "too many attention chunks for the grid");
     // two work-groups per CU: the first-dispatched half of the grid gets the
     // larger share of every phase (measured: it gets through a phase faster)
@@ -728,7 +728,8 @@ static w4_status setup_persistent(w4_model *m) {
                     phase_geometry(rb_lm * nkc, nkc, 32, P, 1, 1, pk.slots_lm, why);
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
     // normalised inputs are staged whole, one element per thread and batch slot
-    W4_CHECK(d <= kStageMax * kThreads && d * 2 <= kStageBytes, W4_EINVAL, "d_model too large for the persistent step");
+    W4_CHECK(d <= kStageMax * kPkThreads && d * 2 <= kStageBytes, W4_EINVAL,
+             "d_model too large for the persistent step");
 
     // step-parity blocks: accumulators of every layer, then counters (per
     // layer: 4 phases x groups, one per head; then the embedding counter)
