@@ -13,6 +13,10 @@ something other than itself live in ``tests/test_oracle_pins.py``.
 Parity status of each function (what pins it):
 
 * ``deq``, ``gemv``: exhaustive exactness + rational brute force — pinned;
+* ``quantize_act_int8``, ``gemv_w4a8`` (int8 activations): rational brute force of
+  the quantiser's definition, reconstruction bound, extreme-value and zero-group
+  cases, exact rational GEMV, and equality with ``gemv`` when the activations
+  are exactly representable — pinned;
 * ``rmsnorm``, ``rope``, ``silu``, ``swiglu``: closed forms and invariants — pinned;
 * ``paged_attention``, ``causal_attention``: one-token, two-token closed form,
   uniform-key mean, GQA mapping, page-shuffle invariance — pinned;

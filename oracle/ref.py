@@ -31,7 +31,7 @@ import numpy as np
 F64 = np.float64
 
 __all__ = [
-    "f16", "deq", "gemv", "rmsnorm", "rope", "silu", "swiglu", "softmax",
+    "f16", "deq", "gemv", "quantize_act_int8", "gemv_w4a8", "rmsnorm", "rope", "silu", "swiglu", "softmax",
     "paged_attention", "causal_attention", "mlp", "argmax_first",
     "KVCache", "layer_step", "decode_step", "forward_teacher_forced",
 ]
@@ -67,6 +67,43 @@ def gemv(q: np.ndarray, s: np.ndarray, x: np.ndarray, group: int = 128) -> np.nd
     if x.ndim == 1:
         return w @ x
     return x @ w.T
+
+
+# --------------------------------------------------------------------------
+# W4A8 GEMV: int8 activations ("Path A" of [TS] "Engineering Challenges",
+# item 3, and [SP] "Three Critical Engineering Challenges", item 3: weights and
+# activations both integer, so the inner products run on integer dot-product
+# instructions, after a separate step that quantises the fp16 activations).
+# The pages do not give the activation quantiser; the reading used here is
+# symmetric, per group of 128 along K (the weights' groups): one float32
+# scale per group, s = max|x| / 127 rounded to float32, codes
+# round-half-even(x / s) in float32, clamped to [-127, 127]; an all-zero group
+# has scale 0 and zero codes.
+# --------------------------------------------------------------------------
+
+def quantize_act_int8(x: np.ndarray, group: int = 128) -> tuple:
+    """(codes int8 [K], scales float32 [K / group]) of an fp16 activation vector."""
+    x = np.asarray(x, dtype=np.float16)
+    k = x.shape[0]
+    if k % group:
+        raise ValueError(f"K={k} is not a multiple of {group}")
+    xg = x.astype(np.float32).reshape(k // group, group)
+    amax = np.max(np.abs(xg), axis=1)
+    scales = (amax / np.float32(127.0)).astype(np.float32)
+    codes = np.zeros_like(xg, dtype=np.int8)
+    for g in range(k // group):
+        if scales[g] == 0:
+            continue
+        r = np.rint(xg[g] / scales[g]).astype(np.float32)     # float32 quotient, ties to even
+        codes[g] = np.clip(r, -127, 127).astype(np.int8)
+    return codes.reshape(k), scales
+
+
+def gemv_w4a8(q: np.ndarray, s: np.ndarray, xq: np.ndarray, xs: np.ndarray, group: int = 128) -> np.ndarray:
+    """y = deq(q, s) @ (xq * xs per group), in float64: the plain definition of
+    the integer-activation GEMV (every product q * s * xq * xs is exact in fp64)."""
+    xdeq = np.asarray(xq, dtype=F64) * np.repeat(np.asarray(xs, dtype=F64), group)
+    return deq(q, s, group) @ xdeq
 
 
 # --------------------------------------------------------------------------

@@ -101,6 +101,93 @@ def test_gemv_rational_bruteforce():
             assert err <= mag * Fraction(1, 2 ** 44), (n, float(err))
 
 
+# ------------------------------------------------ int8 activations (W4A8) ---
+
+def _round_f32(fr: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to binary32 (by bracketing)."""
+    if fr == 0:
+        return Fraction(0)
+    c = np.float32(float(fr))
+    lo, hi = np.nextafter(c, np.float32(-np.inf)), np.nextafter(c, np.float32(np.inf))
+    best = None
+    for cand in (lo, c, hi):
+        d = abs(Fraction(float(cand)) - fr)
+        key = (d, int(np.array(cand, np.float32).view(np.uint32)) & 1)   # ties: even mantissa
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return Fraction(float(best[1]))
+
+
+def _round_half_even(fr: Fraction) -> int:
+    f = math.floor(fr)
+    rem = fr - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
+def test_quantize_act_rational_bruteforce():
+    """Scales and codes equal the quantiser's definition evaluated in exact
+    rationals with explicit float32 roundings (groups of several magnitudes,
+    fp16 subnormals and a group that is all zero)."""
+    r = np.random.default_rng(11)
+    x = (r.standard_normal(4 * 128) * np.repeat([1.0, 1e-3, 300.0, 1e-6], 128)).astype(np.float16)
+    x[256 + 5] = np.float16(-65504.0)          # the largest magnitude fp16
+    x = np.concatenate([x, np.zeros(128, np.float16)])
+    codes, scales = oracle.quantize_act_int8(x)
+    assert codes.dtype == np.int8 and scales.dtype == np.float32
+    for g in range(len(x) // 128):
+        xs = [Fraction(float(v)) for v in x[g * 128:(g + 1) * 128]]
+        amax = max(abs(v) for v in xs)
+        sc = _round_f32(amax / 127)
+        assert Fraction(float(scales[g])) == sc, g
+        for i, v in enumerate(xs):
+            want = 0 if sc == 0 else max(-127, min(127, _round_half_even(_round_f32(v / sc))))
+            assert int(codes[g * 128 + i]) == want, (g, i)
+
+
+def test_quantize_act_bounds_and_extremes():
+    """|x - code * scale| <= scale / 2 (plus the float32 quotient's rounding),
+    the largest magnitude of a group maps to +-127, zero groups stay zero."""
+    x = synth.gemv_cfg0()[2]
+    codes, scales = oracle.quantize_act_int8(x)
+    xr = codes.astype(np.float64) * np.repeat(scales.astype(np.float64), 128)
+    err = np.abs(x.astype(np.float64) - xr)
+    assert np.all(err <= np.repeat(scales.astype(np.float64), 128) * (0.5 + 2 ** -20))
+    xg = np.abs(x.astype(np.float64)).reshape(-1, 128)
+    cg = np.abs(codes.astype(np.int64)).reshape(-1, 128)
+    assert np.all(cg[np.arange(len(cg)), np.argmax(xg, axis=1)] == 127)
+    assert np.all(cg <= 127)
+    z, zs = oracle.quantize_act_int8(np.zeros(256, np.float16))
+    assert np.all(z == 0) and np.all(zs == 0)
+
+
+def test_gemv_w4a8_rational_and_reduces_to_w4a16():
+    """The W4A8 GEMV is the exact rational sum of code * scale * code * scale
+    (within fp64 rounding), and equals the W4A16 GEMV when the activations are
+    exactly code * power-of-two scale."""
+    q, s, x = synth.gemv_case(4, 384, cfg=91)
+    xq, xs = oracle.quantize_act_int8(x)
+    y = oracle.gemv_w4a8(q, s, xq, xs)
+    for n in range(4):
+        exact, mag = Fraction(0), Fraction(0)
+        for kk in range(384):
+            t = (Fraction(int(q[n, kk])) * Fraction(float(s[n, kk // 128])) *
+                 Fraction(int(xq[kk])) * Fraction(float(xs[kk // 128])))
+            exact += t
+            mag += abs(t)
+        assert abs(Fraction(float(y[n])) - exact) <= mag * Fraction(1, 2 ** 44)
+    r = np.random.default_rng(12)
+    codes = r.integers(-127, 128, 384)
+    codes[::128] = 127                                           # every group reaches 127
+    scale = np.repeat([2.0 ** -7, 2.0 ** -3, 2.0 ** -10], 128)
+    xe = (codes * scale).astype(np.float16)
+    assert np.array_equal(xe.astype(np.float64), codes * scale)   # exactly representable
+    xq2, xs2 = oracle.quantize_act_int8(xe)
+    assert np.array_equal(xq2.astype(np.int64), codes)
+    assert np.array_equal(oracle.gemv_w4a8(q, s, xq2, xs2), oracle.gemv(q, s, xe))
+
+
 # ------------------------------------------------------------------- glue ---
 
 def test_rmsnorm_closed_forms():
