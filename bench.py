@@ -628,6 +628,38 @@ def standalone_kernels(attention: bool = True):
                        "launches": 3, "copies": R}
     del bgq, bgs, bdq, bds
 
+    # int8 activations (the pages' integer path) on the config 0 and config 1 shapes: the
+    # quantisation launch and the GEMV, each timed alone
+    for name, (n, k, pq_, ps_) in (("w4a8_gemv_3584x3584", (3584, 3584, pq, ps)),
+                                   ("w4a8_gemv_37888x3584", (2 * f, d, pgq, pgs)),
+                                   ("w4a8_gemv_3584x18944", (d, f, pdq, pds))):
+        nb = pq_.nbytes + ps_.nbytes
+        R = max(2, -(-ROTATE_BYTES // nb))
+        bq, bs = rotated(pq_, R), rotated(ps_, R)
+        xk = torch.from_numpy(synth.normal_f16(synth.rng(0, synth.GLOBAL_LAYER, synth.T_X), (k,))).to(dev)
+        act = torch.empty(lib.w4a8_act_bytes(k), dtype=torch.uint8, device=dev)
+        L.check(lib.w4a8_quantize_act(xk.data_ptr(), k, act.data_ptr(), cur()))
+        yk = torch.empty(n, dtype=torch.float16, device=dev)
+        wsk = torch.zeros(max(lib.w4_gemv_ws_bytes(n, k), 256), dtype=torch.uint8, device=dev)
+
+        def mk8(r, bq=bq, bs=bs, act=act, yk=yk, wsk=wsk, n=n, k=k):
+            def c():
+                L.check(lib.w4a8_gemv(bq[r].data_ptr(), bs[r].data_ptr(), act.data_ptr(), yk.data_ptr(), n, k,
+                                      wsk.data_ptr(), wsk.numel(), cur()))
+            return c
+
+        def mkq(xk=xk, act=act, k=k):
+            def c():
+                L.check(lib.w4a8_quantize_act(xk.data_ptr(), k, act.data_ptr(), cur()))
+            return c
+        us = _graph_time_us(torch, [mk8(r) for r in range(R)])
+        qus = _graph_time_us(torch, [mkq() for _ in range(64)])
+        b = n * k // 2 + n * (k // 128) * 2 + lib.w4a8_act_bytes(k) + n * 2
+        out[name] = {"N": n, "K": k, "us_per_call": round(us, 2), "bytes": b,
+                     "GBps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "quantize_us_per_call": round(qus, 2), "copies": R}
+        del bq, bs
+
     # config 2: paged decode attention; every call reads its own 40 pages of one large pool
     for ctx in ((640, 8192) if attention else ()):
         n_pg = ctx // 16

@@ -118,6 +118,36 @@ w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_s,
                      const uint16_t *x, uint16_t *y, int64_t N, int64_t K,
                      void *workspace, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * W4A8 GEMV: int8 activations (the pages' integer path, "Path A": [TS]
+ * "Engineering Challenges" item 3 and [SP] "Three Critical Engineering
+ * Challenges" item 3 compare it with the fp16-activation path on an H100;
+ * both weights and activations are integer so the inner products run on
+ * integer dot-product instructions, after a separate quantisation step).
+ * The pages do not give the activation quantiser; here it is symmetric per
+ * group of 128 along K: scale s_g = fp32(max|x| / 127), code
+ * c_k = clamp(round-half-even(fp32(x_k / s_g)), -127, 127); an all-zero
+ * group has s_g = 0 and zero codes.
+ *   y[r] = fp16( sum_g s_w[r][g] * s_g * sum_{k in g} q[r][k] * c_k )
+ * with each group's integer sum exact and the groups added in fp64.
+ *
+ * w4a8_act_bytes(K): size of the quantised-activation buffer (0 for a bad K).
+ * w4a8_quantize_act: x device fp16 [K] -> act (device, written).  Layout of
+ *   act: bytes [0, K) the codes, each block of 8 elements e0..e7 stored as
+ *   the words (e0, e4, e1, e5), (e2, e6, e3, e7); at A = K rounded up to 256
+ *   the fp32 scales [K / 128]; at A + (K / 32 rounded up to 256) the int32
+ *   sums of each group's codes.  One launch; K a positive multiple of 128.
+ * w4a8_gemv: packed_q, packed_s as for w4a16_gemv; act from
+ *   w4a8_quantize_act; y device fp16 [N] (packed row order); workspace
+ *   w4_gemv_ws_bytes(N, K) bytes with the same contract as for w4a16_gemv
+ *   (zero before first use, left zero).
+ * Errors: W4_EINVAL, W4_EALIGN, W4_EHIP. */
+size_t w4a8_act_bytes(int64_t K);
+w4_status w4a8_quantize_act(const uint16_t *x, int64_t K, void *act, void *stream);
+w4_status w4a8_gemv(const uint8_t *packed_q, const uint16_t *packed_s, const void *act,
+                    uint16_t *y, int64_t N, int64_t K, void *workspace, size_t ws_bytes,
+                    void *stream);
+
 /* The MLP decode block of one token, two launches of the w4a16_gemv kernel:
  * the fused gate+up GEMV with its SwiGLU epilogue, then the down GEMV
  * (SwiGLU MLP of the Qwen2.5-7B decode workload; int4 projections as above).

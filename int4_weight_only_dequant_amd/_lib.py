@@ -65,6 +65,9 @@ def _declare(lib):
         "w4_pack_f16_matrix": (i32, [vp, i64, i64, vp]),
         "w4_gemv_ws_bytes": (sz, [i64, i64]),
         "w4a16_gemv": (i32, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
+        "w4a8_act_bytes": (sz, [i64]),
+        "w4a8_quantize_act": (i32, [vp, i64, vp, vp]),
+        "w4a8_gemv": (i32, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
         "w4_mlp_ws_bytes": (sz, [i64, i64]),
         "w4a16_mlp": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp]),
         "w4_gemm_ws_bytes": (sz, [i64, i64, i64]),
@@ -218,6 +221,46 @@ def w4a16_gemv(packed_q: torch.Tensor, packed_s: torch.Tensor, x: torch.Tensor, 
     ws = _workspace("gemv", need, x.device, st)
     check(L.w4a16_gemv(_ptr(packed_q), _ptr(packed_s), _ptr(x), _ptr(y), n, k, _ptr(ws),
                        ws.numel(), st))
+    return y
+
+
+def w4a8_quantize_act(x: torch.Tensor, act: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Int8 activation buffer (codes, group scales and code sums; layout in
+    include/w4a16.h) of an fp16 vector x [K]."""
+    _dev(x)
+    if x.dtype != torch.float16 or x.dim() != 1:
+        raise ValueError("x must be a 1-D fp16 tensor")
+    L = lib()
+    need = L.w4a8_act_bytes(x.numel())
+    if need == 0:
+        raise ValueError("K must be a positive multiple of 128")
+    if act is None:
+        act = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _dev(act)
+    if act.numel() * act.element_size() < need:
+        raise ValueError("activation buffer too small")
+    check(L.w4a8_quantize_act(_ptr(x), x.numel(), _ptr(act), _stream(stream)))
+    return act
+
+
+def w4a8_gemv(packed_q: torch.Tensor, packed_s: torch.Tensor, act: torch.Tensor, n: int, k: int,
+              y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = fp16(W x) with int8 activations from w4a8_quantize_act (rows in packed order)."""
+    _dev(packed_q), _dev(packed_s), _dev(act)
+    L = lib()
+    if act.numel() * act.element_size() < L.w4a8_act_bytes(k):
+        raise ValueError("activation buffer too small for K")
+    if packed_q.numel() * packed_q.element_size() < L.w4_packed_qbytes(n, k):
+        raise ValueError("packed codes too small for N x K")
+    if packed_s.numel() * packed_s.element_size() < L.w4_packed_sbytes(n, k):
+        raise ValueError("packed scales too small for N x K")
+    if y is None:
+        y = torch.empty(n, dtype=torch.float16, device=act.device)
+    _dev(y)
+    st = _stream(stream)
+    need = L.w4_gemv_ws_bytes(n, k)
+    ws = _workspace("gemv", need, act.device, st)
+    check(L.w4a8_gemv(_ptr(packed_q), _ptr(packed_s), _ptr(act), _ptr(y), n, k, _ptr(ws), ws.numel(), st))
     return y
 
 

@@ -45,7 +45,8 @@ constexpr int kSgMinTiles = W4_SG_MIN_TILES;   // tiles per work-group below whi
 struct SgProblem {
     const u32x4 *wq;          // packed codes
     const uint16_t *ws;       // packed scales
-    const uint32_t *x;        // activations as fp16 pairs, K/2 words
+    const uint32_t *x;        // activations as fp16 pairs, K/2 words (int8: the activation buffer)
+    uint32_t a8_scales, a8_sums;   // int8 activations: byte offsets of scales and sums in x
     int ng;                   // K / 128
     int T;                    // tiles = row blocks * ng
     int P;                    // work-groups
@@ -119,7 +120,83 @@ __device__ __forceinline__ double sg_tile(const u32x4 (&w)[4], uint16_t s, const
     return static_cast<double>(__builtin_fmaf(acc16, 0.0625f, acc1)) * static_cast<double>(f16_to_f32(s));
 }
 
-template <class Epi>
+// ---------------------------------------------------------------------------
+// Int8 activations (the pages' integer path: "Building a Custom LLM Inference
+// Runtime…", section "Engineering Challenges" item 3, and "The Architecture of
+// Modern Inference…", section "Three Critical Engineering Challenges" item 3).
+// The fp16 activations are quantised by a separate kernel, per group of 128
+// along K: scale s = max|x| / 127 in fp32, codes round-half-even(x / s) in
+// fp32, clamped to [-127, 127] (scale 0 and zero codes for an all-zero group).
+// Activation buffer (device, w4a8_act_bytes(K) bytes):
+//   [0, K)            int8 codes; each block of 8 elements e0..e7 is stored as
+//                     two words (e0, e4, e1, e5), (e2, e6, e3, e7), matching the
+//                     bytes (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) of a
+//                     packed weight word (e0 e2 e4 e6 in the low half-word,
+//                     e1 e3 e5 e7 in the high half-word);
+//   [A, A + K/32)     fp32 scales, A = K rounded up to 256;
+//   [B, B + K/32)     int32 sums of each group's codes, B = A + (K/32 rounded
+//                     up to 256).
+// A group's integer dot product sum_k (u_k - 8) c_k = sum_k u_k c_k - 8 sum_k c_k
+// (u = q + 8, the stored nibble) runs on v_dot4_i32_i8: two of them per packed
+// word, four bytes each, exact in int32.  Scaled by s_w * s_x in fp64 it is
+// exact (11 + 24 + 18 bits), and the groups are added in fp64.
+
+inline size_t a8_scales_off(int64_t K) { return static_cast<size_t>((K + 255) & ~int64_t(255)); }
+inline size_t a8_sums_off(int64_t K) { return a8_scales_off(K) + ((static_cast<size_t>(K / 128) * 4 + 255) & ~size_t(255)); }
+inline size_t a8_act_bytes(int64_t K) { return a8_sums_off(K) + static_cast<size_t>(K / 128) * 4; }
+
+// One wave per group of 128 activations; lane l quantises elements 2l, 2l+1.
+__global__ __launch_bounds__(64) void a8_quantize_kernel(const uint16_t *x, int8_t *codes, float *scales,
+                                                         int *sums) {
+    const int g = blockIdx.x, lane = threadIdx.x;
+    const uint32_t pair = reinterpret_cast<const uint32_t *>(x + static_cast<size_t>(g) * 128)[lane];
+    const float v0 = f16_to_f32(static_cast<uint16_t>(pair & 0xFFFFu));
+    const float v1 = f16_to_f32(static_cast<uint16_t>(pair >> 16));
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float sc = amax / 127.0f;                 // IEEE division, rounded to nearest even
+    int c0 = 0, c1 = 0;
+    if (sc != 0.0f) {
+        c0 = static_cast<int>(fminf(fmaxf(rintf(v0 / sc), -127.0f), 127.0f));
+        c1 = static_cast<int>(fminf(fmaxf(rintf(v1 / sc), -127.0f), 127.0f));
+    }
+    int sum = c0 + c1;
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    // element e of the group: block e / 8, position p = e % 8 -> byte
+    // 8 (e / 8) + 4 ((p >> 1) & 1) + ((p >> 2) & 1) + 2 (p & 1)
+    int8_t *cg = codes + static_cast<size_t>(g) * 128;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = 2 * lane + u, pp = e & 7;
+        cg[(e & ~7) + 4 * ((pp >> 1) & 1) + ((pp >> 2) & 1) + 2 * (pp & 1)] = static_cast<int8_t>(u ? c1 : c0);
+    }
+    if (lane == 0) {
+        scales[g] = sc;
+        sums[g] = sum;
+    }
+}
+
+// One tile's scaled group sum with int8 activations: xg = the group's 32
+// code words, sx its scale, sumc the sum of its codes.
+__device__ __forceinline__ double sg_tile_a8(const u32x4 (&w)[4], uint16_t s, const_u32_ptr xg, float sx,
+                                             int sumc) {
+    int acc = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t ws4[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = c * 4 + i;                 // block of 8 elements within the group
+            const int lo = static_cast<int>(ws4[i] & 0x0F0F0F0Fu), hi = static_cast<int>((ws4[i] >> 4) & 0x0F0F0F0Fu);
+            acc = __builtin_amdgcn_sdot4(lo, static_cast<int>(xg[2 * b]), acc, false);
+            acc = __builtin_amdgcn_sdot4(hi, static_cast<int>(xg[2 * b + 1]), acc, false);
+        }
+    }
+    const int dot = acc - 8 * sumc;
+    return static_cast<double>(f16_to_f32(s)) * static_cast<double>(sx) * static_cast<double>(dot);
+}
+
+template <class Epi, bool kA8 = false>
 __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi) {
     __shared__ double red[kSgMaxRl * 256];
     const int B = blockIdx.x;
@@ -147,7 +224,13 @@ __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi)
             acc = 0.0;
             cur = rl;
         }
-        acc += sg_tile(w, s, xc + g * 64, m_lo, m_hi, magic);
+        if constexpr (kA8) {
+            const const_u32_ptr aux = as_const(p.x);
+            acc += sg_tile_a8(w, s, xc + g * 32, __builtin_bit_cast(float, aux[p.a8_scales / 4 + g]),
+                              static_cast<int>(aux[p.a8_sums / 4 + g]));
+        } else {
+            acc += sg_tile(w, s, xc + g * 64, m_lo, m_hi, magic);
+        }
     };
     while (t < t_end) {
         if (t + 4 < t_end) sg_load(wb, sb, p, t + 4);

@@ -145,8 +145,8 @@ static bool sg_shape_ok(int64_t N, int64_t K) {
     return N >= 1 && K >= kGroup && K % kGroup == 0 && ((N + 63) / 64) * (K / kGroup) < (int64_t(1) << 31);
 }
 
-template <class Epi>
-static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const uint16_t *x, int64_t N, int64_t K,
+template <class Epi, bool kA8 = false>
+static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const void *x, int64_t N, int64_t K,
                             void *ws, const Epi &epi, hipStream_t s) {
     const int n_rb = static_cast<int>((N + 63) / 64), ng = static_cast<int>(K / kGroup);
     const SgGeom g = sg_geom(n_rb, ng);
@@ -154,6 +154,8 @@ static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const uint16_t
     p.wq = reinterpret_cast<const u32x4 *>(q);
     p.ws = sc;
     p.x = reinterpret_cast<const uint32_t *>(x);
+    p.a8_scales = static_cast<uint32_t>(a8_scales_off(K));
+    p.a8_sums = static_cast<uint32_t>(a8_sums_off(K));
     p.ng = ng;
     p.T = g.T;
     p.P = g.P;
@@ -161,7 +163,7 @@ static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const uint16_t
     p.key_by_rb = g.key_by_rb;
     p.ctr = static_cast<unsigned *>(ws);
     p.slots = reinterpret_cast<double *>(static_cast<char *>(ws) + sg_ctr_bytes(g));
-    hipLaunchKernelGGL(sg_gemv_kernel<Epi>, dim3(g.P), dim3(kThreads), 0, s, p, epi);
+    hipLaunchKernelGGL((sg_gemv_kernel<Epi, kA8>), dim3(g.P), dim3(kThreads), 0, s, p, epi);
     return hipGetLastError();
 }
 
@@ -186,6 +188,44 @@ extern "C" w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_
              "workspace of %zu bytes given (16-byte aligned), %zu needed", ws_bytes, need);
     W4_HIP(launch_sg(packed_q, packed_s, x, N, K, workspace, EpiStoreF16{y, static_cast<int>(N)},
                      static_cast<hipStream_t>(stream)));
+    return W4_OK;
+}
+
+// ----------------------------------------------------- int8 activations --
+
+extern "C" size_t w4a8_act_bytes(int64_t K) {
+    if (K < kGroup || K % kGroup || K > (int64_t(1) << 24)) return 0;
+    return a8_act_bytes(K);
+}
+
+extern "C" w4_status w4a8_quantize_act(const uint16_t *x, int64_t K, void *act, void *stream) {
+    clear_error();
+    W4_CHECK(K >= kGroup && K % kGroup == 0 && K <= (int64_t(1) << 24), W4_EINVAL,
+             "K=%lld must be a positive multiple of 128", (long long)K);
+    W4_CHECK(aligned16(x) && aligned16(act), W4_EALIGN, "x and act must be 16-byte aligned device pointers");
+    char *a = static_cast<char *>(act);
+    hipLaunchKernelGGL(a8_quantize_kernel, dim3(static_cast<unsigned>(K / kGroup)), dim3(64), 0,
+                       static_cast<hipStream_t>(stream), x, reinterpret_cast<int8_t *>(a),
+                       reinterpret_cast<float *>(a + a8_scales_off(K)), reinterpret_cast<int *>(a + a8_sums_off(K)));
+    W4_HIP(hipGetLastError());
+    return W4_OK;
+}
+
+extern "C" w4_status w4a8_gemv(const uint8_t *packed_q, const uint16_t *packed_s, const void *act, uint16_t *y,
+                               int64_t N, int64_t K, void *workspace, size_t ws_bytes, void *stream) {
+    clear_error();
+    W4_CHECK(N >= 1 && N <= (int64_t(1) << 31) - 64, W4_EINVAL, "bad N=%lld", (long long)N);
+    W4_CHECK(K >= kGroup && K % kGroup == 0 && K <= (int64_t(1) << 24), W4_EINVAL,
+             "K=%lld must be a positive multiple of 128", (long long)K);
+    W4_CHECK(aligned16(packed_q) && aligned16(packed_s) && aligned16(act), W4_EALIGN,
+             "packed_q, packed_s and act must be 16-byte aligned device pointers");
+    W4_CHECK(y != nullptr && (reinterpret_cast<uintptr_t>(y) & 1) == 0, W4_EALIGN, "bad y pointer");
+    W4_CHECK(sg_shape_ok(N, K), W4_EINVAL, "N=%lld x K=%lld is too large", (long long)N, (long long)K);
+    const size_t need = w4_gemv_ws_bytes(N, K);
+    W4_CHECK(ws_bytes >= need && aligned16(workspace), W4_EINVAL,
+             "workspace of %zu bytes given (16-byte aligned), %zu needed", ws_bytes, need);
+    W4_HIP((launch_sg<EpiStoreF16, true>(packed_q, packed_s, act, N, K, workspace, EpiStoreF16{y, static_cast<int>(N)},
+                                         static_cast<hipStream_t>(stream))));
     return W4_OK;
 }
 

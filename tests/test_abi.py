@@ -38,6 +38,13 @@ def test_host_side_argument_errors():
     # workspace too small
     assert lib.w4a16_gemv(p, p, p, p, 4096, 3584, p, 16, None) == L.W4_EINVAL
     assert lib.w4_gemv_ws_bytes(3584, 3584) > 0 and lib.w4_gemv_ws_bytes(3584, 100) == 0
+    # int8 activations: K, alignment, workspace
+    assert lib.w4a8_act_bytes(100) == 0 and lib.w4a8_act_bytes(3584) >= 3584 + 2 * 4 * 28
+    assert lib.w4a8_quantize_act(p, 100, p, None) == L.W4_EINVAL
+    assert lib.w4a8_quantize_act(p + 2, 128, p, None) == L.W4_EALIGN
+    assert lib.w4a8_gemv(p, p, p, p, 64, 100, p, 4096, None) == L.W4_EINVAL
+    assert lib.w4a8_gemv(p, p, p + 4, p, 64, 128, p, 4096, None) == L.W4_EALIGN
+    assert lib.w4a8_gemv(p, p, p, p, 4096, 3584, p, 16, None) == L.W4_EINVAL
     # attention: head_dim, GQA ratio, context range
     assert lib.paged_attn_decode(p, p, p, p, 10, 28, 4, 64, 40, 0.1, p, p, 1 << 15, None) == L.W4_EINVAL
     assert lib.paged_attn_decode(p, p, p, p, 10, 12, 4, 128, 40, 0.1, p, p, 1 << 15, None) == L.W4_EINVAL

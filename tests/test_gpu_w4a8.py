@@ -1,0 +1,106 @@
+"""Int8-activation GEMV (the pages' integer path) on the GPU against the CPU
+oracle: the quantised activations bit-exact, the GEMV within the GEMV
+tolerance of the oracle's W4A8 GEMV on the same quantised activations."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import int4_weight_only_dequant_amd as w4
+from int4_weight_only_dequant_amd import _lib as L
+from tests._tol import assert_gemv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return torch.from_numpy(a).to(DEV)
+    return torch.from_numpy(a.view(np.uint8) if a.dtype != np.int32 else a).to(DEV)
+
+
+def _decode_act(act: np.ndarray, k: int):
+    """(codes in element order, scales, sums) from the documented buffer layout."""
+    a_off = (k + 255) // 256 * 256
+    b_off = a_off + (k // 32 + 255) // 256 * 256
+    codes = act[:k].view(np.int8).reshape(-1, 8)[:, [0, 2, 4, 6, 1, 3, 5, 7]].reshape(k)
+    scales = act[a_off:a_off + k // 32].view(np.float32)
+    sums = act[b_off:b_off + k // 32].view(np.int32)
+    return codes, scales, sums
+
+
+def _act_inputs():
+    r = np.random.default_rng(21)
+    x = (r.standard_normal(8 * 128) * np.repeat([1, 1e-3, 300, 1e-6, 1, 60000 / 4, 1, 1], 128)).astype(np.float16)
+    x[3 * 128 + 7] = np.float16(6e-8)           # fp16 subnormal
+    x[6 * 128:7 * 128] = 0                      # an all-zero group
+    x[7 * 128:8 * 128] = np.float16(-2.5)       # a constant group
+    return [("mixed", x), ("cfg0", synth.gemv_cfg0()[2]),
+            ("mlp-h", synth.normal_f16(synth.rng(98, 1000, 40), (18944,)))]
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_w4a8_quantize_bitexact(case):
+    name, x = _act_inputs()[case]
+    k = x.shape[0]
+    say(f"case: w4a8 quantise {name} K={k}")
+    act = w4.w4a8_quantize_act(_dev(x))
+    torch.cuda.synchronize()
+    codes, scales, sums = _decode_act(act.cpu().numpy(), k)
+    rc, rs = oracle.quantize_act_int8(x)
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(sums, rc.astype(np.int64).reshape(-1, 128).sum(axis=1))
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (64, 128), (100, 384), (257, 3584), (3584, 3584),
+                                 (3584, 18944), (37888, 3584), (130, 1024)])
+def test_w4a8_gemv_vs_oracle(n, k):
+    say(f"case: w4a8 gemv N={n} K={k}")
+    q, s, x = synth.gemv_case(n, k, cfg=99)
+    pq, ps = w4.pack_int4_weights(q, s)
+    act = w4.w4a8_quantize_act(_dev(x))
+    y = w4.w4a8_gemv(_dev(pq), _dev(ps), act, n, k)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    xq, xs = oracle.quantize_act_int8(x)
+    assert_gemv(y, oracle.gemv_w4a8(q, s, xq, xs), f"w4a8 N={n} K={k}")
+    # the activation quantisation's own effect, against the fp16-activation oracle (reported)
+    y16 = oracle.gemv(q, s, x)
+    dev = float(np.max(np.abs(y - y16)) / np.sqrt(np.mean(y16 * y16)))
+    say(f"  max deviation from the fp16-activation GEMV: {dev:.3e} of its RMS")
+
+
+def test_w4a8_edge_values_and_determinism():
+    """Extreme codes and scales, subnormal and zero activations; 50 repeats bit-identical."""
+    say("case: w4a8 edge values + repeat")
+    n, k = 128, 512
+    r = np.random.default_rng(3)
+    q = np.where(r.random((n, k)) < 0.5, -8, 7).astype(np.int8)
+    s = np.full((n, k // 128), 1.0, np.float16)
+    s[:, 0] = np.float16(6e-8)
+    s[:, 1] = np.float16(60000.0)
+    s[:, 2] = np.float16(-2.0)
+    x = (r.standard_normal(k) * 1e-3).astype(np.float16)
+    x[::7] = np.float16(3e-7)
+    x[384:] = 0
+    pq, ps = w4.pack_int4_weights(q, s)
+    dq, ds, dx = _dev(pq), _dev(ps), _dev(x)
+    act = w4.w4a8_quantize_act(dx)
+    first = w4.w4a8_gemv(dq, ds, act, n, k).clone()
+    for _ in range(50):
+        y = w4.w4a8_gemv(dq, ds, act, n, k)
+    torch.cuda.synchronize()
+    assert torch.equal(first, y)
+    xq, xs = oracle.quantize_act_int8(x)
+    assert_gemv(first.cpu().numpy(), oracle.gemv_w4a8(q, s, xq, xs), "w4a8 edge")
