@@ -80,6 +80,18 @@ w4_status pack_int4_weights(const int8_t *q, const uint16_t *scales, int64_t N,
                             int64_t K, int32_t group, const int32_t *row_perm,
                             uint8_t *packed_q, uint16_t *packed_s);
 
+/* fp16 -> int4 quantiser, the step before pack_int4_weights (the pages keep
+ * symmetric group-wise int4 weights with one fp16 scale per group of 128
+ * but do not give the quantiser).  Per row and group of 128 along K:
+ *   scales[n][g] = fp16(max_k |w[n][k]| / 7)   (one rounding of the exact quotient)
+ *   q[n][k]      = clamp(round-half-even(w[n][k] / scales[n][g]), -8, 7)
+ * and zero codes where the scale rounds to zero.  w: host fp16 [N][K]; q:
+ * host int8 [N][K] and scales: host fp16 [N][K/128], written.  group must be
+ * 128.  Errors: W4_EINVAL (shape, group), W4_ERANGE (a non-finite weight),
+ * W4_EALIGN (NULL pointer). */
+w4_status quantize_int4_weights(const uint16_t *w, int64_t N, int64_t K, int32_t group,
+                                int8_t *q, uint16_t *scales);
+
 /* Exact inverse of pack_int4_weights (same arguments, data flowing back). */
 w4_status unpack_int4_weights(const uint8_t *packed_q, const uint16_t *packed_s,
                               int64_t N, int64_t K, int32_t group,

@@ -8,6 +8,6 @@ int8 activations ``w4a8_quantize_act``, ``w4a8_gemv``.
 """
 from ._lib import (W4Error, W4_EAGER, W4_GRAPH, W4_MULTI, W4_PERM_GATE_UP, W4_PERM_QKV, ModelConfig,  # noqa: F401
                    lib, model_row_perm, pack_f16_matrix, pack_int4_weights, paged_attn_decode,
-                   paged_attn_prefill, unpack_int4_weights, w4a8_gemv, w4a8_quantize_act, w4a16_gemm,
+                   paged_attn_prefill, quantize_int4_weights, unpack_int4_weights, w4a8_gemv, w4a8_quantize_act, w4a16_gemm,
                    w4a16_gemv, w4a16_mlp)
 from .model import DecodeModel, decode_step, prefill  # noqa: F401

@@ -61,6 +61,7 @@ def _declare(lib):
         "w4_packed_sbytes": (sz, [i64, i64]),
         "pack_int4_weights": (i32, [vp, vp, i64, i64, i32, vp, vp, vp]),
         "unpack_int4_weights": (i32, [vp, vp, i64, i64, i32, vp, vp, vp]),
+        "quantize_int4_weights": (i32, [vp, i64, i64, i32, vp, vp]),
         "w4_packed_f16_bytes": (sz, [i64, i64]),
         "w4_pack_f16_matrix": (i32, [vp, i64, i64, vp]),
         "w4_gemv_ws_bytes": (sz, [i64, i64]),
@@ -153,6 +154,16 @@ def pack_int4_weights(q: np.ndarray, s: np.ndarray, row_perm: np.ndarray | None 
     check(L.pack_int4_weights(_ptr(q), _ptr(s), n, k, 128, None if perm is None else _ptr(perm),
                               _ptr(pq), _ptr(ps)))
     return pq, ps
+
+
+def quantize_int4_weights(w: np.ndarray):
+    """Host quantiser: fp16 weights [N, K] -> (codes int8 [N, K], scales fp16 [N, K/128])."""
+    w = np.ascontiguousarray(w, dtype=np.float16)
+    n, k = w.shape
+    q = np.empty((n, k), np.int8)
+    s = np.empty((n, max(k // 128, 1)), np.float16)
+    check(lib().quantize_int4_weights(_ptr(w), n, k, 128, _ptr(q), _ptr(s)))
+    return q, s
 
 
 def unpack_int4_weights(pq: np.ndarray, ps: np.ndarray, n: int, k: int,

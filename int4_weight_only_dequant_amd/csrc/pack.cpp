@@ -169,6 +169,49 @@ w4_status w4_pack_f16_matrix(const uint16_t *w, int64_t N, int64_t K, uint16_t *
     return W4_OK;
 }
 
+// fp16 -> int4 quantiser: scale = fp16(max|w| / 7) (the fp64 quotient of two
+// values with at most 11 significant bits is rounded once more to fp16; the
+// exact quotient's binary expansion repeats with period 3, so it is never
+// within fp64 rounding of an fp16 tie and the two roundings equal one),
+// code = clamp(round-half-even(w / scale), -8, 7), exact in fp64 (a tie of
+// w / scale cannot be created or lost by the fp64 quotient either).
+static double f16_value(uint16_t b) {
+    const int e = (b >> 10) & 0x1F, m = b & 0x3FF;
+    const double v = e ? ldexp(1024.0 + m, e - 25) : ldexp(static_cast<double>(m), -24);
+    return (b & 0x8000) ? -v : v;
+}
+
+w4_status quantize_int4_weights(const uint16_t *w, int64_t N, int64_t K, int32_t group, int8_t *q,
+                                uint16_t *scales) {
+    clear_error();
+    if (!w || !q || !scales) return fail(W4_EALIGN, "NULL pointer");
+    const w4_status st = check_shape(N, K, group);
+    if (st != W4_OK) return st;
+    const int64_t ng = K / kGroup;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const uint16_t *wg = w + n * K + g * kGroup;
+            double amax = 0.0;
+            for (int i = 0; i < kGroup; ++i) {
+                if (!f16_finite(wg[i])) return fail(W4_ERANGE, "non-finite weight at (%lld, %lld)", (long long)n, (long long)(g * kGroup + i));
+                amax = fmax(amax, fabs(f16_value(wg[i])));
+            }
+            const _Float16 s16 = static_cast<_Float16>(amax / 7.0);
+            uint16_t sbits;
+            memcpy(&sbits, &s16, 2);
+            scales[n * ng + g] = sbits;
+            const double sv = static_cast<double>(s16);
+            int8_t *qg = q + n * K + g * kGroup;
+            for (int i = 0; i < kGroup; ++i) {
+                double c = sv > 0.0 ? nearbyint(f16_value(wg[i]) / sv) : 0.0;   // ties to even
+                c = c < -8.0 ? -8.0 : (c > 7.0 ? 7.0 : c);
+                qg[i] = static_cast<int8_t>(c);
+            }
+        }
+    }
+    return W4_OK;
+}
+
 w4_status w4_model_row_perm(int32_t kind, const w4_model_config *cfg, int32_t *perm) {
     clear_error();
     if (!cfg || !perm) return fail(W4_EALIGN, "NULL pointer");

@@ -13,6 +13,8 @@ something other than itself live in ``tests/test_oracle_pins.py``.
 Parity status of each function (what pins it):
 
 * ``deq``, ``gemv``: exhaustive exactness + rational brute force — pinned;
+* ``quantize_int4`` (fp16 -> int4 weights): exact-rational brute force of its
+  definition, reconstruction bound, extremes and zero groups — pinned;
 * ``quantize_act_int8``, ``gemv_w4a8`` (int8 activations): rational brute force of
   the quantiser's definition, reconstruction bound, extreme-value and zero-group
   cases, exact rational GEMV, and equality with ``gemv`` when the activations

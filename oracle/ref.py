@@ -31,7 +31,7 @@ import numpy as np
 F64 = np.float64
 
 __all__ = [
-    "f16", "deq", "gemv", "quantize_act_int8", "gemv_w4a8", "rmsnorm", "rope", "silu", "swiglu", "softmax",
+    "f16", "deq", "gemv", "quantize_int4", "quantize_act_int8", "gemv_w4a8", "rmsnorm", "rope", "silu", "swiglu", "softmax",
     "paged_attention", "causal_attention", "mlp", "argmax_first",
     "KVCache", "layer_step", "decode_step", "forward_teacher_forced",
 ]
@@ -67,6 +67,32 @@ def gemv(q: np.ndarray, s: np.ndarray, x: np.ndarray, group: int = 128) -> np.nd
     if x.ndim == 1:
         return w @ x
     return x @ w.T
+
+
+# --------------------------------------------------------------------------
+# fp16 -> int4 weight quantiser (the step before the packed weights: the
+# pages store symmetric group-wise INT4 weights with one fp16 scale per group
+# of 128, [TS] "Technical Specifications and Hardware Alignment" and
+# ".nanoqwen File Format"; they do not give the quantiser).  Reading: per
+# group, scale = fp16(max|w| / 7) (the exact quotient rounded once to fp16),
+# code = clamp(round-half-even(w / scale), -8, 7); a group whose scale
+# rounds to zero gets zero codes.
+# --------------------------------------------------------------------------
+
+def quantize_int4(w: np.ndarray, group: int = 128) -> tuple:
+    """(codes int8 [N, K] in [-8, 7], scales fp16 [N, K / group]) of fp16 weights."""
+    w = np.asarray(w, dtype=np.float16)
+    n, k = w.shape
+    if k % group:
+        raise ValueError(f"K={k} is not a multiple of {group}")
+    wg = w.astype(F64).reshape(n, k // group, group)
+    amax = np.max(np.abs(wg), axis=2)
+    scales = (amax / 7.0).astype(np.float16)              # fp64 quotient, one rounding to fp16
+    s64 = scales.astype(F64)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(s64 > 0, np.rint(wg / np.where(s64 > 0, s64, 1.0)), 0.0)
+    codes = np.clip(r, -8, 7).astype(np.int8).reshape(n, k)
+    return codes, scales
 
 
 # --------------------------------------------------------------------------

@@ -101,6 +101,54 @@ def test_gemv_rational_bruteforce():
             assert err <= mag * Fraction(1, 2 ** 44), (n, float(err))
 
 
+# ------------------------------------------------- fp16 -> int4 quantiser ---
+
+def _round_f16(fr: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to binary16 (by bracketing)."""
+    if fr == 0:
+        return Fraction(0)
+    c = np.float16(float(fr))
+    cands = [np.nextafter(c, np.float16(-np.inf)), c, np.nextafter(c, np.float16(np.inf))]
+    best = min(cands, key=lambda v: (abs(Fraction(float(v)) - fr),
+                                     int(np.array(v, np.float16).view(np.uint16)) & 1))
+    return Fraction(float(best))
+
+
+def test_quantize_int4_rational_bruteforce():
+    """Scales and codes equal the quantiser's definition in exact rationals
+    with one explicit fp16 rounding (groups of several magnitudes, fp16
+    subnormals, the largest fp16, a zero group and a group whose scale
+    underflows to zero)."""
+    r = np.random.default_rng(13)
+    w = (r.standard_normal((3, 4 * 128)) * np.repeat([0.02, 1e-5, 500.0, 1.0], 128)).astype(np.float16)
+    w[1, 300] = np.float16(65504.0)
+    w[2, 0:128] = 0
+    w[2, 128:256] = np.float16(6e-8)                     # max/7 rounds to zero in fp16
+    codes, scales = oracle.quantize_int4(w)
+    assert codes.dtype == np.int8 and scales.dtype == np.float16
+    for n in range(3):
+        for g in range(4):
+            ws = [Fraction(float(v)) for v in w[n, g * 128:(g + 1) * 128]]
+            sc = _round_f16(max(abs(v) for v in ws) / 7)
+            assert Fraction(float(scales[n, g])) == sc, (n, g)
+            for i, v in enumerate(ws):
+                want = 0 if sc == 0 else max(-8, min(7, _round_half_even(v / sc)))
+                assert int(codes[n, g * 128 + i]) == want, (n, g, i)
+
+
+def test_quantize_int4_bounds():
+    """|w - code * scale| <= scale / 2 except where a code is clamped at -8..7,
+    and every group's largest magnitude maps to +-7 (or clamps from 8)."""
+    w = synth.normal_f16(np.random.default_rng(14), (16, 1024), scale=0.02)
+    codes, scales = oracle.quantize_int4(w)
+    s64 = np.repeat(scales.astype(np.float64), 128, axis=1)
+    err = np.abs(w.astype(np.float64) - codes * s64)
+    assert np.all(err <= s64 * 0.5 * (1 + 2 ** -10) + 1e-300)
+    am = np.argmax(np.abs(w.astype(np.float64)).reshape(16, 8, 128), axis=2)
+    top = np.abs(codes.reshape(16, 8, 128))[np.arange(16)[:, None], np.arange(8)[None, :], am]
+    assert np.all(top == 7)
+
+
 # ------------------------------------------------ int8 activations (W4A8) ---
 
 def _round_f32(fr: Fraction) -> Fraction:
