@@ -39,6 +39,7 @@ typedef int32_t w4_status;
 #define W4_ESTATE  (-4) /* call out of sequence (position mismatch, no model)  */
 #define W4_ENOSPC  (-5) /* the KV page pool or token history is full           */
 #define W4_EHIP    (-6) /* the HIP runtime reported an error                   */
+#define W4_EFORMAT (-7) /* a weight container failed its checks                */
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *w4_last_error(void);
@@ -394,6 +395,49 @@ int32_t w4_model_launches_per_step(const w4_model *m, uint32_t flags);
 #define W4_KERNEL_O       2
 #define W4_KERNEL_LM_HEAD 3
 w4_status w4_model_kernel_replay(w4_model *m, int32_t kind, int32_t reps, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Weight container: a memory-mappable file of packed tensors ([TS] ".nanoqwen
+ * File Format and Safety Protocols" and [SP] "Data Integrity and
+ * Serialization": a fixed 256-byte header opening with an 8-byte magic
+ * string, checked first so a wrong file is refused, then weights stored in
+ * the kernels' packed layout; here the gfx950 layout, with its own magic
+ * "W4GFX950").  Layout: the 256-byte header (magic, version 1, sizes, tensor
+ * count, table offset 256, file size, FNV-1a 64 checksum of the table, the
+ * model config), a table of 96-byte entries (name up to 47 bytes, kind, row
+ * order, rows, cols, offset, bytes), then each tensor at a 4096-byte aligned
+ * offset.  Host-side only; the mapped bytes are uploaded by the caller.
+ * ------------------------------------------------------------------------ */
+#define W4C_INT4_CODES  0   /* pack_int4_weights codes, rows x cols logical  */
+#define W4C_INT4_SCALES 1   /* pack_int4_weights scales                      */
+#define W4C_F16         2   /* raw fp16 [rows][cols]                         */
+#define W4C_F16_ROWS    3   /* w4_pack_f16_matrix rows                       */
+typedef struct {
+    const char *name;    /* NUL-terminated, at most 47 bytes                  */
+    int32_t kind;        /* W4C_*                                             */
+    int32_t row_order;   /* informational: W4_PERM_* + 1, or 0 for identity   */
+    int64_t rows, cols;
+    const void *data;    /* host bytes (write) / inside the mapping (read)    */
+    size_t bytes;        /* must equal what kind, rows and cols imply         */
+} w4c_tensor;
+typedef struct w4c_file w4c_file;
+
+/* Writes the container (tensors in the given order).  Errors: W4_EINVAL. */
+w4_status w4c_write(const char *path, const w4_model_config *cfg, int32_t n_tensors,
+                    const w4c_tensor *tensors);
+/* Maps a container read-only after checking, in order: size and magic (read
+ * before mapping), version, header and entry sizes, file size, table bounds
+ * and checksum, and every entry (name, kind, byte count for its shape,
+ * 4096-byte alignment, bounds, order).  Errors: W4_EFORMAT (a check failed;
+ * the message names it), W4_EINVAL (cannot open or map). */
+w4_status w4c_open(const char *path, w4c_file **out);
+int32_t w4c_count(const w4c_file *f);
+w4_status w4c_config(const w4c_file *f, w4_model_config *cfg);
+/* Tensor i, or the tensor with this name; data points into the mapping and
+ * stays valid until w4c_close. */
+w4_status w4c_tensor_at(const w4c_file *f, int32_t i, w4c_tensor *t);
+w4_status w4c_find(const w4c_file *f, const char *name, w4c_tensor *t);
+void w4c_close(w4c_file *f);
 
 #ifdef __cplusplus
 }

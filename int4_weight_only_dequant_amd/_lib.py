@@ -52,6 +52,15 @@ _lib = None
 _lock = threading.Lock()
 
 
+class W4cTensor(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("kind", C.c_int32), ("row_order", C.c_int32), ("rows", C.c_int64),
+                ("cols", C.c_int64), ("data", C.c_void_p), ("bytes", C.c_size_t)]
+
+
+W4_EFORMAT = -7
+W4C_INT4_CODES, W4C_INT4_SCALES, W4C_F16, W4C_F16_ROWS = 0, 1, 2, 3
+
+
 def _declare(lib):
     vp, i32, i64, sz, u32, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_uint32, C.c_float
     sig = {
@@ -66,6 +75,13 @@ def _declare(lib):
         "w4_pack_f16_matrix": (i32, [vp, i64, i64, vp]),
         "w4_gemv_ws_bytes": (sz, [i64, i64]),
         "w4a16_gemv": (i32, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
+        "w4c_write": (i32, [C.c_char_p, C.POINTER(ModelConfig), i32, C.POINTER(W4cTensor)]),
+        "w4c_open": (i32, [C.c_char_p, C.POINTER(vp)]),
+        "w4c_count": (i32, [vp]),
+        "w4c_config": (i32, [vp, C.POINTER(ModelConfig)]),
+        "w4c_tensor_at": (i32, [vp, i32, C.POINTER(W4cTensor)]),
+        "w4c_find": (i32, [vp, C.c_char_p, C.POINTER(W4cTensor)]),
+        "w4c_close": (None, [vp]),
         "w4a8_act_bytes": (sz, [i64]),
         "w4a8_quantize_act": (i32, [vp, i64, vp, vp]),
         "w4a8_gemv": (i32, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
@@ -154,6 +170,63 @@ def pack_int4_weights(q: np.ndarray, s: np.ndarray, row_perm: np.ndarray | None 
     check(L.pack_int4_weights(_ptr(q), _ptr(s), n, k, 128, None if perm is None else _ptr(perm),
                               _ptr(pq), _ptr(ps)))
     return pq, ps
+
+
+_KIND_DTYPE = {W4C_INT4_CODES: np.uint8, W4C_INT4_SCALES: np.uint16, W4C_F16: np.uint16, W4C_F16_ROWS: np.uint16}
+
+
+def write_container(path: str, cfg: ModelConfig, tensors) -> None:
+    """Writes a weight container; tensors: (name, kind, row_order, rows, cols, numpy array) in file order."""
+    keep = []
+    arr = (W4cTensor * len(tensors))()
+    for i, (name, kind, order, rows, cols, a) in enumerate(tensors):
+        a = np.ascontiguousarray(a)
+        nm = name.encode()
+        keep += [a, nm]
+        arr[i] = W4cTensor(nm, kind, order, rows, cols, a.ctypes.data, a.nbytes)
+    check(lib().w4c_write(os.fsencode(path), C.byref(cfg), len(tensors), arr))
+
+
+class Container:
+    """A weight container mapped read-only; arrays are views of the mapping,
+    valid until close()."""
+
+    def __init__(self, path: str):
+        h = C.c_void_p()
+        check(lib().w4c_open(os.fsencode(path), C.byref(h)))
+        self._h = h
+
+    def config(self) -> ModelConfig:
+        cfg = ModelConfig()
+        check(lib().w4c_config(self._h, C.byref(cfg)))
+        return cfg
+
+    def names(self):
+        out = []
+        for i in range(lib().w4c_count(self._h)):
+            t = W4cTensor()
+            check(lib().w4c_tensor_at(self._h, i, C.byref(t)))
+            out.append(t.name.decode())
+        return out
+
+    def tensor(self, name: str):
+        """(kind, row_order, rows, cols, numpy view of the bytes)."""
+        t = W4cTensor()
+        check(lib().w4c_find(self._h, name.encode(), C.byref(t)))
+        dt = np.dtype(_KIND_DTYPE[t.kind])
+        buf = (C.c_char * t.bytes).from_address(t.data)
+        return t.kind, t.row_order, t.rows, t.cols, np.frombuffer(buf, dtype=dt)
+
+    def close(self) -> None:
+        if self._h:
+            lib().w4c_close(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def quantize_int4_weights(w: np.ndarray):

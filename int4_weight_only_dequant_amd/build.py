@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libw4a16.so")
 TRACE_LIB = os.path.join(HERE, "libw4a16_trace.so")
 ARCH = os.environ.get("W4_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["w4a16.hip", "pack.cpp"]
+SOURCES = ["w4a16.hip", "pack.cpp", "container.cpp"]
 
 
 def hipcc() -> str:

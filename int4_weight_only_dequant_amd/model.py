@@ -19,51 +19,124 @@ def _to_dev(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
+LAYER_NAMES = ("qkv_q", "qkv_s", "qkv_bias", "o_q", "o_s", "gu_q", "gu_s", "down_q", "down_s", "ln1", "ln2")
+
+
+def _config(dims, max_pages: int) -> L.ModelConfig:
+    return L.ModelConfig(d_model=dims.d_model, d_ff=dims.d_ff, n_layers=dims.n_layers,
+                         n_q_heads=dims.n_q_heads, n_kv_heads=dims.n_kv_heads,
+                         head_dim=dims.head_dim, vocab=dims.vocab, max_pages=max_pages,
+                         eps=dims.eps, theta=dims.theta)
+
+
+def _pack_layer(lw, perm_qkv, perm_gu) -> dict:
+    """One layer's tensors in the layout the library reads (packed projections in
+    the model's row orders, fp16 bias and norm weights)."""
+    pq, ps = L.pack_int4_weights(*lw.qkv, row_perm=perm_qkv)
+    parts = {"qkv_q": pq, "qkv_s": ps, "qkv_bias": lw.bqkv, "ln1": lw.ln1, "ln2": lw.ln2}
+    parts["o_q"], parts["o_s"] = L.pack_int4_weights(*lw.o)
+    gq = np.concatenate([lw.gate[0], lw.up[0]])
+    gs = np.concatenate([lw.gate[1], lw.up[1]])
+    parts["gu_q"], parts["gu_s"] = L.pack_int4_weights(gq, gs, row_perm=perm_gu)
+    parts["down_q"], parts["down_s"] = L.pack_int4_weights(*lw.down)
+    return parts
+
+
+def _layer_shapes(dims) -> dict:
+    """(kind, row order, rows, cols) of each layer tensor (logical shapes)."""
+    qkv = (dims.n_q_heads + 2 * dims.n_kv_heads) * dims.head_dim
+    qd = dims.n_q_heads * dims.head_dim
+    return {"qkv_q": (L.W4C_INT4_CODES, 1 + L.W4_PERM_QKV, qkv, dims.d_model),
+            "qkv_s": (L.W4C_INT4_SCALES, 1 + L.W4_PERM_QKV, qkv, dims.d_model),
+            "qkv_bias": (L.W4C_F16, 0, 1, qkv),
+            "o_q": (L.W4C_INT4_CODES, 0, dims.d_model, qd), "o_s": (L.W4C_INT4_SCALES, 0, dims.d_model, qd),
+            "gu_q": (L.W4C_INT4_CODES, 1 + L.W4_PERM_GATE_UP, 2 * dims.d_ff, dims.d_model),
+            "gu_s": (L.W4C_INT4_SCALES, 1 + L.W4_PERM_GATE_UP, 2 * dims.d_ff, dims.d_model),
+            "down_q": (L.W4C_INT4_CODES, 0, dims.d_model, dims.d_ff),
+            "down_s": (L.W4C_INT4_SCALES, 0, dims.d_model, dims.d_ff),
+            "ln1": (L.W4C_F16, 0, 1, dims.d_model), "ln2": (L.W4C_F16, 0, 1, dims.d_model)}
+
+
+def write_model_container(path: str, dims, layer_fn, glob) -> None:
+    """Packs a model (layer_fn(l) -> LayerWeights, glob -> GlobalWeights) into a
+    weight container at path."""
+    cfg = _config(dims, 0)
+    perm_qkv = L.model_row_perm(L.W4_PERM_QKV, cfg)
+    perm_gu = L.model_row_perm(L.W4_PERM_GATE_UP, cfg)
+    shapes = _layer_shapes(dims)
+    tensors = []
+    for l in range(dims.n_layers):
+        parts = _pack_layer(layer_fn(l), perm_qkv, perm_gu)
+        for n in LAYER_NAMES:
+            kind, order, rows, cols = shapes[n]
+            tensors.append((f"layer{l}.{n}", kind, order, rows, cols, parts[n]))
+    tensors.append(("embed", L.W4C_F16, 0, dims.vocab, dims.d_model, glob.embed))
+    tensors.append(("lnf", L.W4C_F16, 0, 1, dims.d_model, glob.lnf))
+    tensors.append(("lm_head", L.W4C_F16_ROWS, 0, dims.vocab, dims.d_model, L.pack_f16_matrix(glob.lm_head)))
+    L.write_container(path, cfg, tensors)
+
+
+class _Dims:
+    """Model shape read back from a container's config."""
+
+    def __init__(self, cfg: L.ModelConfig):
+        for f, _ in L.ModelConfig._fields_:
+            setattr(self, f, getattr(cfg, f))
+        self.eps = float(np.float32(cfg.eps))
+
+
 class DecodeModel:
     """A Qwen2.5-7B-shaped decoder held in device memory.
 
     dims: a ``synth.ModelDims``; layer_fn(l) returns the layer's LayerWeights
     (codes, scales and fp16 tensors as numpy arrays); glob the GlobalWeights;
     free_list the physical page for each successive logical page.
+    ``DecodeModel.from_container`` builds the same model from a weight
+    container's mapped, already packed tensors.
     """
 
     def __init__(self, dims, layer_fn, glob, free_list: np.ndarray, max_pages: int,
                  device="cuda", progress=None):
-        self.dims = dims
-        self.device = torch.device(device)
-        cfg = L.ModelConfig(d_model=dims.d_model, d_ff=dims.d_ff, n_layers=dims.n_layers,
-                            n_q_heads=dims.n_q_heads, n_kv_heads=dims.n_kv_heads,
-                            head_dim=dims.head_dim, vocab=dims.vocab, max_pages=max_pages,
-                            eps=dims.eps, theta=dims.theta)
-        self.cfg = cfg
-        self.max_pages = max_pages
+        cfg = _config(dims, max_pages)
         perm_qkv = L.model_row_perm(L.W4_PERM_QKV, cfg)
         perm_gu = L.model_row_perm(L.W4_PERM_GATE_UP, cfg)
+        layers = (_pack_layer(layer_fn(l), perm_qkv, perm_gu) for l in range(dims.n_layers))
+        self._build(dims, cfg, layers, glob.embed, glob.lnf, L.pack_f16_matrix(glob.lm_head), free_list,
+                    max_pages, device, progress)
+
+    @classmethod
+    def from_container(cls, path: str, free_list: np.ndarray, max_pages: int, device="cuda", progress=None):
+        c = L.Container(path)
+        try:
+            dims = _Dims(c.config())
+            cfg = _config(dims, max_pages)
+            layers = ({n: c.tensor(f"layer{l}.{n}")[4] for n in LAYER_NAMES} for l in range(dims.n_layers))
+            self = cls.__new__(cls)
+            self._build(dims, cfg, layers, c.tensor("embed")[4], c.tensor("lnf")[4], c.tensor("lm_head")[4],
+                        free_list, max_pages, device, progress)
+        finally:
+            c.close()                    # every tensor has been copied to the device
+        return self
+
+    def _build(self, dims, cfg, layers, embed, lnf, lm_head_packed, free_list, max_pages, device, progress):
+        self.dims = dims
+        self.device = torch.device(device)
+        self.cfg = cfg
+        self.max_pages = max_pages
         keep = []                        # device tensors must outlive the model
-        names = ("qkv_q", "qkv_s", "qkv_bias", "o_q", "o_s", "gu_q", "gu_s", "down_q", "down_s",
-                 "ln1", "ln2")
-        ptrs = {n: [] for n in names}
+        ptrs = {n: [] for n in LAYER_NAMES}
         dev = self.device
-        for l in range(dims.n_layers):
-            lw = layer_fn(l)
-            pq, ps = L.pack_int4_weights(*lw.qkv, row_perm=perm_qkv)
-            parts = {"qkv_q": pq, "qkv_s": ps, "qkv_bias": lw.bqkv, "ln1": lw.ln1, "ln2": lw.ln2}
-            parts["o_q"], parts["o_s"] = L.pack_int4_weights(*lw.o)
-            gq = np.concatenate([lw.gate[0], lw.up[0]])
-            gs = np.concatenate([lw.gate[1], lw.up[1]])
-            parts["gu_q"], parts["gu_s"] = L.pack_int4_weights(gq, gs, row_perm=perm_gu)
-            del gq, gs
-            parts["down_q"], parts["down_s"] = L.pack_int4_weights(*lw.down)
-            del lw
-            for n in names:
+        for l, parts in enumerate(layers):
+            for n in LAYER_NAMES:
                 t = _to_dev(parts[n], dev)
                 keep.append(t)
                 ptrs[n].append(t.data_ptr())
+            del parts
             if progress:
                 progress(l)
-        self.embed = _to_dev(glob.embed, dev)
-        self.lnf = _to_dev(glob.lnf, dev)
-        self.lm_head = _to_dev(L.pack_f16_matrix(glob.lm_head), dev)
+        self.embed = _to_dev(embed, dev)
+        self.lnf = _to_dev(lnf, dev)
+        self.lm_head = _to_dev(lm_head_packed, dev)
         kv_elems = dims.n_layers * max_pages * dims.n_kv_heads * 16 * dims.head_dim
         self.k_cache = torch.zeros(kv_elems, dtype=torch.float16, device=dev)
         self.v_cache = torch.zeros(kv_elems, dtype=torch.float16, device=dev)
@@ -72,9 +145,9 @@ class DecodeModel:
         self.tokens = torch.zeros(16 * max_pages + 1, dtype=torch.int32, device=dev)
         self.logits = torch.zeros(dims.vocab, dtype=torch.float32, device=dev)
         self._keep = keep
-        self._arrays = {n: (C.c_void_p * dims.n_layers)(*ptrs[n]) for n in names}
+        self._arrays = {n: (C.c_void_p * dims.n_layers)(*ptrs[n]) for n in LAYER_NAMES}
         buf = L.ModelBuffers()
-        for n in names:
+        for n in LAYER_NAMES:
             setattr(buf, n, C.cast(self._arrays[n], C.POINTER(C.c_void_p)))
         buf.embed, buf.lnf, buf.lm_head = self.embed.data_ptr(), self.lnf.data_ptr(), self.lm_head.data_ptr()
         buf.k_cache, buf.v_cache = self.k_cache.data_ptr(), self.v_cache.data_ptr()

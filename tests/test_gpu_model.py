@@ -120,6 +120,32 @@ def test_tiny_persistent_matches_multikernel():
     assert np.array_equal(ta, tb)
 
 
+def test_tiny_model_from_container_equals_arrays(tmp_path):
+    """A model loaded from the weight container (mapped, pre-packed tensors)
+    steps bit-identically to the same model packed from arrays."""
+    from int4_weight_only_dequant_amd import model as M
+    dims = synth.TINY
+    layers = [synth.layer_weights(dims, l, cfg=121) for l in range(dims.n_layers)]
+    glob = synth.global_weights(dims, cfg=121)
+    free = synth.page_free_list(4, cfg=121)
+    prompt = synth.prompt_ids(dims, 20, cfg=121)
+    path = str(tmp_path / "tiny.w4c")
+    M.write_model_container(path, dims, lambda l: layers[l], glob)
+    say("case: tiny model from container vs from arrays, 20 prompt + 12 steps")
+    a = w4.DecodeModel(dims, lambda l: layers[l], glob, free, 4)
+    try:
+        la, ta = run_model(a, prompt, 32)
+    finally:
+        a.close()
+    b = w4.DecodeModel.from_container(path, free, 4)
+    try:
+        lb, tb = run_model(b, prompt, 32)
+        assert b.device_error() == 0
+    finally:
+        b.close()
+    assert np.array_equal(la, lb) and np.array_equal(ta, tb)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(1500)
 def test_full_model_512_plus_128():
