@@ -44,6 +44,9 @@ struct AttnProblem {
     uint16_t *out;              // fp16 [n_qh][128]
 };
 
+// At least 4 pages per split: at context 640 (40 pages) 1 page per split
+// measured 19.5 us per call, 2 pages 14.9 us, 4 pages 13.6 us (the
+// last-arriver merge of the splits outweighs the shorter page loop).
 inline int attn_pages_per_split(int n_pages_max) {
     int pps = (n_pages_max + 63) / 64;
     return pps < 4 ? 4 : pps;
