@@ -120,6 +120,31 @@ def test_tiny_persistent_matches_multikernel():
     assert np.array_equal(ta, tb)
 
 
+@pytest.mark.parametrize("n_qh,n_kvh", [(14, 2), (4, 2)])
+def test_gqa_step_with_a_large_pool(n_qh, n_kvh):
+    """GQA 7:1 and 2:1 on a 136-page pool (several attention chunks per head):
+    280 teacher-forced + 20 greedy steps against the oracle."""
+    dims = synth.ModelDims(d_model=512, d_ff=1024, n_layers=2, n_q_heads=n_qh, n_kv_heads=n_kvh,
+                           head_dim=128, vocab=1000)
+    layers = [synth.layer_weights(dims, l, cfg=122) for l in range(dims.n_layers)]
+    glob = synth.global_weights(dims, cfg=122)
+    max_pages = 136
+    free = synth.page_free_list(max_pages, cfg=122)
+    prompt = synth.prompt_ids(dims, 280, cfg=122)
+    say(f"case: GQA {n_qh}/{n_kvh}, 136-page pool, 280 prompt + 20 steps")
+    model = w4.DecodeModel(dims, lambda l: layers[l], glob, free, max_pages)
+    try:
+        lg, tk = run_model(model, prompt, 300)
+        assert model.device_error() == 0
+    finally:
+        model.close()
+    positions = np.arange(279, 300)
+    worst, mism = compare_with_oracle(dims, layers, glob, lg, tk, 280, positions)
+    say(f"  max |logit err| {worst:.3e}; mismatches {mism}")
+    assert worst <= LOGIT_ATOL
+    assert not mism
+
+
 def test_tiny_model_from_container_equals_arrays(tmp_path):
     """A model loaded from the weight container (mapped, pre-packed tensors)
     steps bit-identically to the same model packed from arrays."""
