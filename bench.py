@@ -512,6 +512,81 @@ def phase_trace(write_md: bool = True):
     return summary
 
 
+SA_MD = os.path.join(HERE, "profiles", "standalone_calls_kernel_stats.md")
+
+
+def summarize_standalone_trace(d: str, cmd: str):
+    """Per-call kernel durations of a --kernel-trace run of `bench.py --standalone-only`
+    (the calls run in a fixed order, so dispatches of equal grids are told apart by it)."""
+    trace = glob.glob(os.path.join(d, "**", "run_kernel_trace.csv"), recursive=True)
+    if not trace:
+        sys.exit(f"no rocprofv3 kernel trace under {d}")
+    rows = sorted(csv.DictReader(open(trace[0])), key=lambda r: int(r["Start_Timestamp"]))
+    seq = [(r["Kernel_Name"], r["Grid_Size_X"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+           for r in rows if any(k in r["Kernel_Name"] for k in ("sg_gemv", "attn_decode", "a8_quantize"))]
+    B = {"w4a16_gemv 3584x3584 (config 0)": 6637568, "w4a16_gemv 37888x3584": 70099968,
+         "w4a16_gemv 3584x18944": 35053568, "w4a16_mlp: gate+up with SwiGLU": 70062080,
+         "w4a16_mlp: down": 35053568, "w4a8_gemv 3584x3584": None, "w4a8_gemv 37888x3584": None,
+         "w4a8_gemv 3584x18944": None, "w4a8_quantize_act": None,
+         "paged_attn_decode ctx 640 (config 2)": 1325216, "paged_attn_decode ctx 8192": 16793600}
+    groups = {k: [] for k in B}
+    n16 = 0
+    a8_grids = []
+    for name, grid, t in seq:
+        if "attn_decode" in name:
+            groups["paged_attn_decode ctx 640 (config 2)" if grid == "10240" else "paged_attn_decode ctx 8192"].append(t)
+        elif "a8_quantize" in name:
+            groups["w4a8_quantize_act"].append(t)
+        elif "true" in name:
+            a8_grids.append((grid, t))
+        elif "SwiGLU" in name:
+            groups["w4a16_mlp: gate+up with SwiGLU"].append(t)
+        elif grid == "100352":
+            groups["w4a16_gemv 3584x3584 (config 0)"].append(t)
+        else:
+            n16 += 1
+            k = ("w4a16_gemv 37888x3584" if n16 <= 66 else "w4a16_gemv 3584x18944" if n16 <= 192 else "w4a16_mlp: down")
+            groups[k].append(t)
+    # int8-activation GEMVs in call order: 3584x3584 (grid 392 wgs), then 37888x3584, then 3584x18944
+    n_big = 0
+    for grid, t in a8_grids:
+        if grid == "100352":
+            groups["w4a8_gemv 3584x3584"].append(t)
+        else:
+            n_big += 1
+            groups["w4a8_gemv 37888x3584" if n_big <= 66 else "w4a8_gemv 3584x18944"].append(t)
+    for k, n, kk in (("w4a8_gemv 3584x3584", 3584, 3584), ("w4a8_gemv 37888x3584", 37888, 3584),
+                     ("w4a8_gemv 3584x18944", 3584, 18944)):
+        act = (kk + 255) // 256 * 256 + (kk // 32 + 255) // 256 * 256 + kk // 32   # w4a8_act_bytes(K)
+        B[k] = n * kk // 2 + n * (kk // 128) * 2 + act + n * 2
+    lines = ["# Standalone C-ABI calls: kernel durations (GEMV, MLP, int8-activation GEMV, paged attention)", "",
+             "Command (from the repository root on one MI355X):", "", "```", cmd, "```", "",
+             "`bench.py --standalone-only` calls `w4a16_gemv` on the single-GEMV shape (3584 x 3584) and on the",
+             "two MLP shapes, `w4a16_mlp` (gate+up with the SwiGLU epilogue, then down: two launches of",
+             "`sg_gemv_kernel`), `w4a8_quantize_act` + `w4a8_gemv` on the same three shapes, and",
+             "`paged_attn_decode` at contexts 640 and 8192.  Each call reads its own copy of the weights (or its",
+             "own pages of one large pool): the copies total at least 1 GiB, so no call finds its operands in the",
+             "256 MB Infinity Cache.  The calls are captured into one graph per shape and replayed (2 eager calls",
+             "first, then 1 + 3 replays).  Durations are rocprofv3's kernel begin/end per dispatch; algorithmic",
+             "bytes are int4 codes + fp16 scales + activations in (int8 codes, scales and sums for the int8 path)",
+             "+ fp16 outputs; attention: the K and V pages of the context, q, o and the page table.", "",
+             "| call | dispatches | mean us | median us | min us | algorithmic bytes | GB/s (mean) | fraction of 8 TB/s |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for k, v in groups.items():
+        if not v:
+            continue
+        srt = sorted(v)
+        m = sum(v) / len(v)
+        if B[k]:
+            lines.append(f"| {k} | {len(v)} | {m:.2f} | {srt[len(srt) // 2]:.2f} | {srt[0]:.2f} | {B[k]:,} | "
+                         f"{B[k] / m / 1e3:.0f} | {B[k] / m / 1e3 / HBM_PEAK_GBS:.3f} |")
+        else:
+            lines.append(f"| {k} | {len(v)} | {m:.2f} | {srt[len(srt) // 2]:.2f} | {srt[0]:.2f} | - | - | - |")
+    with open(SA_MD, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------------------------------
 # Standalone calls of configs 0-2 through the C ABI, rotating over distinct copies of the
 # operands (>= 1 GiB in total) so that no call finds its weights or pages in the 256 MB
@@ -702,6 +777,7 @@ def main():
                     help="skip the standalone GEMV / MLP / attention calls of configs 0-2")
     ap.add_argument("--standalone-only", action="store_true",
                     help="run only the standalone calls of configs 0-2 (for kernel profiles)")
+    ap.add_argument("--summarize-standalone-trace", metavar="DIR")
     ap.add_argument("--phase-trace", action="store_true",
                     help="phase timestamps of the persistent kernel (needs the trace build)")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
@@ -725,6 +801,8 @@ def main():
     if args.summarize_prefill_trace:
         return summarize_prefill_trace(args.summarize_prefill_trace, args.trace_command)
 
+    if args.summarize_standalone_trace:
+        return summarize_standalone_trace(args.summarize_standalone_trace, args.trace_command)
     if args.phase_trace:
         phase_trace()
         return None
