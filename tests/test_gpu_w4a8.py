@@ -45,6 +45,8 @@ def _act_inputs():
     x[3 * 128 + 7] = np.float16(6e-8)           # fp16 subnormal
     x[6 * 128:7 * 128] = 0                      # an all-zero group
     x[7 * 128:8 * 128] = np.float16(-2.5)       # a constant group
+    ties = np.array([(k + 0.5) / 128 for k in range(-126, 126, 2)], np.float64)
+    x[4 * 128:5 * 128] = np.resize(np.concatenate([ties, [127 / 128]]), 128).astype(np.float16)   # exact ties
     return [("mixed", x), ("cfg0", synth.gemv_cfg0()[2]),
             ("mlp-h", synth.normal_f16(synth.rng(98, 1000, 40), (18944,)))]
 

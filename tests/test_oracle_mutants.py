@@ -67,6 +67,53 @@ def _attn_variant(gqa_mod=False, no_scale=False, ignore_table=False):
     return f
 
 
+def quantize_int4_absmax_8(w, group=128):
+    w = np.asarray(w, dtype=np.float16)
+    n, k = w.shape
+    wg = w.astype(F64).reshape(n, k // group, group)
+    scales = (np.max(np.abs(wg), axis=2) / 8.0).astype(np.float16)     # /8 instead of /7
+    s64 = scales.astype(F64)[:, :, None]
+    r = np.where(s64 > 0, np.rint(wg / np.where(s64 > 0, s64, 1.0)), 0.0)
+    return np.clip(r, -8, 7).astype(np.int8).reshape(n, k), scales
+
+
+def quantize_int4_round_away(w, group=128):
+    w = np.asarray(w, dtype=np.float16)
+    n, k = w.shape
+    wg = w.astype(F64).reshape(n, k // group, group)
+    scales = (np.max(np.abs(wg), axis=2) / 7.0).astype(np.float16)
+    s64 = scales.astype(F64)[:, :, None]
+    qq = np.where(s64 > 0, wg / np.where(s64 > 0, s64, 1.0), 0.0)
+    r = np.sign(qq) * np.floor(np.abs(qq) + 0.5)                          # ties away from zero
+    return np.clip(r, -8, 7).astype(np.int8).reshape(n, k), scales
+
+
+def quantize_act_per_tensor(x, group=128):
+    x = np.asarray(x, dtype=np.float16).astype(np.float32)
+    sc = np.float32(np.max(np.abs(x)) / np.float32(127.0))                 # one scale for all groups
+    codes = np.clip(np.rint(x / sc), -127, 127).astype(np.int8) if sc > 0 else np.zeros(x.shape, np.int8)
+    return codes, np.full(x.shape[0] // group, sc, np.float32)
+
+
+def quantize_act_round_away(x, group=128):
+    x = np.asarray(x, dtype=np.float16)
+    k = x.shape[0]
+    xg = x.astype(np.float32).reshape(k // group, group)
+    scales = (np.max(np.abs(xg), axis=1) / np.float32(127.0)).astype(np.float32)
+    codes = np.zeros_like(xg, dtype=np.int8)
+    for g in range(k // group):
+        if scales[g] == 0:
+            continue
+        qq = (xg[g] / scales[g]).astype(np.float32)
+        codes[g] = np.clip(np.sign(qq) * np.floor(np.abs(qq) + 0.5), -127, 127).astype(np.int8)
+    return codes.reshape(k), scales
+
+
+def gemv_w4a8_scale_of_first_group(q, s, xq, xs, group=128):
+    xdeq = np.asarray(xq, dtype=F64) * float(xs[0])                        # group scale ignored
+    return ref.deq(q, s, group) @ xdeq
+
+
 MUTANTS = [
     ("deq", deq_wrong_group, [pins.test_deq_group_indexing]),
     ("rope", rope_interleaved, [pins.test_rope_closed_forms]),
@@ -76,6 +123,13 @@ MUTANTS = [
     ("paged_attention", "gqa_mod", [pins.test_attention_gqa_mapping]),
     ("paged_attention", "no_scale", [pins.test_attention_two_token_closed_form]),
     ("paged_attention", "ignore_table", [pins.test_attention_page_table_shuffle_invariance_and_tail]),
+    ("quantize_int4", quantize_int4_absmax_8, [pins.test_quantize_int4_rational_bruteforce,
+                                               pins.test_quantize_int4_bounds]),
+    ("quantize_int4", quantize_int4_round_away, [pins.test_quantize_int4_rational_bruteforce]),
+    ("quantize_act_int8", quantize_act_per_tensor, [pins.test_quantize_act_rational_bruteforce,
+                                                   pins.test_quantize_act_bounds_and_extremes]),
+    ("quantize_act_int8", quantize_act_round_away, [pins.test_quantize_act_rational_bruteforce]),
+    ("gemv_w4a8", gemv_w4a8_scale_of_first_group, [pins.test_gemv_w4a8_rational_and_reduces_to_w4a16]),
 ]
 
 

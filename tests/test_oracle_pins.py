@@ -124,6 +124,9 @@ def test_quantize_int4_rational_bruteforce():
     w[1, 300] = np.float16(65504.0)
     w[2, 0:128] = 0
     w[2, 128:256] = np.float16(6e-8)                     # max/7 rounds to zero in fp16
+    # exact ties: scale 1/16 (max 7/16), elements (k + 1/2) / 16 and their negatives
+    ties = np.array([(k + 0.5) / 16 for k in range(-7, 7)], np.float64)
+    w[2, 256:384] = np.resize(np.concatenate([ties, [7 / 16]]), 128).astype(np.float16)
     codes, scales = oracle.quantize_int4(w)
     assert codes.dtype == np.int8 and scales.dtype == np.float16
     for n in range(3):
@@ -181,7 +184,10 @@ def test_quantize_act_rational_bruteforce():
     r = np.random.default_rng(11)
     x = (r.standard_normal(4 * 128) * np.repeat([1.0, 1e-3, 300.0, 1e-6], 128)).astype(np.float16)
     x[256 + 5] = np.float16(-65504.0)          # the largest magnitude fp16
-    x = np.concatenate([x, np.zeros(128, np.float16)])
+    # exact ties: max 127/128 gives scale 2^-7, elements (k + 1/2) / 128
+    ties = np.array([(k + 0.5) / 128 for k in range(-126, 126, 2)], np.float64)
+    tg = np.resize(np.concatenate([ties, [127 / 128]]), 128).astype(np.float16)
+    x = np.concatenate([x, np.zeros(128, np.float16), tg])
     codes, scales = oracle.quantize_act_int8(x)
     assert codes.dtype == np.int8 and scales.dtype == np.float32
     for g in range(len(x) // 128):
