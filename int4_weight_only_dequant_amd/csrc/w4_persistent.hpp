@@ -67,6 +67,7 @@ constexpr int kPkWaves = W4_PK_WAVES;            // waves per work-group
 constexpr int kPkThreads = 64 * kPkWaves;        // work-group size
 constexpr int kPkWgPerCu = kPkWaves == 4 ? 2 : 1;   // resident work-groups per CU
 constexpr int kMaxRbPerWg = kPkWaves == 4 ? 8 : 12;   // row blocks one work-group's range may touch
+constexpr int kEmbChunks = 8;            // 16-byte chunks per lane of the embedding row (d <= 4096)
 constexpr int kRedBytes = kMaxRbPerWg * kPkWaves * 64 * 8;
 constexpr int kStageBytes = 18432;       // staged fp16 input per work-group
 constexpr unsigned kSpinLimit = 1u << 22;
@@ -1130,12 +1131,29 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     Ring ring;
     prefetch_phase(ring, p, phase_desc(p, 0, par, n_split));
 
-    // embedding (one wave); clears the argmax key
+    // embedding (one wave); clears the argmax key.  Every 16-byte load of the
+    // row is issued before any value is stored (a store between loads would
+    // keep the next load behind it: one memory round trip per element).
     if (w == W - 1) {
-        const int d = p.d;
+        const int n8 = p.d / 8;                      // 16-byte chunks of the row (host: d <= 4096)
         const int tok = p.tokens[pos];
-        const uint16_t *row = p.embed + static_cast<size_t>(tok) * d;
-        for (int i = lane; i < d; i += 64) store_agent(p.x0 + i, f16_to_f32(row[i]));
+        const u32x4 *row = reinterpret_cast<const u32x4 *>(p.embed + static_cast<size_t>(tok) * p.d);
+        u32x4 v[kEmbChunks];
+#pragma unroll
+        for (int u = 0; u < kEmbChunks; ++u)
+            if (lane + 64 * u < n8) v[u] = row[lane + 64 * u];
+#pragma unroll
+        for (int u = 0; u < kEmbChunks; ++u) {
+            const int c = lane + 64 * u;
+            if (c < n8) {
+                const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    store_agent(p.x0 + c * 8 + 2 * e, f16_to_f32(static_cast<uint16_t>(wd[e] & 0xFFFFu)));
+                    store_agent(p.x0 + c * 8 + 2 * e + 1, f16_to_f32(static_cast<uint16_t>(wd[e] >> 16)));
+                }
+            }
+        }
         if (lane == 0) store_agent(&p.st->best, 0ull);
         pk_signal(pk_embed_cnt(p, par));
     }

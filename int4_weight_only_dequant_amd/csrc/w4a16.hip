@@ -768,7 +768,7 @@ static w4_status setup_persistent(w4_model *m) {
                     phase_geometry(rb_lm * nkc, nkc, 32, P, 1, 1, pk.slots_lm, why);
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
     // normalised inputs are staged whole, one element per thread and batch slot
-    W4_CHECK(d <= kStageMax * kPkThreads && d * 2 <= kStageBytes, W4_EINVAL,
+    W4_CHECK(d <= kStageMax * kPkThreads && d * 2 <= kStageBytes && d <= kEmbChunks * 64 * 8, W4_EINVAL,
              "d_model too large for the persistent step");
 
     // step-parity blocks: accumulators of every layer, then counters (per
