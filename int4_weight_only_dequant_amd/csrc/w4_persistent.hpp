@@ -1158,15 +1158,6 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
         pk_signal(pk_embed_cnt(p, par));
     }
 
-    // clear the other parity's accumulators and counters for the next step
-    {
-        u32x4 *z = reinterpret_cast<u32x4 *>(p.par[par ^ 1]);
-        const size_t n16 = p.par_bytes / 16;
-        const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (size_t i = static_cast<size_t>(B) * kPkThreads + threadIdx.x; i < n16;
-             i += static_cast<size_t>(p.P) * kPkThreads)
-            z[i] = zero;
-    }
 
     bool ok = true;
     const int n_ph = 4 * L + 1;
@@ -1226,6 +1217,18 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             if (g.kind != kPhLM && wave == 0) pk_signal(g.done + (B / kGW) * kCS);
             if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, par, n_split));
         }
+    }
+
+    // clear the other parity's accumulators and counters for the next step
+    // (after this work-group's last phase: at the start these 12 MB of stores
+    // sat in front of the first dependency wait's loads)
+    {
+        u32x4 *z = reinterpret_cast<u32x4 *>(p.par[par ^ 1]);
+        const size_t n16 = p.par_bytes / 16;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (size_t i = static_cast<size_t>(B) * kPkThreads + threadIdx.x; i < n16;
+             i += static_cast<size_t>(p.P) * kPkThreads)
+            z[i] = zero;
     }
 }
 
