@@ -171,6 +171,42 @@ def test_tiny_prefill_then_decode(n_prompt, chunks):
     assert list(tk[n_prompt:]) == want
 
 
+@pytest.mark.parametrize("flags", [L.W4_MULTI | L.W4_GRAPH, L.W4_MULTI | L.W4_EAGER, L.W4_EAGER])
+def test_tiny_prefill_then_other_step_variants(flags):
+    """After a prefill call, the kernel-per-op step (graph and eager) and the
+    eager persistent step continue the sequence with the same greedy tokens as
+    the persistent graph, and logits within the two implementations' spread."""
+    dims, layers, glob, free = _tiny(106, 8)
+    n_prompt, n_steps = 40, 24
+    prompt = synth.prompt_ids(dims, n_prompt, cfg=106)
+    say(f"case: tiny model prefill {n_prompt} + {n_steps} steps with flags {flags}")
+    model = w4.DecodeModel(dims, lambda l: layers[l], glob, free, 8)
+    try:
+        lg_ref, tk_ref = _run(model, prompt, [n_prompt], n_steps)
+        model.reset(prompt)
+        model.prefill(n_prompt)
+        out = [model.logits.clone()]
+        for _ in range(n_steps):
+            model.step(flags)
+            out.append(model.logits.clone())
+        torch.cuda.synchronize()
+        assert model.device_error() == 0
+        lg = torch.stack(out).cpu().numpy()
+        tk = model.tokens[: n_prompt + n_steps + 1].cpu().numpy()
+        pt = model.page_table.cpu().numpy()
+    finally:
+        model.close()
+    n_used = (n_prompt + n_steps + 15) // 16
+    assert np.array_equal(pt[:n_used], free[:n_used]) and np.all(pt[n_used:] == -1)
+    assert np.array_equal(tk, tk_ref)
+    diff = float(np.max(np.abs(lg - lg_ref)))
+    say(f"  max |logit diff| vs persistent graph {diff:.3e}")
+    if flags & L.W4_MULTI:
+        assert diff <= 1e-2
+    else:
+        assert diff == 0.0                     # eager launches of the same kernel: bitwise
+
+
 def test_tiny_prefill_errors():
     dims, layers, glob, free = _tiny(105, 4)
     prompt = synth.prompt_ids(dims, 60, cfg=105)
