@@ -25,6 +25,9 @@ Measurement modes (run by hand, results committed under profiles/):
                       then WRITE_SIZE) with --traffic-probe, calibrates both
                       counters on a device-to-device copy of known size, and
                       writes profiles/decode_step_qwen7b_traffic.md
+  --launch-study      eager launches vs graph replay of the persistent and the
+                      kernel-per-op step at the same positions; writes
+                      profiles/decode_step_qwen7b_launch_study.md
   --summarize-trace D writes the kernel statistics of a
                       `rocprofv3 --kernel-trace --stats -d D -o run` run of
                       this file to profiles/decode_step_qwen7b_persistent_kernel_stats.md
@@ -512,6 +515,112 @@ def phase_trace(write_md: bool = True):
     return summary
 
 
+LAUNCH_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_launch_study.md")
+PAGES_EAGER_MS, PAGES_GRAPH_MS = 119.0, 17.0   # the pages' eager and graph ms/token on an H100 (context)
+
+
+def launch_study(args):
+    """Eager launches vs graph replay, for the persistent and the kernel-per-op step.
+
+    Each variant starts from the same state (the 512-token prompt prefilled by
+    one prefill call), runs 8 untimed steps and then times args.steps greedy
+    steps from position 520, so all four see the same positions and contexts.
+    Wall clock with device synchronisation at both ends; the graph variants also
+    get HIP events per step on the launch stream."""
+    import torch
+    import synth
+    from int4_weight_only_dequant_amd import _lib as L
+    dims = synth.QWEN7B
+    n_prompt, n_warm = 512, 8
+    model, _, _ = build_model(dims, n_prompt, n_warm + args.steps)
+    prompt = synth.prompt_ids(dims, n_prompt)
+    stream = torch.cuda.current_stream()
+    variants = (("persistent, graph replay", L.W4_GRAPH), ("persistent, eager launch", L.W4_EAGER),
+                ("kernel-per-op, graph replay", L.W4_MULTI | L.W4_GRAPH),
+                ("kernel-per-op, eager launch", L.W4_MULTI | L.W4_EAGER))
+    rows, toks = [], {}
+    p0 = n_prompt + n_warm
+    for name, flags in variants:
+        # pass 1: steps enqueued back to back; pass 2: the host waits for every
+        # step's token before enqueuing the next (a serving loop that inspects it)
+        res = {}
+        for synced in (False, True):
+            model.reset(prompt)
+            model.prefill(n_prompt)
+            for _ in range(n_warm):
+                model.step(flags)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            enq = 0.0
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                ev[i].record(stream)
+                te = time.perf_counter()
+                model.step(flags)
+                enq += time.perf_counter() - te
+                if synced:
+                    torch.cuda.synchronize()
+            ev[-1].record(stream)
+            torch.cuda.synchronize()
+            res[synced] = ((time.perf_counter() - t0) * 1e3 / args.steps,
+                           ev[0].elapsed_time(ev[-1]) / args.steps, enq * 1e6 / args.steps)
+            assert model.device_error() == 0, f"device error in {name}"
+            if not synced:
+                toks[name] = model.tokens[p0 + 1: p0 + args.steps + 1].cpu().numpy()
+        ms, dev_ms, enq_us = res[False]
+        launches = model.launches_per_step(flags & L.W4_MULTI)
+        rows.append({"variant": name, "launches_per_step": launches, "ms_per_token": round(ms, 4),
+                     "tok_s": round(1e3 / ms, 1), "device_ms_per_token": round(dev_ms, 4),
+                     "host_enqueue_us_per_step": round(enq_us, 1),
+                     "host_enqueue_us_per_step_host_sync": round(res[True][2], 1),
+                     "ms_per_token_host_sync_each_step": round(res[True][0], 4)})
+        log(f"[launch] {name}: {launches} launches, {ms:.3f} ms/token (events {dev_ms:.3f}), host enqueue "
+            f"{enq_us:.1f} us/step; {res[True][0]:.3f} ms/token with a host sync per step (host enqueue "
+            f"{res[True][2]:.1f} us/step)")
+    model.close()
+    ref = toks[variants[0][0]]
+    for r in rows:
+        r["tokens_equal_persistent_graph"] = bool(np.array_equal(toks[r["variant"]], ref))
+    by = {r["variant"]: r for r in rows}
+    ratio_multi = by["kernel-per-op, eager launch"]["ms_per_token"] / by["kernel-per-op, graph replay"]["ms_per_token"]
+    ratio_sync = (by["kernel-per-op, eager launch"]["ms_per_token_host_sync_each_step"] /
+                  by["kernel-per-op, graph replay"]["ms_per_token_host_sync_each_step"])
+    fused = by["kernel-per-op, graph replay"]["ms_per_token"] / by["persistent, graph replay"]["ms_per_token"]
+    summary = {"positions": f"{n_prompt + n_warm}-{n_prompt + n_warm + args.steps - 1}", "variants": rows,
+               "eager_over_graph_kernel_per_op": round(ratio_multi, 2),
+               "eager_over_graph_kernel_per_op_host_sync": round(ratio_sync, 2),
+               "kernel_per_op_graph_over_persistent_graph": round(fused, 2),
+               "pages_eager_over_graph": round(PAGES_EAGER_MS / PAGES_GRAPH_MS, 2)}
+    print(json.dumps({"launch_study": summary}), flush=True)
+    with open(LAUNCH_MD, "w") as fh:
+        fh.write("# Eager launches vs graph replay of the decode step (Qwen2.5-7B shape)\n\n")
+        fh.write("Command (from the repository root on one MI355X):\n\n")
+        fh.write(f"```\npython3 -u bench.py --launch-study --steps {args.steps}\n```\n\n")
+        fh.write("Every variant starts from the same 512-token prompt (one prefill call), runs 8 untimed "
+                 f"greedy steps and times {args.steps} more at positions {summary['positions']}; ms/token is "
+                 "wall clock with device synchronisation at both ends, `events` the HIP events on the "
+                 "launch stream, `host enqueue` the host time inside the decode_step calls (back to back it "
+                 "includes waiting for room in the launch queue while the device is behind).  A second pass "
+                 "over the same positions waits on the host for every step before enqueuing the next, so its "
+                 "enqueue time is the host's own cost per step.  "
+                 "Launches per step exclude the page append of steps that open a KV page.\n\n")
+        fh.write("| variant | launches per step | ms/token | tok/s | events ms/token | host enqueue us/step | "
+                 "ms/token, host sync per step | host enqueue us/step, host sync per step | "
+                 "tokens equal to the persistent graph |\n")
+        fh.write("|---|---:|---:|---:|---:|---:|---:|---:|---|\n")
+        for r in rows:
+            fh.write(f"| {r['variant']} | {r['launches_per_step']} | {r['ms_per_token']} | {r['tok_s']} | "
+                     f"{r['device_ms_per_token']} | {r['host_enqueue_us_per_step']} | "
+                     f"{r['ms_per_token_host_sync_each_step']} | {r['host_enqueue_us_per_step_host_sync']} | "
+                     f"{r['tokens_equal_persistent_graph']} |\n")
+        fh.write(f"\nKernel-per-op step, eager over graph: {summary['eager_over_graph_kernel_per_op']}x "
+                 f"({summary['eager_over_graph_kernel_per_op_host_sync']}x with a host sync per step) "
+                 f"(the pages: {PAGES_EAGER_MS:.0f} vs {PAGES_GRAPH_MS:.0f} ms/token on an H100, "
+                 f"{summary['pages_eager_over_graph']}x).  Kernel-per-op graph over the persistent graph: "
+                 f"{summary['kernel_per_op_graph_over_persistent_graph']}x.\n")
+    return summary
+
+
 SA_MD = os.path.join(HERE, "profiles", "standalone_calls_kernel_stats.md")
 
 
@@ -778,6 +887,8 @@ def main():
     ap.add_argument("--standalone-only", action="store_true",
                     help="run only the standalone calls of configs 0-2 (for kernel profiles)")
     ap.add_argument("--summarize-standalone-trace", metavar="DIR")
+    ap.add_argument("--launch-study", action="store_true",
+                    help="eager vs graph, persistent vs kernel-per-op step (writes a profiles/ summary)")
     ap.add_argument("--phase-trace", action="store_true",
                     help="phase timestamps of the persistent kernel (needs the trace build)")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
@@ -803,6 +914,9 @@ def main():
 
     if args.summarize_standalone_trace:
         return summarize_standalone_trace(args.summarize_standalone_trace, args.trace_command)
+    if args.launch_study:
+        launch_study(args)
+        return None
     if args.phase_trace:
         phase_trace()
         return None
