@@ -763,7 +763,7 @@ def standalone_kernels(attention: bool = True):
         bq, bs = rotated(pq, R), rotated(ps, R)
         x = torch.from_numpy(synth.normal_f16(synth.rng(0, synth.GLOBAL_LAYER, synth.T_X), (k,))).to(dev)
         y = torch.empty(n, dtype=torch.float16, device=dev)
-        ws = torch.empty(max(lib.w4_gemv_ws_bytes(n, k), 256), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(lib.w4_gemv_ws_bytes(n, k), 256), dtype=torch.uint8, device=dev)
 
         def mk(r):
             def c():
@@ -771,6 +771,11 @@ def standalone_kernels(attention: bool = True):
                                        ws.data_ptr(), ws.numel(), cur()))
             return c
         us = _graph_time_us(torch, [mk(r) for r in range(R)])
+        # the replays did the whole call: the last one's output equals a call
+        # on a fresh workspace
+        want = w4.w4a16_gemv(bq[R - 1], bs[R - 1], x, n, k)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"{name}: replayed output differs"
         b = _w4_bytes(n, k)
         out[name] = {"N": n, "K": k, "us_per_call": round(us, 2), "bytes": b,
                      "GBps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -798,7 +803,7 @@ def standalone_kernels(attention: bool = True):
     x = torch.from_numpy(m["x"]).to(dev)
     h = torch.empty(f, dtype=torch.float16, device=dev)
     y = torch.empty(d, dtype=torch.float16, device=dev)
-    ws = torch.empty(max(lib.w4_mlp_ws_bytes(d, f), 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(lib.w4_mlp_ws_bytes(d, f), 256), dtype=torch.uint8, device=dev)
 
     def mk_mlp(r):
         def c():
@@ -806,6 +811,9 @@ def standalone_kernels(attention: bool = True):
                                   x.data_ptr(), h.data_ptr(), y.data_ptr(), d, f, ws.data_ptr(), ws.numel(), cur()))
         return c
     us = _graph_time_us(torch, [mk_mlp(r) for r in range(R)])
+    _, want = w4.w4a16_mlp(bgq[R - 1], bgs[R - 1], bdq[R - 1], bds[R - 1], x, d, f)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), want.view(torch.int16)), "mlp: replayed output differs"
     b = _w4_bytes(2 * f, d) + _w4_bytes(d, f)
     out["mlp_cfg1"] = {"D": d, "F": f, "us_per_call": round(us, 2), "bytes": b,
                        "GBps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -837,6 +845,9 @@ def standalone_kernels(attention: bool = True):
                 L.check(lib.w4a8_quantize_act(xk.data_ptr(), k, act.data_ptr(), cur()))
             return c
         us = _graph_time_us(torch, [mk8(r) for r in range(R)])
+        want = w4.w4a8_gemv(bq[R - 1], bs[R - 1], act, n, k)
+        torch.cuda.synchronize()
+        assert torch.equal(yk.view(torch.int16), want.view(torch.int16)), f"{name}: replayed output differs"
         qus = _graph_time_us(torch, [mkq() for _ in range(64)])
         b = n * k // 2 + n * (k // 128) * 2 + lib.w4a8_act_bytes(k) + n * 2
         out[name] = {"N": n, "K": k, "us_per_call": round(us, 2), "bytes": b,
@@ -857,7 +868,7 @@ def standalone_kernels(attention: bool = True):
         tables = torch.from_numpy(np.stack([table + r * n_pg for r in range(R)]).astype(np.int32)).to(dev)
         qt = torch.from_numpy(q).to(dev)
         o = torch.empty_like(qt)
-        ws = torch.empty(max(lib.w4_attn_ws_bytes(28, 4, n_pg), 256), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(lib.w4_attn_ws_bytes(28, 4, n_pg), 256), dtype=torch.uint8, device=dev)
 
         def mk_att(r):
             def c():
@@ -866,6 +877,9 @@ def standalone_kernels(attention: bool = True):
                                               ws.data_ptr(), ws.numel(), cur()))
             return c
         us = _graph_time_us(torch, [mk_att(r) for r in range(R)])
+        want = w4.paged_attn_decode(qt, kpool, vpool, tables[R - 1], ctx, float(1 / np.sqrt(128)))
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), want.view(torch.int16)), f"attention {ctx}: replayed output differs"
         b = 2 * n_pg * page_bytes + 2 * q.nbytes + n_pg * 4
         out[f"attn_ctx{ctx}"] = {"ctx": ctx, "pages": n_pg, "us_per_call": round(us, 2), "bytes": b,
                                  "GBps": round(b / (us * 1e-6) / 1e9, 1),
