@@ -639,31 +639,44 @@ def summarize_standalone_trace(d: str, cmd: str):
          "w4a8_gemv 3584x18944": None, "w4a8_quantize_act": None,
          "paged_attn_decode ctx 640 (config 2)": 1325216, "paged_attn_decode ctx 8192": 16793600}
     groups = {k: [] for k in B}
+
+    def n_disp(n, k):
+        # dispatches of one shape in standalone_kernels: 2 eager calls, 1 + 3 replays of
+        # R captured calls, and the check call
+        r = max(2, -(-ROTATE_BYTES // (n * k // 2 + n * (k // 128) * 2)))
+        return 2 + 4 * r + 1
+
+    full = str(512 * 256)              # the large shapes run the full 512-work-group grid
+    att_grids = sorted({int(g) for n_, g, _ in seq if "attn_decode" in n_})
+    n_gu, n_dn = n_disp(37888, 3584), n_disp(3584, 18944)
     n16 = 0
     a8_grids = []
     for name, grid, t in seq:
         if "attn_decode" in name:
-            groups["paged_attn_decode ctx 640 (config 2)" if grid == "10240" else "paged_attn_decode ctx 8192"].append(t)
+            # context 640 launches fewer splits than context 8192
+            groups["paged_attn_decode ctx 640 (config 2)" if int(grid) < att_grids[-1]
+                   else "paged_attn_decode ctx 8192"].append(t)
         elif "a8_quantize" in name:
             groups["w4a8_quantize_act"].append(t)
         elif "true" in name:
             a8_grids.append((grid, t))
         elif "SwiGLU" in name:
             groups["w4a16_mlp: gate+up with SwiGLU"].append(t)
-        elif grid == "100352":
+        elif grid != full:
             groups["w4a16_gemv 3584x3584 (config 0)"].append(t)
         else:
             n16 += 1
-            k = ("w4a16_gemv 37888x3584" if n16 <= 66 else "w4a16_gemv 3584x18944" if n16 <= 192 else "w4a16_mlp: down")
+            k = ("w4a16_gemv 37888x3584" if n16 <= n_gu else "w4a16_gemv 3584x18944" if n16 <= n_gu + n_dn
+                 else "w4a16_mlp: down")
             groups[k].append(t)
-    # int8-activation GEMVs in call order: 3584x3584 (grid 392 wgs), then 37888x3584, then 3584x18944
+    # int8-activation GEMVs in call order: 3584x3584 (the smaller grid), then 37888x3584, then 3584x18944
     n_big = 0
     for grid, t in a8_grids:
-        if grid == "100352":
+        if grid != full:
             groups["w4a8_gemv 3584x3584"].append(t)
         else:
             n_big += 1
-            groups["w4a8_gemv 37888x3584" if n_big <= 66 else "w4a8_gemv 3584x18944"].append(t)
+            groups["w4a8_gemv 37888x3584" if n_big <= n_gu else "w4a8_gemv 3584x18944"].append(t)
     for k, n, kk in (("w4a8_gemv 3584x3584", 3584, 3584), ("w4a8_gemv 37888x3584", 37888, 3584),
                      ("w4a8_gemv 3584x18944", 3584, 18944)):
         act = (kk + 255) // 256 * 256 + (kk // 32 + 255) // 256 * 256 + kk // 32   # w4a8_act_bytes(K)
@@ -676,7 +689,8 @@ def summarize_standalone_trace(d: str, cmd: str):
              "`paged_attn_decode` at contexts 640 and 8192.  Each call reads its own copy of the weights (or its",
              "own pages of one large pool): the copies total at least 1 GiB, so no call finds its operands in the",
              "256 MB Infinity Cache.  The calls are captured into one graph per shape and replayed (2 eager calls",
-             "first, then 1 + 3 replays).  Durations are rocprofv3's kernel begin/end per dispatch; algorithmic",
+             "first, then 1 + 3 replays, then one check call).  Durations are rocprofv3's kernel begin/end per",
+             "dispatch; algorithmic",
              "bytes are int4 codes + fp16 scales + activations in (int8 codes, scales and sums for the int8 path)",
              "+ fp16 outputs; attention: the K and V pages of the context, q, o and the page table.", "",
              "| call | dispatches | mean us | median us | min us | algorithmic bytes | GB/s (mean) | fraction of 8 TB/s |",

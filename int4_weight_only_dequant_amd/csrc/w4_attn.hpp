@@ -17,8 +17,8 @@
 // end the 16 slots are merged through LDS, the work-group publishes its
 // partial, and the last work-group of the kv head merges all splits and
 // writes fp16 outputs.  Every barrier is reached by all waves (no barrier in
-// lane- or wave-dependent control flow).  Partials travel through device-scope
-// (sc1) stores and loads; every wave waits for its stores to be acknowledged
+// lane- or wave-dependent control flow).  Partials are written with device-
+// scope (sc1) stores; every wave waits for its stores to be acknowledged
 // before the barrier that precedes the arrival atomic, so the last work-group
 // never reads a partial before it is complete.
 #pragma once
@@ -44,12 +44,23 @@ struct AttnProblem {
     uint16_t *out;              // fp16 [n_qh][128]
 };
 
-// At least 4 pages per split: at context 640 (40 pages) 1 page per split
-// measured 19.5 us per call, 2 pages 14.9 us, 4 pages 13.6 us (the
-// last-arriver merge of the splits outweighs the shorter page loop).
+// Splits per kv head: about kAttnTargetSplits, each at least kAttnMinPps
+// pages (a short split saves page-loop time but adds partials for the
+// last-arriver merge to read).  Measured per call: context 640, at least 1,
+// 2 or 4 pages per split 15.8, 12.4 and 12.6 us; context 8192 (512 pages),
+// 32, 64 or 128 splits 27.9, 27.2 and 37.4 us.
+#ifndef W4_ATTN_TARGET_SPLITS
+#define W4_ATTN_TARGET_SPLITS 64
+#endif
+#ifndef W4_ATTN_MIN_PPS
+#define W4_ATTN_MIN_PPS 2
+#endif
+constexpr int kAttnTargetSplits = W4_ATTN_TARGET_SPLITS;
+constexpr int kAttnMinPps = W4_ATTN_MIN_PPS;
+static_assert(kAttnTargetSplits >= 1 && kAttnTargetSplits <= 256 && kAttnMinPps >= 1, "attention split bounds");
 inline int attn_pages_per_split(int n_pages_max) {
-    int pps = (n_pages_max + 63) / 64;
-    return pps < 4 ? 4 : pps;
+    const int pps = (n_pages_max + kAttnTargetSplits - 1) / kAttnTargetSplits;
+    return pps < kAttnMinPps ? kAttnMinPps : pps;
 }
 inline int attn_n_split(int n_pages_max) {
     const int pps = attn_pages_per_split(n_pages_max);
@@ -189,14 +200,23 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
     // merge all splits of kv head j in split order (deterministic).  The
-    // (max, sum) pairs go through LDS (reusing s_acc); then lane (h, 4 dims)
-    // streams its n_split float4 partials with independent loads.
+    // partials are complete (their stores were acknowledged before the
+    // arrivals) and nothing on this device read them earlier in this launch,
+    // so no L2 holds a stale copy and plain 16-byte loads see them: up to 32
+    // of them in flight per lane, where device-scope 4-byte loads took one
+    // round trip per 8 splits.  The (max, sum) pairs go through LDS (reusing
+    // s_acc, which holds them for n_split <= 1024); lane (h, 4 dims) then
+    // streams its n_split float4 partials.
     float *sml = &s_acc[0][0][0];
     const int n_ml = a.n_split * G;
-    for (int i = t; i < n_ml; i += kThreads) {
-        const size_t pb = static_cast<size_t>(j) * a.n_split * G + i;   // (s, h) flattened
-        sml[2 * i] = load_agent(a.part_ml + pb * 2);
-        sml[2 * i + 1] = load_agent(a.part_ml + pb * 2 + 1);
+    const float2 *mlp = reinterpret_cast<const float2 *>(a.part_ml) + static_cast<size_t>(j) * n_ml;
+    for (int i0 = 0; i0 < n_ml; i0 += 2 * kThreads) {             // (s, h) flattened
+        const int ia = i0 + t, ib = i0 + kThreads + t;                // both loads in flight at once
+        float2 va = make_float2(0.f, 0.f), vb = make_float2(0.f, 0.f);
+        if (ia < n_ml) va = mlp[ia];
+        if (ib < n_ml) vb = mlp[ib];
+        if (ia < n_ml) { sml[2 * ia] = va.x; sml[2 * ia + 1] = va.y; }
+        if (ib < n_ml) { sml[2 * ib] = vb.x; sml[2 * ib + 1] = vb.y; }
     }
     __syncthreads();
     if (t < G * 32) {
@@ -204,19 +224,16 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
         float M = -INFINITY;
         for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, sml[2 * (s * G + h)]);
         float L = 0.f, A0 = 0.f, A1 = 0.f, A2 = 0.f, A3 = 0.f;
-        const float *base = a.part_acc + (static_cast<size_t>(j) * a.n_split * G + h) * 128 + d4;
-        const size_t stride = static_cast<size_t>(G) * 128;
-        for (int s0 = 0; s0 < a.n_split; s0 += 8) {
-            float4 pa[8];
+        const float4 *base =
+            reinterpret_cast<const float4 *>(a.part_acc + (static_cast<size_t>(j) * a.n_split * G + h) * 128 + d4);
+        const size_t stride = static_cast<size_t>(G) * 32;              // float4 per split
+        for (int s0 = 0; s0 < a.n_split; s0 += 32) {
+            float4 pa[32];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (s0 + u < a.n_split) {
-                    const float *pp = base + (s0 + u) * stride;
-                    pa[u] = make_float4(load_agent(pp), load_agent(pp + 1), load_agent(pp + 2), load_agent(pp + 3));
-                }
-            }
+            for (int u = 0; u < 32; ++u)
+                if (s0 + u < a.n_split) pa[u] = base[(s0 + u) * stride];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 32; ++u) {
                 const int s = s0 + u;
                 if (s < a.n_split) {
                     const float ms = sml[2 * (s * G + h)];

@@ -37,8 +37,13 @@ constexpr int kSgMaxRl = 8;          // row blocks one work-group's range may to
 #define W4_SG_WG_TARGET 512
 #endif
 constexpr int kSgWgTarget = W4_SG_WG_TARGET;   // work-groups per launch (2 per CU)
+// At least 8 tiles per work-group: on the 3584 x 3584 GEMV (1568 tiles) a
+// call measured 8.4 us with 4 (392 work-groups), 7.7 with 8, 8.0 with 12 and
+// 8.5 with 16: fewer work-groups share fewer row blocks, so fewer
+// last-arriver reductions, until too few CUs stream.  Larger matrices keep
+// kSgWgTarget work-groups either way.
 #ifndef W4_SG_MIN_TILES
-#define W4_SG_MIN_TILES 4
+#define W4_SG_MIN_TILES 8
 #endif
 constexpr int kSgMinTiles = W4_SG_MIN_TILES;   // tiles per work-group below which P shrinks
 
