@@ -177,6 +177,30 @@ def test_attn_long_context_8193():
     assert_attn(o, ref, "ctx=8193")
 
 
+@pytest.mark.parametrize("n_pages,ctx", [(1, 5), (1, 16), (2, 17), (3, 40), (128, 2041), (512, 8192),
+                                         (2048, 32763)])
+def test_attn_split_geometry(n_pages, ctx):
+    """Pools from 1 to 2048 pages: one split per kv head up to 64 splits of
+    32 pages, so the last-arriver merge runs from one partial to two full
+    rounds of 32; ragged and full last pages."""
+    say(f"case: attention ctx {ctx}, {n_pages}-page pool")
+    q, kp, vp, table = synth.attn_case(ctx, n_pages=n_pages, cfg=107)
+    o = _gpu_attn(q, kp, vp, table, ctx, n_pages_max=n_pages)
+    ref = oracle.paged_attention(q, kp, vp, table, ctx, 1 / math.sqrt(128))
+    say(f"  abs err {assert_attn(o, ref, f'ctx={ctx} pool={n_pages}'):.3e}")
+
+
+def test_attn_long_context_repeat_bit_identical():
+    """64 splits per kv head (two merge rounds): 200 calls give bit-identical outputs."""
+    say("case: attention ctx 8190 x200 repeat, 512-page pool")
+    q, kp, vp, table = synth.attn_case(8190, n_pages=512, cfg=108)
+    dq, dk, dv, dt = _dev(q), _dev(kp), _dev(vp), _dev(table)
+    first = w4.paged_attn_decode(dq, dk, dv, dt, 8190, 1 / math.sqrt(128)).clone()
+    outs = [w4.paged_attn_decode(dq, dk, dv, dt, 8190, 1 / math.sqrt(128)).clone() for _ in range(200)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(first, o) for o in outs)
+
+
 def test_attn_one_token_is_v_row():
     say("case: attention one token")
     q, kp, vp, table = synth.attn_case(640, cfg=98)
