@@ -40,7 +40,7 @@ struct AttnProblem {
     float scale_log2;           // softmax scale * log2(e)
     float *part_ml;             // [n_kvh][n_split][G][2] (max, sum) base-2 domain
     float *part_acc;            // [n_kvh][n_split][G][128]
-    unsigned *counter;          // [n_kvh]
+    unsigned *counter;          // [n_kvh][kAttnCtrStride]: one 128-byte line per kv head
     uint16_t *out;              // fp16 [n_qh][128]
 };
 
@@ -68,6 +68,11 @@ inline int attn_n_split(int n_pages_max) {
 }
 
 constexpr int kAttnChunk = 4;   // pages loaded together (8 x 16 B per lane)
+
+// Arrival counters one 128-byte line apart: atomics on one line serialise
+// (about 18 ns each), so with the kv heads' counters on one line the 4 x 64
+// arrivals of a long context queued behind each other.
+constexpr int kAttnCtrStride = 32;
 
 template <int G>
 __device__ __forceinline__ void attn_load_chunk(const AttnProblem &a, int j, int c0, int p_end, size_t lane_off,
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t < 64) {
-        const bool last = arrive_last(a.counter + j, static_cast<unsigned>(a.n_split));
+        const bool last = arrive_last(a.counter + j * kAttnCtrStride, static_cast<unsigned>(a.n_split));
         if (t == 0) s_last = last ? 1 : 0;
     }
     __syncthreads();

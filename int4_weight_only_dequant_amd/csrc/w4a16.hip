@@ -119,7 +119,7 @@ static size_t gemv_partials(int n_rb, int n_split) {
 constexpr int kAttnMaxKvh = 256;
 
 static size_t attn_ws_bytes(int n_kvh, int G, int n_split) {
-    return align256(static_cast<size_t>(kAttnMaxKvh) * 4) +
+    return align256(static_cast<size_t>(kAttnMaxKvh) * kAttnCtrStride * 4) +
            align256(static_cast<size_t>(n_kvh) * n_split * G * 2 * 4) +
            static_cast<size_t>(n_kvh) * n_split * G * 128 * 4;
 }
@@ -127,7 +127,7 @@ static size_t attn_ws_bytes(int n_kvh, int G, int n_split) {
 static void attn_ws_carve(void *ws, int n_kvh, int G, int n_split, AttnProblem &a) {
     char *b = static_cast<char *>(ws);
     a.counter = reinterpret_cast<unsigned *>(b);
-    b += align256(static_cast<size_t>(kAttnMaxKvh) * 4);
+    b += align256(static_cast<size_t>(kAttnMaxKvh) * kAttnCtrStride * 4);
     a.part_ml = reinterpret_cast<float *>(b);
     b += align256(static_cast<size_t>(n_kvh) * n_split * G * 2 * 4);
     a.part_acc = reinterpret_cast<float *>(b);
