@@ -58,7 +58,7 @@ struct SgProblem {
     int slot_stride;          // partial slots per shared row block
     int key_by_rb;            // shared row blocks keyed by row block (else by first owner)
     double *slots;            // [n_keys][slot_stride][64], zero between calls
-    unsigned *ctr;            // [n_keys] arrival counters, zero between calls
+    unsigned *ctr;            // [n_keys][kSgCtrStride] arrival counters, zero between calls
 };
 
 // A row block shared by several work-groups is keyed by its index or by its
@@ -89,7 +89,13 @@ inline SgGeom sg_geom(int n_rb, int ng) {
     return g;
 }
 
-inline size_t sg_ctr_bytes(const SgGeom &g) { return (static_cast<size_t>(g.n_keys) * 4 + 255) & ~size_t(255); }
+// Each counter on its own 128-byte line: atomics on one line serialise
+// (about 18 ns each), and the shared row blocks of a small matrix all finish
+// at about the same time.
+constexpr int kSgCtrStride = 32;
+inline size_t sg_ctr_bytes(const SgGeom &g) {
+    return (static_cast<size_t>(g.n_keys) * kSgCtrStride * 4 + 255) & ~size_t(255);
+}
 
 // Workspace: counters first, then the slots.
 inline size_t sg_ws_bytes(int n_rb, int ng) {
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi)
         const int key = p.key_by_rb ? rb : first;
         double *base = p.slots + static_cast<size_t>(key) * p.slot_stride * 64 + lane;
         store_agent(base + (B - first) * 64, v);
-        if (!arrive_last(p.ctr + key, static_cast<unsigned>(n_c))) continue;
+        if (!arrive_last(p.ctr + static_cast<size_t>(key) * kSgCtrStride, static_cast<unsigned>(n_c))) continue;
         // all slots in parallel, summed in slot order, then cleared
         double tot = 0.0;
         int k = 0;
