@@ -33,8 +33,12 @@ struct W4Problem {
     int n_rb;             // row blocks
     int n_split;          // work-groups per row block along K
     double *partial;      // [n_split][n_rb * 64] (n_split > 1)
-    unsigned *counter;    // [n_rb], zero between calls
+    unsigned *counter;    // [n_rb][kGemvCtrStride], zero between calls
 };
+
+// One 128-byte line per row block's arrival counter: atomics on one line
+// serialise, and the split-K work-groups of many row blocks arrive together.
+constexpr int kGemvCtrStride = 32;
 
 // 8 weights of one 32-bit word against 4 activation pairs.  Word layout:
 // element 2j in bits [4j, 4j+4), element 2j+1 in bits [16+4j, 16+4j+4),
@@ -128,7 +132,8 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(W4Problem p, Epi epi)
         const size_t n_rows = static_cast<size_t>(p.n_rb) * 64;
         if (wave == 0) {
             store_agent(p.partial + sp * n_rows + row, total);
-            const bool last = arrive_last(p.counter + rb, static_cast<unsigned>(p.n_split));
+            const bool last = arrive_last(p.counter + static_cast<size_t>(rb) * kGemvCtrStride,
+                                          static_cast<unsigned>(p.n_split));
             if (lane == 0) s_flag = last ? 1 : 0;
         }
         __syncthreads();

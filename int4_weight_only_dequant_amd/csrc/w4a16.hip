@@ -100,12 +100,13 @@ static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // partials.  A fixed counter region keeps every GEMV's counters away from any
 // other GEMV's partials.
 static size_t gemv_ws_bytes(int ctr_rb, size_t max_partials) {
-    return align256(static_cast<size_t>(ctr_rb) * 4) + max_partials * 8;
+    return align256(static_cast<size_t>(ctr_rb) * kGemvCtrStride * 4) + max_partials * 8;
 }
 
 static void gemv_ws_carve(void *ws, int ctr_rb, W4Problem &p) {
     p.counter = static_cast<unsigned *>(ws);
-    p.partial = reinterpret_cast<double *>(static_cast<char *>(ws) + align256(static_cast<size_t>(ctr_rb) * 4));
+    p.partial = reinterpret_cast<double *>(static_cast<char *>(ws) +
+                                           align256(static_cast<size_t>(ctr_rb) * kGemvCtrStride * 4));
 }
 
 static size_t gemv_partials(int n_rb, int n_split) {
