@@ -201,6 +201,28 @@ def test_attn_long_context_repeat_bit_identical():
     assert all(torch.equal(first, o) for o in outs)
 
 
+def test_attn_alternating_inputs_on_one_workspace():
+    """The split partials are re-read with plain loads by the last work-group:
+    calls alternating two different queries (and contexts) on one workspace
+    must each reproduce their own first output bit for bit, so no call reads
+    a partial left in a cache by the call before."""
+    say("case: attention alternating inputs x100, 512-page pool")
+    q, kp, vp, table = synth.attn_case(8190, n_pages=512, cfg=109)
+    q2 = synth.attn_case(8190, n_pages=512, cfg=110)[0]
+    dq, dq2, dk, dv, dt = _dev(q), _dev(q2), _dev(kp), _dev(vp), _dev(table)
+    scale = 1 / math.sqrt(128)
+    a0 = w4.paged_attn_decode(dq, dk, dv, dt, 8190, scale).clone()
+    b0 = w4.paged_attn_decode(dq2, dk, dv, dt, 7001, scale).clone()
+    outs = []
+    for _ in range(100):
+        outs.append((w4.paged_attn_decode(dq, dk, dv, dt, 8190, scale).clone(),
+                     w4.paged_attn_decode(dq2, dk, dv, dt, 7001, scale).clone()))
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, a0) and torch.equal(b, b0) for a, b in outs)
+    ref = oracle.paged_attention(q2, kp, vp, table, 7001, scale)
+    assert_attn(b0.cpu().numpy(), ref, "ctx=7001")
+
+
 def test_attn_one_token_is_v_row():
     say("case: attention one token")
     q, kp, vp, table = synth.attn_case(640, cfg=98)
