@@ -205,7 +205,9 @@ w4_status w4c_open(const char *path, w4c_file **out) {
         if (memchr(e.name, 0, sizeof e.name) == nullptr || e.name[0] == 0) return refuse("bad tensor name");
         const size_t want = expected_bytes(e.kind, e.rows, e.cols);
         if (want == 0 || e.bytes != want) return refuse("tensor size does not match its kind and shape");
-        if (e.offset % kAlign || e.offset < end || e.offset + e.bytes > size) return refuse("tensor offset out of order or bounds");
+        // (written so that no sum can wrap past 2^64)
+        if (e.offset % kAlign || e.offset < end || e.offset > size || e.bytes > size - e.offset)
+            return refuse("tensor offset out of order or bounds");
         end = e.offset + e.bytes;
     }
     w4c_file *f = new w4c_file;

@@ -140,8 +140,13 @@ class DecodeModel:
         kv_elems = dims.n_layers * max_pages * dims.n_kv_heads * 16 * dims.head_dim
         self.k_cache = torch.zeros(kv_elems, dtype=torch.float16, device=dev)
         self.v_cache = torch.zeros(kv_elems, dtype=torch.float16, device=dev)
+        fl = np.ascontiguousarray(free_list, dtype=np.int32)
+        # the step writes K/V rows to the pages the free list hands out: an
+        # entry outside the pool would be a write out of bounds
+        if fl.shape != (max_pages,) or not np.array_equal(np.sort(fl), np.arange(max_pages, dtype=np.int32)):
+            raise L.W4Error(L.W4_EINVAL, f"free_list must be a permutation of [0, {max_pages})")
         self.page_table = torch.full((max_pages,), -1, dtype=torch.int32, device=dev)
-        self.free_list = torch.from_numpy(np.ascontiguousarray(free_list, dtype=np.int32)).to(dev)
+        self.free_list = torch.from_numpy(fl).to(dev)
         self.tokens = torch.zeros(16 * max_pages + 1, dtype=torch.int32, device=dev)
         self.logits = torch.zeros(dims.vocab, dtype=torch.float32, device=dev)
         self._keep = keep
@@ -162,6 +167,11 @@ class DecodeModel:
     # ------------------------------------------------------------------
     def reset(self, prompt: np.ndarray, stream=None) -> None:
         prompt = np.ascontiguousarray(prompt, dtype=np.int32)
+        # token ids index the embedding rows; the pool bounds the positions
+        if prompt.ndim != 1 or len(prompt) < 1 or len(prompt) > 16 * self.max_pages:
+            raise L.W4Error(L.W4_EINVAL, f"prompt must hold 1..{16 * self.max_pages} token ids")
+        if prompt.min() < 0 or prompt.max() >= self.dims.vocab:
+            raise L.W4Error(L.W4_EINVAL, f"prompt token ids must lie in [0, {self.dims.vocab})")
         self.tokens.zero_()
         self.tokens[: len(prompt)] = torch.from_numpy(prompt).to(self.device)
         self.page_table.fill_(-1)

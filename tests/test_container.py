@@ -80,6 +80,31 @@ def test_damaged_files_are_refused(container, tmp_path, what, edit):
     assert e.value.status == L.W4_EFORMAT, what
 
 
+def _fnv1a64(b: bytes) -> int:
+    h = 1469598103934665603
+    for c in b:
+        h = ((h ^ c) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def test_wrapped_tensor_offset_is_refused(container, tmp_path):
+    """An entry whose offset + size wraps past 2^64 (table checksum recomputed,
+    so only the bounds check stands in the way) is refused."""
+    def edit(r):
+        n_t = struct.unpack_from("<I", r, 16)[0]
+        last = 256 + 96 * (n_t - 1)
+        nbytes = struct.unpack_from("<Q", r, last + 80)[0]
+        assert nbytes > 4096                               # so the sum really wraps
+        struct.pack_into("<Q", r, last + 72, (1 << 64) - 4096)
+        struct.pack_into("<Q", r, 40, _fnv1a64(bytes(r[256:256 + 96 * n_t])))
+        return r
+    path = _damaged(container[0], tmp_path, edit)
+    with pytest.raises(L.W4Error) as e:
+        L.Container(path)
+    assert e.value.status == L.W4_EFORMAT
+    assert "bounds" in str(e.value)
+
+
 def test_open_and_write_errors(tmp_path):
     with pytest.raises(L.W4Error) as e:
         L.Container(str(tmp_path / "missing.w4c"))

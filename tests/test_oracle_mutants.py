@@ -144,3 +144,136 @@ def test_planted_mistake_is_caught(monkeypatch, i):
     for t in tests:
         with pytest.raises(AssertionError):
             t()
+
+
+# --------------------------------------------------------------------------
+# decoder-block wiring: each mistake is planted in both the sequential layer
+# (layer_step, run by decode_step) and the batched teacher-forced pass, and the
+# closed-form pins of tests/test_oracle_layer_pins.py must catch it.
+# --------------------------------------------------------------------------
+
+import tests.test_oracle_layer_pins as lpins  # noqa: E402
+
+WIRING = ["ln_swap", "bias_after_rope", "mlp_reads_a", "split_qvk", "no_attn_residual",
+          "no_mlp_residual", "attn_before_append"]
+
+
+def _split(dims, y, mut):
+    qd, kd = dims.q_dim, dims.kv_dim
+    lead = y.shape[:-1]
+    q = y[..., :qd]
+    if mut == "split_qvk":
+        v, k = y[..., qd:qd + kd], y[..., qd + kd:]
+    else:
+        k, v = y[..., qd:qd + kd], y[..., qd + kd:]
+    return (q.reshape(*lead, dims.n_q_heads, dims.head_dim), k.reshape(*lead, dims.n_kv_heads, dims.head_dim),
+            v.reshape(*lead, dims.n_kv_heads, dims.head_dim))
+
+
+def _mutant_layer_step(mut):
+    def layer_step(dims, lw, x, pos, cache, layer, trace=None):
+        w1, w2 = (lw.ln2, lw.ln1) if mut == "ln_swap" else (lw.ln1, lw.ln2)
+        a = ref.f16(ref.rmsnorm(x, w1, dims.eps))
+        y = ref.gemv(*lw.qkv, a)
+        b = lw.bqkv.astype(F64)
+        if mut == "bias_after_rope":
+            q, k, v = _split(dims, y, mut)
+            bq, bk, bv = _split(dims, b, mut)
+            q, k, v = ref.rope(q, pos, dims.theta) + bq, ref.rope(k, pos, dims.theta) + bk, v + bv
+        else:
+            q, k, v = _split(dims, y + b, mut)
+            q, k = ref.rope(q, pos, dims.theta), ref.rope(k, pos, dims.theta)
+        q, k, v = ref.f16(q), ref.f16(k), ref.f16(v)
+        if mut == "attn_before_append" and pos > 0:
+            o = ref.paged_attention(q, cache.k[layer], cache.v[layer], cache.page_table, pos,
+                                    1.0 / np.sqrt(dims.head_dim), dims.page)
+            cache.store(layer, pos, k, v)
+        else:
+            cache.store(layer, pos, k, v)
+            o = ref.paged_attention(q, cache.k[layer], cache.v[layer], cache.page_table, pos + 1,
+                                    1.0 / np.sqrt(dims.head_dim), dims.page)
+        o = ref.f16(o).reshape(-1)
+        x = ref.gemv(*lw.o, o) if mut == "no_attn_residual" else x + ref.gemv(*lw.o, o)
+        a2 = ref.f16(ref.rmsnorm(x, w2, dims.eps))
+        mi = a if mut == "mlp_reads_a" else a2
+        h = ref.f16(ref.swiglu(ref.gemv(*lw.gate, mi), ref.gemv(*lw.up, mi)))
+        return ref.gemv(*lw.down, h) if mut == "no_mlp_residual" else x + ref.gemv(*lw.down, h)
+    return layer_step
+
+
+def _mutant_forward(mut):
+    def forward_teacher_forced(dims, layers, glob, tokens, out_positions, progress=None):
+        get = layers if callable(layers) else layers.__getitem__
+        tokens = np.asarray(tokens)
+        T = len(tokens)
+        pos = np.arange(T)
+        X = glob.embed[tokens].astype(F64)
+        scale = 1.0 / np.sqrt(dims.head_dim)
+        for layer in range(dims.n_layers):
+            lw = get(layer)
+            w1, w2 = (lw.ln2, lw.ln1) if mut == "ln_swap" else (lw.ln1, lw.ln2)
+            A = ref.f16(ref.rmsnorm(X, w1, dims.eps))
+            Y = ref.gemv(*lw.qkv, A)
+            b = lw.bqkv.astype(F64)
+            if mut == "bias_after_rope":
+                Q, K, V = _split(dims, Y, mut)
+                bq, bk, bv = _split(dims, b, mut)
+                Q, K, V = ref.rope(Q, pos, dims.theta) + bq, ref.rope(K, pos, dims.theta) + bk, V + bv
+            else:
+                Q, K, V = _split(dims, Y + b, mut)
+                Q, K = ref.rope(Q, pos, dims.theta), ref.rope(K, pos, dims.theta)
+            Q, K, V = ref.f16(Q), ref.f16(K), ref.f16(V)
+            if mut == "attn_before_append":
+                # position p sees 0..p-1 only (position 0 sees itself)
+                grp = dims.n_q_heads // dims.n_kv_heads
+                O = np.empty((T, dims.n_q_heads, dims.head_dim))
+                for p in range(T):
+                    lo = max(p, 1)
+                    for h in range(dims.n_q_heads):
+                        j = h // grp
+                        w = ref.softmax((K[:lo, j].astype(F64) @ Q[p, h].astype(F64)) * scale)
+                        O[p, h] = w @ V[:lo, j].astype(F64)
+            else:
+                O = ref.causal_attention(Q, K, V, scale)
+            O = ref.f16(O).reshape(T, -1)
+            X = ref.gemv(*lw.o, O) if mut == "no_attn_residual" else X + ref.gemv(*lw.o, O)
+            A2 = ref.f16(ref.rmsnorm(X, w2, dims.eps))
+            MI = A if mut == "mlp_reads_a" else A2
+            H = ref.f16(ref.swiglu(ref.gemv(*lw.gate, MI), ref.gemv(*lw.up, MI)))
+            X = ref.gemv(*lw.down, H) if mut == "no_mlp_residual" else X + ref.gemv(*lw.down, H)
+        idx = np.asarray(out_positions)
+        XF = ref.f16(ref.rmsnorm(X[idx], glob.lnf, dims.eps)).astype(F64)
+        return XF @ glob.lm_head.astype(F64).T
+    return forward_teacher_forced
+
+
+LAYER_PINS = [lpins.test_hand_model_single_position_closed_form,
+              lpins.test_hand_model_two_positions_rope_after_bias_closed_form]
+
+
+@pytest.mark.parametrize("mut", WIRING)
+@pytest.mark.parametrize("path", ["layer_step", "forward_teacher_forced"])
+def test_planted_wiring_mistake_is_caught(monkeypatch, mut, path):
+    """Planted in one path at a time: a pin must fail on that path alone."""
+    if path == "layer_step":
+        monkeypatch.setattr(ref, "layer_step", _mutant_layer_step(mut))
+    else:
+        monkeypatch.setattr(ref, "forward_teacher_forced", _mutant_forward(mut))
+        monkeypatch.setattr(oracle, "forward_teacher_forced", ref.forward_teacher_forced)
+    failed = 0
+    for t in LAYER_PINS:
+        try:
+            t()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"wiring mistake {mut} in {path} passed every layer pin"
+
+
+def test_unmutated_copies_pass_the_pins(monkeypatch):
+    """The mutant harness itself is faithful: with no mistake planted, its
+    copies of both paths pass the pins (so a caught mutant is the mistake)."""
+    monkeypatch.setattr(ref, "layer_step", _mutant_layer_step(None))
+    monkeypatch.setattr(ref, "forward_teacher_forced", _mutant_forward(None))
+    monkeypatch.setattr(oracle, "forward_teacher_forced", ref.forward_teacher_forced)
+    for t in LAYER_PINS:
+        t()
