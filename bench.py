@@ -91,49 +91,128 @@ def step_bytes(dims, ctx_lo: int, ctx_hi: int) -> float:
     return L * layer + small + lm + kv_per_tok * mean_ctx + kv_per_tok
 
 
-def cpu_baseline(dims, glob_w, seconds_budget: float = 20.0):
-    """Oracle decode step on a bounded sample: a few decoder layers at a
-    mid-run position plus the final norm and lm_head, extrapolated to 28 layers."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_time(fn, reps: int) -> float:
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_baseline(dims, glob_w, n_prompt: int = 512, pos: int = 576, sample_layers: int = 2):
+    """The float64 numpy oracle on the host cores, on bounded samples of every
+    workload (about 30 s of CPU work in all):
+
+    * configs 0 and 1: oracle.gemv on the 3584 x 3584 GEMV and oracle.mlp on the
+      MLP shapes, ms per call (the oracle dequantises inside each call);
+    * config 2: oracle.paged_attention at context 640 (40 shuffled pages), ms per call;
+    * config 3: the sequential decode step with the weights dequantised to fp64
+      once before timing (the lm_head converted once): `sample_layers` decoder
+      layers timed over 3 steps at position `pos`, extrapolated to every layer,
+      plus the final norm, lm_head and argmax -> ms/token and tok/s (the headline
+      `value`);
+    * config 4: CPU "time to first token": the batched teacher-forced pass over
+      the 512-token prompt, one decoder layer timed (dequantising as the oracle
+      does) and extrapolated to every layer, plus the last row's lm_head.
+    """
     import oracle
+    import oracle.ref as oref
     import synth
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    pos = 576
+    t_all = time.time()
+    res = {}
+    # config 0
+    q, s_, x = synth.gemv_cfg0()
+    res["cfg0_gemv_ms"] = round(_median_time(lambda: oracle.gemv(q, s_, x), 3) * 1e3, 2)
+    # config 1
+    m = synth.mlp_cfg1()
+    res["cfg1_mlp_ms"] = round(_median_time(lambda: oracle.mlp(m["x"], m["gate"], m["up"], m["down"]), 2) * 1e3, 1)
+    del m
+    # config 2
+    qa, kp, vp, table = synth.attn_cfg2()
+    res["cfg2_attention_ms"] = round(_median_time(
+        lambda: oracle.paged_attention(qa, kp, vp, table, 640, 1 / np.sqrt(128)), 3) * 1e3, 2)
+    # config 3: weights dequantised once (fp64) before timing
+    layers = [synth.layer_weights(dims, l) for l in range(sample_layers)]
+    deq_cache = {}
+    orig_deq = oref.deq
+
+    def cached_deq(q_, s2, group=128):
+        key = (id(q_), id(s2))
+        if key not in deq_cache:
+            deq_cache[key] = orig_deq(q_, s2, group)
+        return deq_cache[key]
+
     n_pages = pos // 16 + 1
     rng = np.random.default_rng(7)
     cache = oracle.KVCache(dims, n_pages, np.arange(n_pages, dtype=np.int32))
-    for l in range(dims.n_layers):
-        # filled with seeded values; the oracle's cost does not depend on them
-        cache.k[l] = (rng.standard_normal(cache.k[l].shape, dtype=np.float32)).astype(np.float16)
-        cache.v[l] = cache.k[l]
-    x = glob_w.embed[123].astype(np.float64)
-    t_layers = []
-    t_start = time.time()
-    for l in range(dims.n_layers):
-        lw = synth.layer_weights(dims, l)
-        t0 = time.perf_counter()
-        x = oracle.layer_step(dims, lw, x, pos, cache, l)
-        t_layers.append(time.perf_counter() - t0)
-        if time.time() - t_start > seconds_budget * 0.6 and len(t_layers) >= 2:
-            break
+    kv = rng.standard_normal(cache.k[0].shape, dtype=np.float32).astype(np.float16)
+    for l in range(dims.n_layers):       # seeded filler; the oracle's cost does not depend on it
+        cache.k[l] = kv
+        cache.v[l] = kv
+    lm64 = glob_w.lm_head.astype(np.float64)
+    oref.deq = cached_deq
+    try:
+        x0 = glob_w.embed[123].astype(np.float64)
+        for lw in layers:                # dequantise (untimed)
+            x0 = oracle.layer_step(dims, lw, x0, pos, cache, 0)
+        t_layer = []
+        for _ in range(3):
+            xx = glob_w.embed[123].astype(np.float64)
+            for l, lw in enumerate(layers):
+                t0 = time.perf_counter()
+                xx = oracle.layer_step(dims, lw, xx, pos, cache, l)
+                t_layer.append(time.perf_counter() - t0)
+    finally:
+        oref.deq = orig_deq
+    deq_cache.clear()
+
+    def head():
+        xf = oracle.f16(oracle.rmsnorm(xx, glob_w.lnf, dims.eps))
+        return oracle.argmax_first(lm64 @ xf.astype(np.float64))
+    t_head = _median_time(head, 2)
+    del lm64
+    per_tok = dims.n_layers * float(np.mean(t_layer)) + t_head
+    res["cfg3_ms_per_token"] = round(per_tok * 1e3, 1)
+    # config 4: batched 512-token pass, one layer timed as the oracle runs it
+    prompt = synth.prompt_ids(dims, n_prompt)
+    one = synth.ModelDims(**{**dims.__dict__, "n_layers": 1, "vocab": 1})
+    glob_small = synth.GlobalWeights(embed=glob_w.embed, lnf=glob_w.lnf, lm_head=glob_w.lm_head[:1])
     t0 = time.perf_counter()
-    xf = oracle.f16(oracle.rmsnorm(x, glob_w.lnf, dims.eps))
-    logits = glob_w.lm_head.astype(np.float64) @ xf.astype(np.float64)
-    oracle.argmax_first(logits)
-    t_head = time.perf_counter() - t0
-    per_tok = dims.n_layers * float(np.mean(t_layers)) + t_head
+    oracle.forward_teacher_forced(one, [layers[0]], glob_small, prompt, [n_prompt - 1])
+    t_pass_layer = time.perf_counter() - t0
+    ttft = dims.n_layers * t_pass_layer + t_head
+    res["cfg4_ttft_s"] = round(ttft, 2)
     return {
-        "value": 1.0 / per_tok, "unit": "tok/s", "cores": int(threads),
+        "value": round(1.0 / per_tok, 4), "unit": "tok/s", "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{len(t_layers)} of {dims.n_layers} decoder layers (float64 numpy oracle, "
-                   f"dequantising each matrix per call) at position {pos} plus final norm + lm_head; "
-                   f"per-token time = {dims.n_layers} x mean layer time ({np.mean(t_layers):.2f} s) + "
-                   f"head ({t_head:.2f} s)"),
+        "sample": (f"config 3: {sample_layers} of {dims.n_layers} decoder layers, weights dequantised to fp64 "
+                   f"once before timing, 3 steps at position {pos}, extrapolated to {dims.n_layers} layers "
+                   f"({np.mean(t_layer) * 1e3:.0f} ms per layer) + final norm, fp64 lm_head and argmax "
+                   f"({t_head * 1e3:.0f} ms); config 4: 1 layer of the batched {n_prompt}-token pass "
+                   f"({t_pass_layer:.2f} s, dequantising inside) x {dims.n_layers} + the lm_head"),
+        "ms_per_token": round(per_tok * 1e3, 1),
+        "configs": res,
+        "cpu_model": _cpu_model(),
+        "blas_threads": int(threads),
         "host_cores_visible": len(os.sched_getaffinity(0)),
-        "ms_per_token": per_tok * 1e3,
+        "wall_s": round(time.time() - t_all, 1),
     }
 
 
@@ -994,18 +1073,10 @@ def main():
     ttft_dev_ms = float(np.median([t[1] for t in ttft]))
     log(f"[bench] prefill of {n_prompt} tokens: TTFT {ttft_ms:.2f} ms (device {ttft_dev_ms:.2f} ms), token {prefill_tok}")
 
-    # prompt through the decode step; eager timing on 16 prompt steps; the last W steps are warmup
+    # prompt through the decode step (teacher-forced); the last W steps are the warmup
     model.reset(prompt)
-    eager_lo, eager_n = 400, 16
     for p in range(n_prompt):
-        if p == eager_lo:
-            torch.cuda.synchronize()
-            te = time.perf_counter()
-        flags = L.W4_EAGER if eager_lo <= p < eager_lo + eager_n else L.W4_GRAPH
-        model.step(flags)
-        if p == eager_lo + eager_n - 1:
-            torch.cuda.synchronize()
-            eager_ms = (time.perf_counter() - te) * 1e3 / eager_n
+        model.step(L.W4_GRAPH)
         if p == n_prompt - args.warmup - 1:
             torch.cuda.synchronize()
             log(f"[bench] prompt prefilled through decode steps; warmup {args.warmup} steps")
@@ -1031,6 +1102,20 @@ def main():
     gen = model.tokens[n_prompt: n_prompt + args.steps + 1].cpu().numpy()
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/token, {tok_s:.1f} tok/s; persistent kernel "
         f"{kern_us:.1f} us per launch (events); first tokens {gen[:8]}")
+
+    # eager launches at the positions the graph steps were timed at (the
+    # prompt refilled by one prefill call): the same steps enqueued back to back
+    eager_n = min(16, args.steps)
+    model.reset(prompt)
+    model.prefill(n_prompt)
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    for _ in range(eager_n):
+        model.step(L.W4_EAGER)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - te) * 1e3 / eager_n
+    graph_same_ms = float(step_us[:eager_n].mean()) / 1e3
+    assert model.device_error() == 0, "device error during the eager steps"
 
     # kernel-per-op variant, per-kernel times (timing hook; clobbers the activation scratch)
     kern = {}
@@ -1078,8 +1163,9 @@ def main():
         "vs_baseline": round(tok_s / PAGES_PUBLISHED_TOKS, 3),
         "dtype": "fp16",
         "data": "synthetic (seeded random-init weights of the Qwen2.5-7B shapes, uniform random prompt ids)",
-        "config": {"workload": "Qwen2.5-7B-shaped W4A16 decode step, batch 1, 512-token prompt + 128 greedy "
-                               "graph-captured steps, int4 group-128 projections with fp16 scales",
+        "config": {"workload": f"Qwen2.5-7B-shaped W4A16 decode step, batch 1, {n_prompt}-token prompt + "
+                               f"{args.steps} greedy graph-captured steps, int4 group-128 projections with fp16 "
+                               "scales",
                    "layers": dims.n_layers, "hidden": dims.d_model, "mlp": dims.d_ff,
                    "heads": f"{dims.n_q_heads}q/{dims.n_kv_heads}kv x {dims.head_dim}",
                    "vocab": dims.vocab, "context": f"{ctx_lo}-{ctx_hi}",
@@ -1093,6 +1179,8 @@ def main():
                      "traffic_source": os.path.relpath(TRAFFIC_MD, HERE) if tr else None},
         "vs_baseline_note": f"ratio to the pages' {PAGES_PUBLISHED_TOKS:.0f} tok/s on an H100-class GPU (context)",
         "eager_ms_per_step": round(eager_ms, 3),
+        "eager_vs_graph": {"positions": f"{n_prompt}-{n_prompt + eager_n - 1}", "eager_ms_per_step": round(eager_ms, 3),
+                           "graph_ms_per_step_same_positions": round(graph_same_ms, 3)},
         "launches_per_step": launches,
         "kernel_per_op_variant": {"launches_per_step": multi_launches, **kern},
         "standalone_calls": standalone,

@@ -371,12 +371,69 @@ w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream);
 w4_status w4_model_prefill(w4_model *m, int32_t pos, int32_t n_tokens, void *stream);
 
 /* Synchronises the device and reports the persistent step's error word:
- * 0 = no error; otherwise a dependency wait exceeded its spin limit (the step
- * bailed out and its outputs are invalid). */
+ * 0 = no error; otherwise the step bailed out and its outputs are invalid:
+ * 1000-3999 a dependency wait exceeded its spin limit, 5000 the page-table
+ * entry of the step's position lies outside [0, max_pages), 5001 the step's
+ * token id lies outside [0, vocab) (checked before anything is read through
+ * them). */
 w4_status w4_model_status(w4_model *m, int32_t *device_error);
 
-/* Work-groups of the persistent step (all resident at once). */
+/* Work-groups of the persistent step.  The step's phases hand over through
+ * device-memory counters that every work-group waits on, so all of them must
+ * be resident at once: the grid is sized from the kernel's occupancy for a
+ * device with nothing else running.  decode_step therefore needs the whole
+ * device; a kernel running concurrently on another stream can hold CUs the
+ * step needs, and its waits then end at their spin limit with a device error.
+ * After any device error (w4_model_status non-zero) later steps do nothing
+ * (the error word stays set, outputs are stale, the host-side position keeps
+ * counting) until w4_model_reset. */
 int32_t w4_model_grid(const w4_model *m);
+
+/* ------------------------------------------------------------------------
+ * Inspection of the persistent step, for layer-level parity tests.  The
+ * step keeps its per-layer intermediates in library-owned device memory:
+ *  - acc[par]: int64 accumulators, [n_layers][acc_layer] in fixed point
+ *    (value = acc / 2^fix_bits), rows in packed order: the QKV GEMV (without
+ *    bias) at acc_q in W4_PERM_QKV row order, the O GEMV at acc_o, the gate/up
+ *    GEMV at acc_gu in W4_PERM_GATE_UP order, the down GEMV at acc_d.  A step
+ *    fills the block of parity last_parity and clears the other one.
+ *  - resid: fp32 [2 n_layers + 1][resid_stride]: the embedding row, then per
+ *    layer the residual stream after the O projection and after the down
+ *    projection.
+ *  - att_part: fp32 attention chunk partials, att_layer_floats per layer; per
+ *    query head att_smax chunks of 132 floats: running max of the scores in
+ *    log2 units, sum of exponentials, 2 unused, 128 weighted sums of V.  Chunk
+ *    c covers pages [c, c+1) * att_pages_per_chunk.
+ * Pointers stay valid until w4_model_destroy.  Synchronises the device.
+ * Errors: W4_EINVAL, W4_EHIP. */
+typedef struct {
+    const void *acc[2];
+    int64_t acc_layer;
+    int32_t acc_q, acc_o, acc_gu, acc_d;
+    int32_t fix_bits;
+    int32_t last_parity;
+    const float *resid;
+    int64_t resid_stride;
+    const float *att_part;
+    int64_t att_layer_floats;
+    int32_t att_smax, att_pages_per_chunk;
+    int32_t stage_stride;
+    int32_t reserved;
+} w4_debug_layout;
+w4_status w4_model_debug_layout(w4_model *m, w4_debug_layout *out);
+
+/* Staged-input dump for the same tests: with buf set (device memory, fp16,
+ * w4_model_stage_dump_elems(m) elements, caller-owned), every later
+ * persistent step also writes the fp16 input each GEMV phase read, phase ph
+ * at buf + ph * stage_stride: per layer (ph = 4 l + k) the normalised input of
+ * the QKV GEMV (k = 0, d elements), the attention output entering the O GEMV
+ * (k = 1, n_q_heads * 128), the normalised input of the gate/up GEMV (k = 2,
+ * d) and the SwiGLU output entering the down GEMV (k = 3, d_ff); then the
+ * final normalised state entering the lm_head (ph = 4 n_layers, d).  NULL
+ * turns the dump off (the default).  Synchronises the device.
+ * Errors: W4_EINVAL, W4_EALIGN, W4_EHIP. */
+size_t w4_model_stage_dump_elems(const w4_model *m);
+w4_status w4_model_set_stage_dump(w4_model *m, uint16_t *buf);
 
 /* Number of kernel launches one step of the variant selected by flags
  * (W4_MULTI or not) makes, not counting the page append that steps at a page

@@ -61,6 +61,15 @@ W4_EFORMAT = -7
 W4C_INT4_CODES, W4C_INT4_SCALES, W4C_F16, W4C_F16_ROWS = 0, 1, 2, 3
 
 
+class DebugLayout(C.Structure):
+    """w4_debug_layout: where the persistent step keeps its intermediates."""
+    _fields_ = [("acc", C.c_void_p * 2), ("acc_layer", C.c_int64), ("acc_q", C.c_int32), ("acc_o", C.c_int32),
+                ("acc_gu", C.c_int32), ("acc_d", C.c_int32), ("fix_bits", C.c_int32), ("last_parity", C.c_int32),
+                ("resid", C.c_void_p), ("resid_stride", C.c_int64), ("att_part", C.c_void_p),
+                ("att_layer_floats", C.c_int64), ("att_smax", C.c_int32), ("att_pages_per_chunk", C.c_int32),
+                ("stage_stride", C.c_int32), ("reserved", C.c_int32)]
+
+
 def _declare(lib):
     vp, i32, i64, sz, u32, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_uint32, C.c_float
     sig = {
@@ -103,6 +112,9 @@ def _declare(lib):
         "w4_model_kernel_replay": (i32, [vp, i32, i32, vp]),
         "w4_model_status": (i32, [vp, C.POINTER(i32)]),
         "w4_model_grid": (i32, [vp]),
+        "w4_model_debug_layout": (i32, [vp, C.POINTER(DebugLayout)]),
+        "w4_model_stage_dump_elems": (sz, [vp]),
+        "w4_model_set_stage_dump": (i32, [vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -13,10 +13,11 @@
 // group's 128 activations once through the scalar cache (s_load), so the
 // activation operand of every dot product is an SGPR.  Batch-1 GEMV is a
 // vector-matrix product with one use per weight, so there is no MFMA here:
-// the VALU turns nibbles into fp16 (mask + OR 0x6400 + subtract) and
-// v_dot2c_f32_f16 accumulates.  Within a group the fp32 sums of q*x are
-// exact except when an activation is below 2^-8 in magnitude; across groups
-// the scaled sums are accumulated in fp64.  Work-groups that split one row
+// the VALU turns nibbles into fp16 (mask + OR an exponent + subtract) and
+// v_dot2c_f32_f16 accumulates.  Every product q*x is exact in fp32; a
+// group's sum of 128 of them rounds in fp32 (relative to the magnitude of its
+// terms, about 2^-24 per addition), and across groups the scaled sums are
+// accumulated in fp64.  Work-groups that split one row
 // block along K publish fp64 partials, and the last to arrive sums them in a
 // fixed order and runs the epilogue, so results are deterministic.
 #pragma once
@@ -43,39 +44,77 @@ constexpr int kGemvCtrStride = 32;
 // 8 weights of one 32-bit word against 4 activation pairs.  Word layout:
 // element 2j in bits [4j, 4j+4), element 2j+1 in bits [16+4j, 16+4j+4),
 // stored as u = q + 8.  (w & 0x000F000F) | 0x6400_6400 is the fp16 pair
-// (1024 + u0, 1024 + u1); subtracting 1032 gives (q0, q1) exactly.  The
-// nibbles at bits 4..7 come out as 1024 + 16u, and minus 1152 gives 16q: those
-// products go to the second accumulator, which is scaled by 1/16 (exactly)
-// at the end of the group.
-__device__ __forceinline__ void dot8(uint32_t w, const_u32_ptr xs, float &acc1, float &acc16,
-                                     uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+// (1024 + u0, 1024 + u1): the nibble lands on the mantissa bits of weight 1
+// under exponent 2^10, and subtracting 1032 gives (q0, q1) exactly.  The
+// nibbles at bits 4..7 sit on mantissa bits of weight 16 under 2^10, so they
+// are OR-ed under exponent 2^6 instead ((w & 0x00F000F0) | 0x5400_5400 =
+// 64 + u, minus 72 gives q).  Every product q x is exact in fp32.
+//
+// dot8 / dot8v accumulate the 8 products into an fp32 accumulator with
+// v_dot2c_f32_f16 (13 VALU operations per 8 weights).  That instruction does
+// not round correctly: the low bits of its accumulator operand are cut where
+// the sum is formed (measured on gfx950: 0.7% of random sums off by more than
+// half an ulp, up to about one ulp), so a long chain drifts by about 3 times
+// the error of correctly rounded fp32 sums.
+__device__ __forceinline__ void dot8(uint32_t w, const_u32_ptr xs, float &acc1, float &acc2, uint32_t m_lo,
+                                     uint32_t m_hi, uint32_t magic, uint32_t magic_hi) {
     const h2 k1032 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-    const h2 k1152 = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    const h2 k72 = {static_cast<_Float16>(72.0f), static_cast<_Float16>(72.0f)};
     const uint32_t w8 = w >> 8;
     const h2 q01 = as_h2((w & m_lo) | magic) - k1032;
-    const h2 q23 = as_h2((w & m_hi) | magic) - k1152;
+    const h2 q23 = as_h2((w & m_hi) | magic_hi) - k72;
     const h2 q45 = as_h2((w8 & m_lo) | magic) - k1032;
-    const h2 q67 = as_h2((w8 & m_hi) | magic) - k1152;
+    const h2 q67 = as_h2((w8 & m_hi) | magic_hi) - k72;
     acc1 = __builtin_amdgcn_fdot2(q01, as_h2(xs[0]), acc1, false);
-    acc16 = __builtin_amdgcn_fdot2(q23, as_h2(xs[1]), acc16, false);
+    acc2 = __builtin_amdgcn_fdot2(q23, as_h2(xs[1]), acc2, false);
     acc1 = __builtin_amdgcn_fdot2(q45, as_h2(xs[2]), acc1, false);
-    acc16 = __builtin_amdgcn_fdot2(q67, as_h2(xs[3]), acc16, false);
+    acc2 = __builtin_amdgcn_fdot2(q67, as_h2(xs[3]), acc2, false);
 }
 
 // Same as dot8 with the 4 activation pairs in VGPRs (broadcast LDS reads).
-__device__ __forceinline__ void dot8v(uint32_t w, const uint32_t (&xs)[4], float &acc1, float &acc16,
-                                      uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+__device__ __forceinline__ void dot8v(uint32_t w, const uint32_t (&xs)[4], float &acc1, float &acc2,
+                                      uint32_t m_lo, uint32_t m_hi, uint32_t magic, uint32_t magic_hi) {
     const h2 k1032 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-    const h2 k1152 = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    const h2 k72 = {static_cast<_Float16>(72.0f), static_cast<_Float16>(72.0f)};
     const uint32_t w8 = w >> 8;
     const h2 q01 = as_h2((w & m_lo) | magic) - k1032;
-    const h2 q23 = as_h2((w & m_hi) | magic) - k1152;
+    const h2 q23 = as_h2((w & m_hi) | magic_hi) - k72;
     const h2 q45 = as_h2((w8 & m_lo) | magic) - k1032;
-    const h2 q67 = as_h2((w8 & m_hi) | magic) - k1152;
+    const h2 q67 = as_h2((w8 & m_hi) | magic_hi) - k72;
     acc1 = __builtin_amdgcn_fdot2(q01, as_h2(xs[0]), acc1, false);
-    acc16 = __builtin_amdgcn_fdot2(q23, as_h2(xs[1]), acc16, false);
+    acc2 = __builtin_amdgcn_fdot2(q23, as_h2(xs[1]), acc2, false);
     acc1 = __builtin_amdgcn_fdot2(q45, as_h2(xs[2]), acc1, false);
-    acc16 = __builtin_amdgcn_fdot2(q67, as_h2(xs[3]), acc16, false);
+    acc2 = __builtin_amdgcn_fdot2(q67, as_h2(xs[3]), acc2, false);
+}
+
+// A pair sum a.x b.x + a.y b.y from a zero accumulator: correctly rounded
+// (the same measurement: every sum but 13 in 2^20 random ones).  Written as
+// the three-operand form with an inline zero; through the builtin the compiler
+// folds an addition of two such sums back into a chained accumulation.
+__device__ __forceinline__ float dot2z(h2 a, h2 b) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// The 8 products of dot8v summed without the chained-accumulator error: four
+// correctly rounded pair sums, added with IEEE fp32 adds; callers add these
+// 8-term sums in fp64.  A group's error then stays at the unbiased rounding of
+// 8-term sums.  Used where activations are large (attention output, SwiGLU
+// output of 10^2 and more), so that outputs near zero stay within the GEMV
+// tolerance: 18 VALU operations per 8 weights instead of 13.
+__device__ __forceinline__ float dot8v_exact(uint32_t w, const uint32_t (&xs)[4], uint32_t m_lo, uint32_t m_hi,
+                                             uint32_t magic, uint32_t magic_hi) {
+    const h2 k1032 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const h2 k72 = {static_cast<_Float16>(72.0f), static_cast<_Float16>(72.0f)};
+    const uint32_t w8 = w >> 8;
+    const h2 q01 = as_h2((w & m_lo) | magic) - k1032;
+    const h2 q23 = as_h2((w & m_hi) | magic_hi) - k72;
+    const h2 q45 = as_h2((w8 & m_lo) | magic) - k1032;
+    const h2 q67 = as_h2((w8 & m_hi) | magic_hi) - k72;
+    const float p0 = dot2z(q01, as_h2(xs[0])), p1 = dot2z(q23, as_h2(xs[1]));
+    const float p2 = dot2z(q45, as_h2(xs[2])), p3 = dot2z(q67, as_h2(xs[3]));
+    return (p0 + p1) + (p2 + p3);
 }
 
 // Sum over the work-group's 4 waves of one fp64 value per lane; result valid
@@ -103,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(W4Problem p, Epi epi)
     const u32x4 *wq = p.wq + static_cast<size_t>(rb) * p.n_groups * 4 * 64 + lane;
     const uint16_t *ws = p.ws + static_cast<size_t>(rb) * p.n_groups * 64 + lane;
     const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u),
-                   magic = vreg_const(0x64006400u);
+                   magic = vreg_const(0x64006400u), magic_hi = vreg_const(0x54005400u);
 
     double acc = 0.0;
     for (int g = g_begin + wave; g < g_end; g += 4) {
@@ -112,16 +151,15 @@ __global__ __launch_bounds__(kThreads) void w4_gemv_kernel(W4Problem p, Epi epi)
         for (int c = 0; c < 4; ++c) v[c] = __builtin_nontemporal_load(wq + (g * 4 + c) * 64);
         const uint16_t sbits = ws[g * 64];
         const const_u32_ptr xg = as_const(p.x) + g * 64;
-        float acc1 = 0.f, acc16 = 0.f;
+        float acc1 = 0.f, acc2 = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            dot8(v[c].x, xg + c * 16 + 0, acc1, acc16, m_lo, m_hi, magic);
-            dot8(v[c].y, xg + c * 16 + 4, acc1, acc16, m_lo, m_hi, magic);
-            dot8(v[c].z, xg + c * 16 + 8, acc1, acc16, m_lo, m_hi, magic);
-            dot8(v[c].w, xg + c * 16 + 12, acc1, acc16, m_lo, m_hi, magic);
+            dot8(v[c].x, xg + c * 16 + 0, acc1, acc2, m_lo, m_hi, magic, magic_hi);
+            dot8(v[c].y, xg + c * 16 + 4, acc1, acc2, m_lo, m_hi, magic, magic_hi);
+            dot8(v[c].z, xg + c * 16 + 8, acc1, acc2, m_lo, m_hi, magic, magic_hi);
+            dot8(v[c].w, xg + c * 16 + 12, acc1, acc2, m_lo, m_hi, magic, magic_hi);
         }
-        const float group_sum = __builtin_fmaf(acc16, 0.0625f, acc1);
-        acc += static_cast<double>(group_sum) * static_cast<double>(f16_to_f32(sbits));
+        acc += static_cast<double>(acc1 + acc2) * static_cast<double>(f16_to_f32(sbits));
     }
 
     double total = wg_sum4(acc, red);

@@ -119,16 +119,16 @@ __device__ __forceinline__ void sg_load(u32x4 (&w)[4], uint16_t &s, const SgProb
 
 // One tile's scaled group sum (fp32 inside the group, as in w4_gemv_kernel).
 __device__ __forceinline__ double sg_tile(const u32x4 (&w)[4], uint16_t s, const_u32_ptr xg, uint32_t m_lo,
-                                          uint32_t m_hi, uint32_t magic) {
-    float acc1 = 0.f, acc16 = 0.f;
+                                          uint32_t m_hi, uint32_t magic, uint32_t magic_hi) {
+    float acc1 = 0.f, acc2 = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        dot8(w[c].x, xg + c * 16 + 0, acc1, acc16, m_lo, m_hi, magic);
-        dot8(w[c].y, xg + c * 16 + 4, acc1, acc16, m_lo, m_hi, magic);
-        dot8(w[c].z, xg + c * 16 + 8, acc1, acc16, m_lo, m_hi, magic);
-        dot8(w[c].w, xg + c * 16 + 12, acc1, acc16, m_lo, m_hi, magic);
+        dot8(w[c].x, xg + c * 16 + 0, acc1, acc2, m_lo, m_hi, magic, magic_hi);
+        dot8(w[c].y, xg + c * 16 + 4, acc1, acc2, m_lo, m_hi, magic, magic_hi);
+        dot8(w[c].z, xg + c * 16 + 8, acc1, acc2, m_lo, m_hi, magic, magic_hi);
+        dot8(w[c].w, xg + c * 16 + 12, acc1, acc2, m_lo, m_hi, magic, magic_hi);
     }
-    return static_cast<double>(__builtin_fmaf(acc16, 0.0625f, acc1)) * static_cast<double>(f16_to_f32(s));
+    return static_cast<double>(acc1 + acc2) * static_cast<double>(f16_to_f32(s));
 }
 
 // ---------------------------------------------------------------------------
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi)
     // each thread clears the slots it later writes (rl, its wave, its lane)
     for (int i = threadIdx.x; i < n_rl * 256; i += kThreads) red[i] = 0.0;
 
-    const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u);
+    const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u), magic_hi = vreg_const(0x54005400u);
     const const_u32_ptr xc = as_const(p.x);
     u32x4 wa[4], wb[4];
     uint16_t sa = 0, sb = 0;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi)
             acc += sg_tile_a8(w, s, xc + g * 32, __builtin_bit_cast(float, aux[p.a8_scales / 4 + g]),
                               static_cast<int>(aux[p.a8_sums / 4 + g]));
         } else {
-            acc += sg_tile(w, s, xc + g * 64, m_lo, m_hi, magic);
+            acc += sg_tile(w, s, xc + g * 64, m_lo, m_hi, magic, magic_hi);
         }
     };
     while (t < t_end) {

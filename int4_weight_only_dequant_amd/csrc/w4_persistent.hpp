@@ -122,6 +122,9 @@ struct PKParams {
     int cnt_layer;             // counters per layer: 4 phases x n_grp, then one per head
     unsigned long long *trace; // [P][phases][kTraceSlots] timestamps (trace builds only)
     int wa, wb;                // tile-range weights of the grid's first and second half
+    int max_pages;             // physical pages of the KV pools
+    uint16_t *dbg_stage;       // if set: every GEMV phase's staged fp16 input, [phases][dbg_stride]
+    int dbg_stride;
 };
 
 // Phase timestamps for profiling (built with -DW4_PK_TRACE; off in the
@@ -615,10 +618,13 @@ __device__ __forceinline__ bool pk_reduce(const PKParams &p, int rb, int nk, int
 
 // int4 tile loop of one wave: its tiles rg.b + wave + 4k, consuming the ring
 // (already holding the first tiles) and refilling it; per-row-block sums are
-// parked in red[rl][wave][lane].
+// parked in red[rl][wave][lane].  kExact: the correctly rounded 8-term sums
+// (the O and down projections, whose inputs are large), else the chained
+// fp32 accumulation.
+template <bool kExact>
 __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_t *ws, int ng, Range rg,
                                          bool whole, int rb0, const uint16_t *lds, double *red) {
-    const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u);
+    const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u), magic_hi = vreg_const(0x54005400u);
     const int wave = wave_id(), lane = lane_id();
     const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + kPkWaves - 1) / kPkWaves : 0;
     int cur = -1;
@@ -637,20 +643,38 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
                     cur = rl;
                 }
                 const u32x4 *xl = reinterpret_cast<const u32x4 *>(lds + (whole ? t % ng : i) * 128);
-                float a1 = 0.f, a16 = 0.f;
+                double gs;
+                if constexpr (kExact) {
+                    gs = 0.0;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const u32x4 x0 = xl[c * 4 + 0], x1 = xl[c * 4 + 1], x2 = xl[c * 4 + 2], x3 = xl[c * 4 + 3];
-                    const uint32_t xa[4] = {x0.x, x0.y, x0.z, x0.w};
-                    const uint32_t xb[4] = {x1.x, x1.y, x1.z, x1.w};
-                    const uint32_t xc[4] = {x2.x, x2.y, x2.z, x2.w};
-                    const uint32_t xd[4] = {x3.x, x3.y, x3.z, x3.w};
-                    dot8v(r.w[s][c].x, xa, a1, a16, m_lo, m_hi, magic);
-                    dot8v(r.w[s][c].y, xb, a1, a16, m_lo, m_hi, magic);
-                    dot8v(r.w[s][c].z, xc, a1, a16, m_lo, m_hi, magic);
-                    dot8v(r.w[s][c].w, xd, a1, a16, m_lo, m_hi, magic);
+                    for (int c = 0; c < 4; ++c) {
+                        const u32x4 x0 = xl[c * 4 + 0], x1 = xl[c * 4 + 1], x2 = xl[c * 4 + 2], x3 = xl[c * 4 + 3];
+                        const uint32_t xa[4] = {x0.x, x0.y, x0.z, x0.w};
+                        const uint32_t xb[4] = {x1.x, x1.y, x1.z, x1.w};
+                        const uint32_t xc[4] = {x2.x, x2.y, x2.z, x2.w};
+                        const uint32_t xd[4] = {x3.x, x3.y, x3.z, x3.w};
+                        gs += static_cast<double>(dot8v_exact(r.w[s][c].x, xa, m_lo, m_hi, magic, magic_hi));
+                        gs += static_cast<double>(dot8v_exact(r.w[s][c].y, xb, m_lo, m_hi, magic, magic_hi));
+                        gs += static_cast<double>(dot8v_exact(r.w[s][c].z, xc, m_lo, m_hi, magic, magic_hi));
+                        gs += static_cast<double>(dot8v_exact(r.w[s][c].w, xd, m_lo, m_hi, magic, magic_hi));
+                    }
+                } else {
+                    float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const u32x4 x0 = xl[c * 4 + 0], x1 = xl[c * 4 + 1], x2 = xl[c * 4 + 2], x3 = xl[c * 4 + 3];
+                        const uint32_t xa[4] = {x0.x, x0.y, x0.z, x0.w};
+                        const uint32_t xb[4] = {x1.x, x1.y, x1.z, x1.w};
+                        const uint32_t xc[4] = {x2.x, x2.y, x2.z, x2.w};
+                        const uint32_t xd[4] = {x3.x, x3.y, x3.z, x3.w};
+                        dot8v(r.w[s][c].x, xa, a1, a2, m_lo, m_hi, magic, magic_hi);
+                        dot8v(r.w[s][c].y, xb, a1, a2, m_lo, m_hi, magic, magic_hi);
+                        dot8v(r.w[s][c].z, xc, a1, a2, m_lo, m_hi, magic, magic_hi);
+                        dot8v(r.w[s][c].w, xd, a1, a2, m_lo, m_hi, magic, magic_hi);
+                    }
+                    gs = static_cast<double>(a1 + a2);
                 }
-                acc += static_cast<double>(__builtin_fmaf(a16, 0.0625f, a1)) * static_cast<double>(f16_to_f32(r.s[s]));
+                acc += gs * static_cast<double>(f16_to_f32(r.s[s]));
                 if (k + kRing < n) load_w4_tile(r, s, wq, ws, ng, t + kPkWaves * kRing);
             }
         }
@@ -979,6 +1003,7 @@ __device__ __forceinline__ PhaseDesc phase_desc(const PKParams &p, int ph, int p
         g.nk = d / 32; g.V = 32; g.n_rb = (p.vocab + 63) / 64; g.T = g.n_rb * g.nk;
         g.dep = pk_grp_cnt(p, par, L - 1, kPhD);
         g.x_prev = pk_layer(p, L - 1)->xo; g.acc_in = pk_acc(p, par, L - 1, p.acc_d); g.w = p.lnf;
+        g.x_out = pk_layer(p, L - 1)->xd;
         return g;
     }
     const int l = ph >> 2;
@@ -1038,6 +1063,24 @@ __device__ __forceinline__ void prefetch_phase(Ring &r, const PKParams &p, const
     else prefetch_w4(r, g.wq, g.ws, g.nk, rg);
 }
 
+// Inspection hook (off unless a dump buffer is set): the phase's staged fp16
+// input at its element positions.  A normalised input, or one staged whole,
+// comes from work-group 0; slices staged per tile are written by every
+// work-group that staged them (identical values).
+__device__ __noinline__ void pk_dump_stage(uint16_t *dst, const uint16_t *lds, int n_whole, int rb, int re, int nk,
+                                           int V) {
+    if (n_whole > 0) {
+        if (blockIdx.x != 0) return;
+        for (int i = threadIdx.x; i < n_whole; i += kPkThreads) dst[i] = lds[i];
+        return;
+    }
+    const int n = (re - rb) * V;
+    for (int i = threadIdx.x; i < n; i += kPkThreads) {
+        const int u = i / V, e = i - u * V;
+        dst[((rb + u) % nk) * V + e] = lds[i];
+    }
+}
+
 __device__ __noinline__ void pk_finish_lm(const PKParams &p, const PhaseDesc &g, int rb, double v, int pos,
                                           unsigned epoch) {
     PKFinLogits fin{&p, g.n_rb, pos, epoch, (epoch + 1) * static_cast<unsigned>(n_groups(g.n_rb))};
@@ -1095,6 +1138,20 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     const int par = static_cast<int>(e1 & 1u);
     const int ctx = pos + 1;
     const int phys = p.page_table[pos >> 4];
+    // A failed step leaves its error word set: later steps do nothing until
+    // the model is reset.  A token id or page outside its table would be an
+    // access out of bounds: every work-group sees the same values and leaves.
+    {
+        const int tok0 = p.tokens[pos];
+        int bad = 0;
+        if (load_agent(p.err) != 0) bad = -1;
+        else if (phys < 0 || phys >= p.max_pages) bad = 5000;
+        else if (tok0 < 0 || tok0 >= p.vocab) bad = 5001;
+        if (bad != 0) {
+            if (bad > 0 && B == 0 && threadIdx.x == 0) store_agent(p.err, bad);
+            return;
+        }
+    }
     const int L = p.n_layers;
     const int n_pages = (ctx + kPage - 1) / kPage;
     // attention chunks of kPkWaves x att_pps pages per head at this context
@@ -1203,19 +1260,31 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
                 stage_attn(s_stage, rg, g.nk, p.att_part + g.l * p.att_layer, p.att_smax, n_split);
             __syncthreads();
             PK_STAMP(ph, kTrStaged);
+            if (p.dbg_stage)
+                pk_dump_stage(p.dbg_stage + static_cast<size_t>(ph) * p.dbg_stride, s_stage,
+                              g.stage == kStNorm ? p.d : (whole ? g.nk * g.V : 0), rg.b, rg.e, g.nk, g.V);
             if (g.kind == kPhLM) f16_tiles(ring, p.lm, g.nk, rg, rb0, s_stage, s_red);
-            else w4_tiles(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
+            else if (g.kind == kPhO || g.kind == kPhD)
+                w4_tiles<true>(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
+            else
+                w4_tiles<false>(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
             PK_STAMP(ph, kTrTiles);
             // publish before issuing the next phase's loads: vmcnt is in
             // order, so waiting for the adds would also wait for the prefetch
             phase_reduce(p, g, s_red, rb0, n_rl, pos, epoch);
             PK_STAMP(ph, kTrSignal);
-            if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, par, n_split));
+            if (has_next && !next_after_att) {
+                const PhaseDesc gn = phase_desc(p, ph + 1, par, n_split);
+                prefetch_phase(ring, p, gn);
+            }
         } else {
             if (!ok) break;
             // no tiles here: the work-group still counts as done
             if (g.kind != kPhLM && wave == 0) pk_signal(g.done + (B / kGW) * kCS);
-            if (has_next && !next_after_att) prefetch_phase(ring, p, phase_desc(p, ph + 1, par, n_split));
+            if (has_next && !next_after_att) {
+                const PhaseDesc gn = phase_desc(p, ph + 1, par, n_split);
+                prefetch_phase(ring, p, gn);
+            }
         }
     }
 

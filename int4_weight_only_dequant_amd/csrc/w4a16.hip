@@ -479,6 +479,7 @@ struct w4_model {
     PKLayer *pk_layers;       // device array
     PKParams *pk_dev;         // device copy of pk
     size_t trace_bytes = 0;   // phase-timestamp buffer (trace builds)
+    size_t resid_stride = 0;  // floats between the residual-stream vectors
     int pk_grid;              // resident work-groups
     int n_ctr;
 
@@ -788,11 +789,12 @@ static w4_status setup_persistent(w4_model *m) {
     const size_t part = static_cast<size_t>(rb_lm) * pk.slots_lm * 64 * 8;
     const int n_ctr = 2 + rb_lm + n_groups(rb_lm);
     const size_t ctr_bytes = align256(static_cast<size_t>(n_ctr) * kCS * 4);
-    const size_t per_layer = align256(static_cast<size_t>(d) * 8) * 2;
-    const size_t total = align256(sizeof(PKLayer) * L) + align256(sizeof(PKParams)) +
-                         align256(static_cast<size_t>(d) * 8) + align256(part) +
-                         align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) * L + 256 + per_layer * L +
-                         ctr_bytes + 2 * pk.par_bytes;
+    // residual stream: the embedding row, then per layer after O and after down
+    const size_t rstride = align256(static_cast<size_t>(d) * 4) / 4;
+    const size_t resid_bytes = rstride * 4 * (2 * static_cast<size_t>(L) + 1);
+    const size_t total = align256(sizeof(PKLayer) * L) + align256(sizeof(PKParams)) + align256(resid_bytes) +
+                         align256(part) + align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) * L +
+                         256 + ctr_bytes + 2 * pk.par_bytes;
 #ifdef W4_PK_TRACE
     const size_t trace_bytes = static_cast<size_t>(P) * (4 * L + 1) * kTraceSlots * 8;
     W4_HIP(hipMalloc(&m->pk_arena, total + trace_bytes));
@@ -805,7 +807,8 @@ static w4_status setup_persistent(w4_model *m) {
     char *b = static_cast<char *>(m->pk_arena);
     m->pk_layers = reinterpret_cast<PKLayer *>(b); b += align256(sizeof(PKLayer) * L);
     m->pk_dev = reinterpret_cast<PKParams *>(b); b += align256(sizeof(PKParams));
-    pk.x0 = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(d) * 8);
+    pk.x0 = reinterpret_cast<float *>(b); b += align256(resid_bytes);
+    m->resid_stride = rstride;
     pk.partial = reinterpret_cast<double *>(b); b += align256(part);
     pk.att_layer = align256(static_cast<size_t>(c.n_q_heads) * pk.att_smax * 132 * 4) / 4;
     pk.att_part = reinterpret_cast<float *>(b); b += pk.att_layer * 4 * L;
@@ -820,8 +823,8 @@ static w4_status setup_persistent(w4_model *m) {
         y.dn_q = reinterpret_cast<const u32x4 *>(m->down_q[l]); y.dn_s = m->down_s[l];
         y.ln1 = m->ln1[l]; y.ln2 = m->ln2[l];
         y.kc = m->k_cache + l * kv_layer; y.vc = m->v_cache + l * kv_layer;
-        y.xo = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(d) * 8);
-        y.xd = reinterpret_cast<float *>(b); b += align256(static_cast<size_t>(d) * 8);
+        y.xo = pk.x0 + (2 * static_cast<size_t>(l) + 1) * rstride;
+        y.xd = pk.x0 + (2 * static_cast<size_t>(l) + 2) * rstride;
     }
     // counters and both parity blocks last and contiguous: reset clears them in one sweep
     pk.ctr = reinterpret_cast<unsigned *>(b); b += ctr_bytes;
@@ -835,6 +838,9 @@ static w4_status setup_persistent(w4_model *m) {
     pk.rope = m->rope;
     pk.st = m->state;
     pk.att_scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(double(kHeadDim)));
+    pk.max_pages = c.max_pages;
+    pk.dbg_stage = nullptr;
+    pk.dbg_stride = std::max(std::max(d, f), c.n_q_heads * kHeadDim);
     pk.eps = static_cast<double>(c.eps);
     pk.c_arr_lm = 2;
     pk.c_grp_lm = 2 + rb_lm;
@@ -1122,3 +1128,45 @@ extern "C" w4_status w4_model_status(w4_model *m, int32_t *device_error) {
 }
 
 extern "C" int32_t w4_model_grid(const w4_model *m) { return m ? m->pk_grid : 0; }
+
+// ------------------------------------------------------------ inspection --
+
+extern "C" w4_status w4_model_debug_layout(w4_model *m, w4_debug_layout *out) {
+    clear_error();
+    W4_CHECK(m != nullptr && out != nullptr, W4_EINVAL, "NULL argument");
+    W4_HIP(hipDeviceSynchronize());
+    StepState st;
+    W4_HIP(hipMemcpy(&st, m->state, sizeof st, hipMemcpyDeviceToHost));
+    const PKParams &pk = m->pk;
+    out->acc[0] = pk.par[0];
+    out->acc[1] = pk.par[1];
+    out->acc_layer = static_cast<int64_t>(pk.acc_layer);
+    out->acc_q = pk.acc_q;
+    out->acc_o = pk.acc_o;
+    out->acc_gu = pk.acc_gu;
+    out->acc_d = pk.acc_d;
+    out->fix_bits = 32;
+    out->last_parity = static_cast<int32_t>(st.step & 1u);
+    out->resid = pk.x0;
+    out->resid_stride = static_cast<int64_t>(m->resid_stride);
+    out->att_part = pk.att_part;
+    out->att_layer_floats = static_cast<int64_t>(pk.att_layer);
+    out->att_smax = pk.att_smax;
+    out->att_pages_per_chunk = pk.att_pps * kPkWaves;
+    out->stage_stride = pk.dbg_stride;
+    return W4_OK;
+}
+
+extern "C" size_t w4_model_stage_dump_elems(const w4_model *m) {
+    return m ? static_cast<size_t>(4 * m->cfg.n_layers + 1) * static_cast<size_t>(m->pk.dbg_stride) : 0;
+}
+
+extern "C" w4_status w4_model_set_stage_dump(w4_model *m, uint16_t *buf) {
+    clear_error();
+    W4_CHECK(m != nullptr, W4_EINVAL, "no model");
+    W4_CHECK(buf == nullptr || (reinterpret_cast<uintptr_t>(buf) & 1) == 0, W4_EALIGN, "bad dump buffer");
+    W4_HIP(hipDeviceSynchronize());
+    m->pk.dbg_stage = buf;
+    W4_HIP(hipMemcpy(m->pk_dev, &m->pk, sizeof(PKParams), hipMemcpyHostToDevice));
+    return W4_OK;
+}

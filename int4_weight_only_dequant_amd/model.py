@@ -194,6 +194,23 @@ class DecodeModel:
         L.check(L.lib().w4_model_status(self._m, C.byref(v)))
         return v.value
 
+    def debug_layout(self) -> "L.DebugLayout":
+        """Where the persistent step keeps its per-layer intermediates (synchronises)."""
+        out = L.DebugLayout()
+        L.check(L.lib().w4_model_debug_layout(self._m, C.byref(out)))
+        return out
+
+    def set_stage_dump(self, on: bool) -> None:
+        """Turn the staged-input dump of later persistent steps on or off; the
+        buffer (fp16, [4 n_layers + 1][stage_stride]) is self.stage_dump."""
+        if on:
+            n = L.lib().w4_model_stage_dump_elems(self._m)
+            self.stage_dump = torch.zeros(n, dtype=torch.float16, device=self.device)
+            L.check(L.lib().w4_model_set_stage_dump(self._m, self.stage_dump.data_ptr()))
+        else:
+            L.check(L.lib().w4_model_set_stage_dump(self._m, None))
+            self.stage_dump = None
+
     def grid(self) -> int:
         return L.lib().w4_model_grid(self._m)
 

@@ -1,6 +1,8 @@
 """Decode-step parity: the graph-captured GPU step against the oracle's
 teacher-forced pass, graph == eager bitwise, page-table bookkeeping, and the
 step's error paths."""
+import json
+import os
 import sys
 import time
 
@@ -51,12 +53,22 @@ def compare_with_oracle(dims, layers, glob, logits, toks, n_prompt, positions, c
     err = np.abs(logits[positions] - ref)
     worst = float(err.max())
     mism = []
+    margins = []
     for i, p in enumerate(positions):
         want = oracle.argmax_first(ref[i])
         srt = np.sort(ref[i])
         margin = float(srt[-1] - srt[-2])
+        margins.append(margin)
         if p + 1 >= n_prompt and toks[p + 1] != want:
             mism.append((int(p), int(toks[p + 1]), want, margin))
+    gen = toks[positions + 1]
+    rec = {"positions": f"{int(positions[0])}-{int(positions[-1])}", "max_logit_err": worst,
+           "min_top2_margin": float(min(margins)), "distinct_generated_tokens": int(len(np.unique(gen))),
+           "token_mismatches": len(mism)}
+    say(f"  parity record: {json.dumps(rec)}")
+    if os.environ.get("W4_PARITY_REPORT"):
+        with open(os.environ["W4_PARITY_REPORT"], "a") as fh:
+            fh.write(json.dumps({"case": cache_key or "model", **rec}) + "\n")
     return worst, mism
 
 
