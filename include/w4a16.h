@@ -131,6 +131,23 @@ w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_s,
                      const uint16_t *x, uint16_t *y, int64_t N, int64_t K,
                      void *workspace, size_t ws_bytes, void *stream);
 
+/* w4a16_gemv for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernel and result, bit for bit, with the workspace taken from a fixed
+ * device array inside the library instead of an argument.  The array holds
+ * w4_noalloc_scratch_bytes() bytes (4 MiB) on every GPU the library runs on,
+ * until the process ends; shapes whose w4_gemv_ws_bytes(N, K) exceed it are
+ * refused with W4_EINVAL (the 7B shapes need at most 576 KiB).  The call
+ * allocates nothing (its first call on a device looks up the array's
+ * address).  All calls on one GPU share its array and every call leaves it
+ * zero again: calls that overlap on one GPU (concurrent streams) race and
+ * must be ordered by the caller.  Arguments and errors otherwise as for
+ * w4a16_gemv. */
+size_t w4_noalloc_scratch_bytes(void);
+w4_status w4a16_gemv_noalloc(const uint8_t *packed_q, const uint16_t *packed_s,
+                             const uint16_t *x, uint16_t *y, int64_t N, int64_t K,
+                             void *stream);
+
 /* ------------------------------------------------------------------------
  * W4A8 GEMV: int8 activations (the pages' integer path, "Path A": [TS]
  * "Engineering Challenges" item 3 and [SP] "Three Critical Engineering

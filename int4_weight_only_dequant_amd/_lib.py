@@ -84,6 +84,8 @@ def _declare(lib):
         "w4_pack_f16_matrix": (i32, [vp, i64, i64, vp]),
         "w4_gemv_ws_bytes": (sz, [i64, i64]),
         "w4a16_gemv": (i32, [vp, vp, vp, vp, i64, i64, vp, sz, vp]),
+        "w4_noalloc_scratch_bytes": (sz, []),
+        "w4a16_gemv_noalloc": (i32, [vp, vp, vp, vp, i64, i64, vp]),
         "w4c_write": (i32, [C.c_char_p, C.POINTER(ModelConfig), i32, C.POINTER(W4cTensor)]),
         "w4c_open": (i32, [C.c_char_p, C.POINTER(vp)]),
         "w4c_count": (i32, [vp]),
@@ -318,6 +320,21 @@ def w4a16_gemv(packed_q: torch.Tensor, packed_s: torch.Tensor, x: torch.Tensor, 
     check(L.w4a16_gemv(_ptr(packed_q), _ptr(packed_s), _ptr(x), _ptr(y), n, k, _ptr(ws),
                        ws.numel(), st))
     return y
+
+
+def w4a16_gemv_noalloc(packed_q: torch.Tensor, packed_s: torch.Tensor, x: torch.Tensor, y: torch.Tensor,
+                       n: int, k: int, stream=None) -> None:
+    """w4a16_gemv into a caller-given y, with the library's fixed workspace
+    (the call allocates nothing)."""
+    _dev(packed_q), _dev(packed_s), _dev(x), _dev(y)
+    if x.dtype != torch.float16 or x.numel() != k or y.dtype != torch.float16 or y.numel() < n:
+        raise ValueError("x must be fp16 of length K, y fp16 of length >= N")
+    L = lib()
+    if packed_q.numel() * packed_q.element_size() < L.w4_packed_qbytes(n, k):
+        raise ValueError("packed codes too small for N x K")
+    if packed_s.numel() * packed_s.element_size() < L.w4_packed_sbytes(n, k):
+        raise ValueError("packed scales too small for N x K")
+    check(L.w4a16_gemv_noalloc(_ptr(packed_q), _ptr(packed_s), _ptr(x), _ptr(y), n, k, _stream(stream)))
 
 
 def w4a8_quantize_act(x: torch.Tensor, act: torch.Tensor | None = None, stream=None) -> torch.Tensor:

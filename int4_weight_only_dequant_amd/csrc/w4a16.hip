@@ -9,6 +9,7 @@
 #include <string>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "w4_attn.hpp"
@@ -190,6 +191,61 @@ extern "C" w4_status w4a16_gemv(const uint8_t *packed_q, const uint16_t *packed_
     W4_HIP(launch_sg(packed_q, packed_s, x, N, K, workspace, EpiStoreF16{y, static_cast<int>(N)},
                      static_cast<hipStream_t>(stream)));
     return W4_OK;
+}
+
+// ------------------------------------------- GEMV without allocation --
+//
+// For callers that cannot allocate: the workspace of w4a16_gemv lives in a
+// fixed device array of this library.  In host code `scratch` names a
+// host-side stand-in, not device memory, so its device address is looked up
+// once per device and only that address is handed to kernels.
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use).
+// The array is zero when the code object is loaded, and every w4a16_gemv
+// launch leaves its workspace zero again, so it needs no clearing.
+w4_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    W4_HIP(hipGetDevice(&dev));
+    W4_CHECK(dev >= 0 && dev < kMaxDevices, W4_EINVAL, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        W4_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        W4_CHECK(ptr != nullptr && aligned16(ptr), W4_EHIP, "scratch symbol has no device address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" size_t w4_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" w4_status w4a16_gemv_noalloc(const uint8_t *packed_q, const uint16_t *packed_s, const uint16_t *x,
+                                        uint16_t *y, int64_t N, int64_t K, void *stream) {
+    clear_error();
+    W4_CHECK(N >= 1 && N <= (int64_t(1) << 31) - 64, W4_EINVAL, "bad N=%lld", (long long)N);
+    W4_CHECK(K >= kGroup && K % kGroup == 0 && K <= (int64_t(1) << 24), W4_EINVAL,
+             "K=%lld must be a positive multiple of 128", (long long)K);
+    W4_CHECK(sg_shape_ok(N, K), W4_EINVAL, "N=%lld x K=%lld is too large", (long long)N, (long long)K);
+    const size_t need = w4_gemv_ws_bytes(N, K);
+    W4_CHECK(need > 0 && need <= kNoAllocScratchBytes, W4_EINVAL,
+             "N=%lld x K=%lld needs %zu bytes of workspace, beyond the fixed %zu", (long long)N, (long long)K, need,
+             kNoAllocScratchBytes);
+    void *ws = nullptr;
+    const w4_status st = scratch_for_current_device(&ws);
+    if (st != W4_OK) return st;
+    return w4a16_gemv(packed_q, packed_s, x, y, N, K, ws, kNoAllocScratchBytes, stream);
 }
 
 // ----------------------------------------------------- int8 activations --
