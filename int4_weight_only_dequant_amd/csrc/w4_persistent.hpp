@@ -121,7 +121,7 @@ struct PKParams {
     int n_grp;                 // completion groups of kGW work-groups
     int cnt_layer;             // counters per layer: 4 phases x n_grp, then one per head
     unsigned long long *trace; // [P][phases][kTraceSlots] timestamps (trace builds only)
-    int wa, wb;                // tile-range weights of the grid's first and second half
+    int wa[4], wb[4];          // tile-range weights of the grid's first and second half, per phase kind
     int max_pages;             // physical pages of the KV pools
     uint16_t *dbg_stage;       // if set: every GEMV phase's staged fp16 input, [phases][dbg_stride]
     int dbg_stride;
@@ -156,6 +156,14 @@ enum {
 // Counters sit 128 bytes apart: atomics on one line are serialised at the
 // memory side, so unrelated counters must not share a line.
 constexpr int kCS = 32;
+// Copies of every completion counter (phase groups, heads, embedding): a
+// signal bumps all copies and work-group B polls copy B % kCRep, so each
+// line has 64 pollers (the work-groups of one XCD) instead of 512.  Measured:
+// 1572 -> 1554 us per step with 8 copies.
+#ifndef W4_PK_CREP
+#define W4_PK_CREP 8
+#endif
+constexpr int kCRep = W4_PK_CREP;
 constexpr int kGrp = 8;         // lm_head row blocks per completion group
 
 // done counter of the lm_head
@@ -181,7 +189,7 @@ __device__ __forceinline__ long long *pk_acc(const PKParams &p, int par, int l, 
 // completion counters of (layer, phase kind), one per group; per-head
 // attention counters; the embedding counter
 __device__ __forceinline__ unsigned *pk_cnt(const PKParams &p, int par, int idx) {
-    return reinterpret_cast<unsigned *>(p.par[par] + p.cnt_off) + static_cast<size_t>(idx) * kCS;
+    return reinterpret_cast<unsigned *>(p.par[par] + p.cnt_off) + static_cast<size_t>(idx) * kCS * kCRep;
 }
 __device__ __forceinline__ unsigned *pk_grp_cnt(const PKParams &p, int par, int l, int kind) {
     return pk_cnt(p, par, l * p.cnt_layer + kind * p.n_grp);
@@ -220,11 +228,17 @@ struct Part {
 };
 // Measured on the 7B step (ms per step): 1:1 1.591, 53:47 1.563, 56:44
 // 1.551, 59:41 1.537, 62:38 1.510, 66:34 1.506, 70:30 1.522, 75:25 1.595.
-#ifndef W4_PK_WA
-#define W4_PK_WA 2
-#define W4_PK_WB 1
+#ifndef W4_PK_W_GU
+#define W4_PK_W_GU 2, 1
 #endif
-constexpr int kPkWeightFirst = W4_PK_WA, kPkWeightSecond = W4_PK_WB;
+#ifndef W4_PK_W_D
+#define W4_PK_W_D 2, 1
+#endif
+// weights (first half, second half) per phase kind: QKV, O, gate+up, down
+// (QKV and O have fewer than 4 tiles per work-group and use equal ranges).
+// Measured with the exact O/down arithmetic (us per step): gate+up 2:1 and
+// down 2:1 1572, 5:2 and 3:2 1581, 5:2 and 1:1 1600, 3:1 and 1:1 1628.
+constexpr int kPkWeights[4][2] = {{1, 1}, {1, 1}, {W4_PK_W_GU}, {W4_PK_W_D}};
 __host__ __device__ inline Part make_part(int T, int P, int wa, int wb) {
     return T < 4 * P ? Part{T, P, 1, 1} : Part{T, P, wa, wb};
 }
@@ -271,7 +285,8 @@ __device__ __noinline__ bool pk_wait_cnt(const PKParams &p, const unsigned *base
         bool done = true;
         for (int u = lane; u < n; u += 64) {
             const unsigned target = want ? want : static_cast<unsigned>(min(kGW, p.P - u * kGW));
-            done = done && load_agent(base + static_cast<size_t>((b + u) % nk) * kCS) >= target;
+            done = done && load_agent(base + (static_cast<size_t>((b + u) % nk) * kCRep +
+                                               static_cast<size_t>(blockIdx.x % kCRep)) * kCS) >= target;
         }
         if (__all(done)) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -311,6 +326,13 @@ __device__ __forceinline__ unsigned pk_signal(unsigned *ctr) {
     unsigned old = 0;
     if (lane_id() == 0) old = atomicAdd(ctr, 1u);
     return __builtin_amdgcn_readfirstlane(old);
+}
+
+// Signal on a replicated completion counter: all its copies.
+__device__ __forceinline__ void pk_signal_rep(unsigned *ctr) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane_id() < kCRep) atomicAdd(ctr + lane_id() * kCS, 1u);
 }
 
 // A finished lm_head row block bumps its group's counter; the last unit of a
@@ -964,7 +986,7 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
             store_agent(part, M);
             store_agent(part + 1, Ls);
         }
-        pk_signal(head_cnt + h * kCS);
+        pk_signal_rep(head_cnt + h * kCS * kCRep);
     }
     return true;
 }
@@ -1054,7 +1076,7 @@ __device__ __forceinline__ PhaseDesc phase_desc(const PKParams &p, int ph, int p
 // (measured: with the 2:1 weights the first half's lm_head tiles took 167 us
 // against 99 us for the second half).
 __device__ __forceinline__ Part phase_part(const PKParams &p, const PhaseDesc &g) {
-    return g.kind == kPhLM ? make_part(g.T, p.P, 1, 1) : make_part(g.T, p.P, p.wa, p.wb);
+    return g.kind == kPhLM ? make_part(g.T, p.P, 1, 1) : make_part(g.T, p.P, p.wa[g.kind], p.wb[g.kind]);
 }
 
 __device__ __forceinline__ void prefetch_phase(Ring &r, const PKParams &p, const PhaseDesc &g) {
@@ -1112,7 +1134,7 @@ __device__ __forceinline__ void phase_reduce(const PKParams &p, const PhaseDesc 
     if (g.kind != kPhLM) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (wave == 0) pk_signal(g.done + (blockIdx.x / kGW) * kCS);
+        if (wave == 0) pk_signal_rep(g.done + (blockIdx.x / kGW) * kCS * kCRep);
     }
     // no trailing barrier: the next phase's LDS writes come after its own
     // work-group-wide barrier
@@ -1212,7 +1234,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             }
         }
         if (lane == 0) store_agent(&p.st->best, 0ull);
-        pk_signal(pk_embed_cnt(p, par));
+        pk_signal_rep(pk_embed_cnt(p, par));
     }
 
 
@@ -1280,7 +1302,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
         } else {
             if (!ok) break;
             // no tiles here: the work-group still counts as done
-            if (g.kind != kPhLM && wave == 0) pk_signal(g.done + (B / kGW) * kCS);
+            if (g.kind != kPhLM && wave == 0) pk_signal_rep(g.done + (B / kGW) * kCS * kCRep);
             if (has_next && !next_after_att) {
                 const PhaseDesc gn = phase_desc(p, ph + 1, par, n_split);
                 prefetch_phase(ring, p, gn);

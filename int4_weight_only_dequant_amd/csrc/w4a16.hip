@@ -817,12 +817,14 @@ static w4_status setup_persistent(w4_model *m) {
     W4_CHECK(c.n_q_heads * pk.att_smax <= P, W4_EINVAL, "too many attention chunks for the grid");
     // two work-groups per CU: the first-dispatched half of the grid gets the
     // larger share of every phase (measured: it gets through a phase faster)
-    pk.wa = P == 2 * n_cu ? kPkWeightFirst : 1;
-    pk.wb = P == 2 * n_cu ? kPkWeightSecond : 1;
-    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
-                    phase_geometry(rb_d * no, no, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
-                    phase_geometry(rb_gu * nq, nq, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
-                    phase_geometry(rb_d * nf, nf, kGroup, P, pk.wa, pk.wb, slots_unused, why) &&
+    for (int k = 0; k < 4; ++k) {
+        pk.wa[k] = P == 2 * n_cu ? kPkWeights[k][0] : 1;
+        pk.wb[k] = P == 2 * n_cu ? kPkWeights[k][1] : 1;
+    }
+    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, pk.wa[kPhQ], pk.wb[kPhQ], slots_unused, why) &&
+                    phase_geometry(rb_d * no, no, kGroup, P, pk.wa[kPhO], pk.wb[kPhO], slots_unused, why) &&
+                    phase_geometry(rb_gu * nq, nq, kGroup, P, pk.wa[kPhGU], pk.wb[kPhGU], slots_unused, why) &&
+                    phase_geometry(rb_d * nf, nf, kGroup, P, pk.wa[kPhD], pk.wb[kPhD], slots_unused, why) &&
                     phase_geometry(rb_lm * nkc, nkc, 32, P, 1, 1, pk.slots_lm, why);
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
     // normalised inputs are staged whole, one element per thread and batch slot
@@ -839,7 +841,7 @@ static w4_status setup_persistent(w4_model *m) {
     pk.acc_d = pk.acc_gu + 2 * f;
     pk.acc_layer = static_cast<size_t>(pk.acc_d + d);
     pk.cnt_off = align256(pk.acc_layer * L * 8);
-    pk.par_bytes = pk.cnt_off + align256((static_cast<size_t>(L) * pk.cnt_layer + 1) * kCS * 4);
+    pk.par_bytes = pk.cnt_off + align256((static_cast<size_t>(L) * pk.cnt_layer + 1) * kCS * kCRep * 4);
 
     // library-owned persistent buffers
     const size_t part = static_cast<size_t>(rb_lm) * pk.slots_lm * 64 * 8;
