@@ -907,7 +907,8 @@ def standalone_kernels(attention: bool = True):
     _, want = w4.w4a16_mlp(bgq[R - 1], bgs[R - 1], bdq[R - 1], bds[R - 1], x, d, f)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), want.view(torch.int16)), "mlp: replayed output differs"
-    b = _w4_bytes(2 * f, d) + _w4_bytes(d, f)
+    # weights and scales of both matrices, x, h written and read back, y
+    b = 2 * f * d // 2 + 2 * f * (d // 128) * 2 + d * f // 2 + d * (f // 128) * 2 + 2 * d + 2 * (2 * f) + 2 * d
     out["mlp_cfg1"] = {"D": d, "F": f, "us_per_call": round(us, 2), "bytes": b,
                        "GBps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                        "launches": 3, "copies": R}

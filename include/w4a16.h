@@ -110,7 +110,9 @@ w4_status w4_pack_f16_matrix(const uint16_t *w, int64_t N, int64_t K,
  * W4A16 GEMV  ([TS] "Engineering Challenges" item 3, the fp16-activation
  * path: int4 weights unpacked on the fly, fp16 activations, no activation
  * quantisation).  y[r] = fp16( sum_k W[r][k] * x[k] ) for packed rows
- * r < N, accumulated in fp32 within a group and fp64 across groups.
+ * r < N: every 8 consecutive products summed with correctly rounded fp32
+ * operations (pair sums, then two adds), those 8-term sums and the groups
+ * added in fp64.
  *
  *   packed_q, packed_s : device, from pack_int4_weights (any row_perm; y is
  *                        in packed row order)
@@ -188,6 +190,11 @@ w4_status w4a8_gemv(const uint8_t *packed_q, const uint16_t *packed_s, const voi
  *   x              : device, fp16 [D];  h : fp16 [F] and y : fp16 [D] (written)
  *   workspace      : device, w4_mlp_ws_bytes(D, F) bytes of scratch, zero
  *                    before first use and left zero (as for w4a16_gemv)
+ * The down GEMV sums as w4a16_gemv does.  The gate+up GEMV, whose input is
+ * the block's normalised activation (O(1) entries), chains each group's
+ * products in one fp32 accumulator (v_dot2 accumulation: about 40% less VALU
+ * work; the accumulator's low bits are cut, which stays within the GEMV
+ * tolerance only when outputs are not much smaller than their terms).
  * D and F must be positive multiples of 128.  Errors as for w4a16_gemv. */
 size_t w4_mlp_ws_bytes(int64_t D, int64_t F);
 w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *down_q,

@@ -88,12 +88,16 @@ __device__ __forceinline__ void dot8v(uint32_t w, const uint32_t (&xs)[4], float
 }
 
 // A pair sum a.x b.x + a.y b.y from a zero accumulator: correctly rounded
-// (the same measurement: every sum but 13 in 2^20 random ones).  Written as
-// the three-operand form with an inline zero; through the builtin the compiler
-// folds an addition of two such sums back into a chained accumulation.
+// (the same measurement: every sum but 13 in 2^20 random ones).  The result
+// passes through an empty asm: otherwise the compiler folds an addition of two
+// such sums back into a chained accumulation.  Kept as the builtin, not an asm
+// dot: the compiler then spaces a dot's result from its reader by the wait
+// states the hardware needs, which it cannot do for an instruction hidden in
+// asm (an asm dot read one instruction later returned the previous contents of
+// its destination).
 __device__ __forceinline__ float dot2z(h2 a, h2 b) {
-    float r;
-    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    float r = __builtin_amdgcn_fdot2(a, b, 0.0f, false);
+    asm volatile("" : "+v"(r));
     return r;
 }
 

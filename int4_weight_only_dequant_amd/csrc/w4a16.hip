@@ -147,7 +147,7 @@ static bool sg_shape_ok(int64_t N, int64_t K) {
     return N >= 1 && K >= kGroup && K % kGroup == 0 && ((N + 63) / 64) * (K / kGroup) < (int64_t(1) << 31);
 }
 
-template <class Epi, bool kA8 = false>
+template <class Epi, bool kA8 = false, bool kExact = true>
 static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const void *x, int64_t N, int64_t K,
                             void *ws, const Epi &epi, hipStream_t s) {
     const int n_rb = static_cast<int>((N + 63) / 64), ng = static_cast<int>(K / kGroup);
@@ -165,7 +165,7 @@ static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const void *x,
     p.key_by_rb = g.key_by_rb;
     p.ctr = static_cast<unsigned *>(ws);
     p.slots = reinterpret_cast<double *>(static_cast<char *>(ws) + sg_ctr_bytes(g));
-    hipLaunchKernelGGL((sg_gemv_kernel<Epi, kA8>), dim3(g.P), dim3(kThreads), 0, s, p, epi);
+    hipLaunchKernelGGL((sg_gemv_kernel<Epi, kA8, kExact>), dim3(g.P), dim3(kThreads), 0, s, p, epi);
     return hipGetLastError();
 }
 
@@ -306,7 +306,8 @@ extern "C" w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const 
     const size_t need = w4_mlp_ws_bytes(D, F);
     W4_CHECK(ws_bytes >= need, W4_EINVAL, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    W4_HIP(launch_sg(gu_q, gu_s, x, 2 * F, D, workspace, EpiSwiGLU{h, static_cast<int>(F)}, s));
+    W4_HIP((launch_sg<EpiSwiGLU, false, false>(gu_q, gu_s, x, 2 * F, D, workspace, EpiSwiGLU{h, static_cast<int>(F)},
+                                              s)));
     W4_HIP(launch_sg(down_q, down_s, h, D, F, workspace, EpiStoreF16{y, static_cast<int>(D)}, s));
     return W4_OK;
 }

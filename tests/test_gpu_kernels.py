@@ -142,6 +142,47 @@ def test_mlp_cfg1():
     say(f"mlp end-to-end rel err {np.max(np.abs(y - y_ref) / np.maximum(np.abs(y_ref), 1e-3)):.3e}")
 
 
+def _mlp_operands(d, f, seed_cfg):
+    m = synth.mlp_cfg1(seed=seed_cfg, d=d, f=f)
+    cfg = L.ModelConfig(d_model=d, d_ff=f, n_layers=1, n_q_heads=max(1, d // 128), n_kv_heads=1, head_dim=128,
+                        vocab=1, max_pages=1, eps=1e-6, theta=1e6)
+    perm = w4.model_row_perm(L.W4_PERM_GATE_UP, cfg)
+    pgq, pgs = w4.pack_int4_weights(np.concatenate([m["gate"][0], m["up"][0]]),
+                                    np.concatenate([m["gate"][1], m["up"][1]]), row_perm=perm)
+    pdq, pds = w4.pack_int4_weights(*m["down"])
+    return m, [_dev(a) for a in (pgq, pgs, pdq, pds, m["x"])]
+
+
+def _mlp_raw(ops, d, f, ws):
+    """One w4a16_mlp call through the C ABI on a caller-held workspace."""
+    lib = L.lib()
+    h = torch.empty(f, dtype=torch.float16, device=DEV)
+    y = torch.empty(d, dtype=torch.float16, device=DEV)
+    L.check(lib.w4a16_mlp(*[t.data_ptr() for t in ops], h.data_ptr(), y.data_ptr(), d, f, ws.data_ptr(),
+                          ws.numel(), torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    return h.cpu().numpy(), y.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,f", [(128, 128), (256, 384), (384, 1280), (1024, 2816), (3584, 18944)])
+def test_mlp_shapes_and_workspace_reuse(d, f):
+    """Small, ragged and full shapes; five calls on one workspace give the
+    same bits as the first, and the workspace is left zero."""
+    say(f"case: mlp D={d} F={f}, 5 calls on one workspace")
+    m, ops = _mlp_operands(d, f, 131)
+    ws = torch.zeros(max(L.lib().w4_mlp_ws_bytes(d, f), 256), dtype=torch.uint8, device=DEV)
+    h0, y0 = _mlp_raw(ops, d, f, ws)
+    g_ref = oracle.gemv(*m["gate"], m["x"])
+    u_ref = oracle.gemv(*m["up"], m["x"])
+    assert_gemv(h0, oracle.swiglu(g_ref, u_ref), f"h D={d} F={f}")
+    assert_gemv(y0, oracle.gemv(*m["down"], h0), f"y D={d} F={f}")
+    for i in range(4):
+        h, y = _mlp_raw(ops, d, f, ws)
+        assert np.array_equal(h.view(np.uint16), h0.view(np.uint16)), f"call {i + 2}: h differs"
+        assert np.array_equal(y.view(np.uint16), y0.view(np.uint16)), f"call {i + 2}: y differs"
+    assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
+
+
 # ------------------------------------------------------------ attention ----
 
 def _gpu_attn(q, kp, vp, table, ctx, n_pages_max=None, scale=1 / math.sqrt(128)):
