@@ -1118,6 +1118,29 @@ def main():
     graph_same_ms = float(step_us[:eager_n].mean()) / 1e3
     assert model.device_error() == 0, "device error during the eager steps"
 
+    # the int8-activation variant (W4_A8: the pages' Path A), graph replays
+    # after the same prefill; 4 warmup steps (the first captures its graphs)
+    a8_n = max(1, min(60, args.steps - 4))   # the pool holds n_prompt + steps positions
+    model.reset(prompt)
+    model.prefill(n_prompt)
+    for _ in range(4):
+        model.step(L.W4_GRAPH | L.W4_A8)
+    torch.cuda.synchronize()
+    ev8 = [torch.cuda.Event(enable_timing=True) for _ in range(a8_n + 1)]
+    t8 = time.perf_counter()
+    for i in range(a8_n):
+        ev8[i].record(stream)
+        model.step(L.W4_GRAPH | L.W4_A8)
+    ev8[-1].record(stream)
+    torch.cuda.synchronize()
+    a8_ms = (time.perf_counter() - t8) * 1e3 / a8_n
+    a8_us = np.array([ev8[i].elapsed_time(ev8[i + 1]) * 1e3 for i in range(a8_n)])
+    a8_bnd = np.array([(n_prompt + 4 + i) % 16 == 0 for i in range(a8_n)])
+    a8_kern_us = float(a8_us[~a8_bnd].mean())
+    assert model.device_error() == 0, "device error during the int8-activation steps"
+    log(f"[bench] int8-activation step: {a8_ms:.3f} ms/token, kernel {a8_kern_us:.1f} us "
+        f"(fp16 path {kern_us:.1f} us)")
+
     # kernel-per-op variant, per-kernel times (timing hook; clobbers the activation scratch)
     kern = {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1183,6 +1206,11 @@ def main():
         "eager_vs_graph": {"positions": f"{n_prompt}-{n_prompt + eager_n - 1}", "eager_ms_per_step": round(eager_ms, 3),
                            "graph_ms_per_step_same_positions": round(graph_same_ms, 3)},
         "launches_per_step": launches,
+        "int8_activation_step": {"flag": "W4_A8", "positions": f"{n_prompt + 4}-{n_prompt + 3 + a8_n}",
+                                 "ms_per_step": round(a8_ms, 4), "kernel_us": round(a8_kern_us, 2),
+                                 "fp16_kernel_us": round(kern_us, 2),
+                                 "note": "every int4 GEMV input quantised per group of 128 to int8 inside "
+                                         "the persistent kernel's staging; integer dot products; lm_head fp16"},
         "kernel_per_op_variant": {"launches_per_step": multi_launches, **kern},
         "standalone_calls": standalone,
         "tokens_head": [int(t) for t in gen[:16]],

@@ -368,11 +368,20 @@ int32_t w4_model_pos(const w4_model *m);
  * flags: W4_GRAPH replays the captured graph of the matching variant;
  * W4_EAGER launches the same kernels directly.
  * Errors: W4_ESTATE (pos mismatch), W4_ENOSPC (pos >= 16*max_pages),
- * W4_EHIP. */
+ * W4_EINVAL (unknown or conflicting flags), W4_EHIP. */
 #define W4_GRAPH 0u   /* replay the captured graph (default)                 */
 #define W4_EAGER 1u   /* launch the same kernels directly                     */
 #define W4_MULTI 2u   /* with W4_GRAPH/W4_EAGER: the one-kernel-per-operation
                          step (143 launches) instead of the persistent one    */
+#define W4_A8    4u   /* with W4_GRAPH/W4_EAGER, not W4_MULTI: the persistent
+                         step with int8 activations ([TS] "Engineering
+                         Challenges" item 3, Path A): every int4 GEMV input
+                         (the normalised residual, the attention output, h)
+                         is quantised per group of 128 as w4a8_quantize_act
+                         does, and the GEMVs take integer dot products; the
+                         lm_head stays fp16.  Its graphs are captured on first
+                         use.  W4_EINVAL if a work-group would stage more than
+                         32 groups (d_model > 4096).                          */
 w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void *stream);
 
 /* Prefill of n_tokens (1..512) prompt tokens at positions pos .. pos +

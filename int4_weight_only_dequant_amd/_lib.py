@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 W4_OK, W4_EINVAL, W4_EALIGN, W4_ERANGE, W4_ESTATE, W4_ENOSPC, W4_EHIP = 0, -1, -2, -3, -4, -5, -6
 W4_PERM_QKV, W4_PERM_GATE_UP = 0, 1
-W4_GRAPH, W4_EAGER, W4_MULTI = 0, 1, 2
+W4_GRAPH, W4_EAGER, W4_MULTI, W4_A8 = 0, 1, 2, 4
 W4_KERNEL_GATE_UP, W4_KERNEL_DOWN, W4_KERNEL_O, W4_KERNEL_LM_HEAD = 0, 1, 2, 3
 
 _STATUS = {W4_EINVAL: "W4_EINVAL", W4_EALIGN: "W4_EALIGN", W4_ERANGE: "W4_ERANGE",

@@ -704,6 +704,148 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
     if (cur >= 0) red[cur * kPkThreads + wave * 64 + lane] = acc;
 }
 
+// ------------------------------------------- int8 activations (W4_A8) --
+// The int8-activation variant of the step ("Building a Custom LLM Inference
+// Runtime…", section "Engineering Challenges" item 3; "The Architecture of
+// Modern Inference…", section "Three Critical Engineering Challenges" item
+// 3): each int4 GEMV's staged fp16 input is quantised per group of 128 in
+// the staging area itself, as w4a8_quantize_act does: scale s = max|x| / 127
+// in fp32, codes round-half-even(x / s) in fp32 clamped to [-127, 127] (an
+// all-zero group: scale 0, zero codes), plus each group's code sum.  Codes
+// of group u go to bytes 128 u .. 128 u + 127 of the staging area in the
+// order the int4 words pair them with (words (e0, e4, e1, e5), (e2, e6, e3,
+// e7) per block of 8), the scales and sums after them.
+constexpr int kA8GroupsPerWave = 8;                       // host-checked: at most 32 staged groups
+// scales and sums sit past the fp16 input of the largest staging (written
+// while the fp16 is still being read)
+constexpr int kA8ScaleOff = kA8GroupsPerWave * kPkWaves * 256;
+constexpr int kA8SumOff = kA8ScaleOff + kA8GroupsPerWave * kPkWaves * 4;
+static_assert(kA8SumOff + kA8GroupsPerWave * kPkWaves * 4 <= kStageBytes, "int8 staging fits the stage area");
+
+// Wave-wide max and sum: within each 16-lane row by DPP (as row16_sum),
+// then the four row results by readlane (a shuffle through LDS per step
+// measured about 4 us per phase on the step).
+__device__ __forceinline__ int dpp_i32(int v, int ctrl_q) {
+    switch (ctrl_q) {   // the DPP control must be a constant
+        case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+        case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+        default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    }
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v = fmaxf(v, __builtin_bit_cast(float, dpp_i32(__builtin_bit_cast(int, v), c)));
+    const int b = __builtin_bit_cast(int, v);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v += dpp_i32(v, c);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// ng staged groups of 128 fp16 (group u at element 128 u), in place; wave w
+// takes groups w, w + 4, ...; lane holds elements 2 lane, 2 lane + 1.  All
+// reads finish before the barrier, all writes come after it (the codes of a
+// group overlap the fp16 of lower groups).  Ends with a barrier.
+__device__ __forceinline__ void stage_quant_a8(uint16_t *lds, int ng) {
+    const int wave = wave_id(), lane = lane_id();
+    unsigned char *cb = reinterpret_cast<unsigned char *>(lds);
+    uint32_t code2[kA8GroupsPerWave];
+#pragma unroll
+    for (int k = 0; k < kA8GroupsPerWave; ++k) {
+        const int u = wave + kPkWaves * k;
+        code2[k] = 0u;
+        if (u < ng) {
+            const uint32_t pr = reinterpret_cast<const uint32_t *>(lds)[u * 64 + lane];
+            const float x0 = f16_to_f32(static_cast<uint16_t>(pr & 0xFFFFu));
+            const float x1 = f16_to_f32(static_cast<uint16_t>(pr >> 16));
+            const float amax = wave_max_f32(fmaxf(fabsf(x0), fabsf(x1)));
+            const float sc = amax / 127.0f;                        // IEEE division, as the oracle's float32
+            int c0 = 0, c1 = 0;
+            if (sc != 0.f) {
+                c0 = static_cast<int>(fminf(fmaxf(rintf(x0 / sc), -127.f), 127.f));
+                c1 = static_cast<int>(fminf(fmaxf(rintf(x1 / sc), -127.f), 127.f));
+            }
+            code2[k] = static_cast<uint32_t>(c0 & 0xFF) | (static_cast<uint32_t>(c1 & 0xFF) << 8);
+            const int sm = wave_sum_i32(c0 + c1);
+            if (lane == 0) {
+                reinterpret_cast<float *>(cb + kA8ScaleOff)[u] = sc;
+                reinterpret_cast<int *>(cb + kA8SumOff)[u] = sm;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kA8GroupsPerWave; ++k) {
+        const int u = wave + kPkWaves * k;
+        if (u < ng) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * lane + h, blk = e >> 3, r = e & 7;
+                const int word = 2 * blk + ((r >> 1) & 1), byte = ((r & 1) << 1) | (r >> 2);
+                cb[u * 128 + word * 4 + byte] = static_cast<unsigned char>((code2[k] >> (8 * h)) & 0xFFu);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// int4 x int8 tile loop of one wave (same walk as w4_tiles): per tile the
+// integer dot product of the unsigned nibbles (q + 8) with the codes, minus
+// 8 x the group's code sum, times the activation and weight scales in fp64.
+__device__ __forceinline__ void w4_tiles_a8(Ring &r, const u32x4 *wq, const uint16_t *ws, int ng, Range rg,
+                                            bool whole, int rb0, const uint16_t *lds, double *red) {
+    const int wave = wave_id(), lane = lane_id();
+    const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + kPkWaves - 1) / kPkWaves : 0;
+    const unsigned char *cb = reinterpret_cast<const unsigned char *>(lds);
+    int cur = -1;
+    double acc = 0.0;
+    for (int k0 = 0; k0 < n; k0 += kRing) {
+#pragma unroll
+        for (int s = 0; s < kRing; ++s) {
+            const int k = k0 + s;
+            if (k < n) {
+                const int i = wave + kPkWaves * k;
+                const int t = rg.b + i;
+                const int rl = t / ng - rb0;
+                if (rl != cur) {
+                    if (cur >= 0) red[cur * kPkThreads + wave * 64 + lane] = acc;
+                    acc = 0.0;
+                    cur = rl;
+                }
+                const int gx = whole ? t % ng : i;
+                const u32x4 *xc = reinterpret_cast<const u32x4 *>(cb + gx * 128);
+                int dot = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 xa = xc[2 * c], xb = xc[2 * c + 1];
+                    const uint32_t wv[4] = {r.w[s][c].x, r.w[s][c].y, r.w[s][c].z, r.w[s][c].w};
+                    const uint32_t xl[4] = {xa.x, xa.z, xb.x, xb.z}, xh[4] = {xa.y, xa.w, xb.y, xb.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        dot = __builtin_amdgcn_sdot4(static_cast<int>(wv[q] & 0x0F0F0F0Fu), static_cast<int>(xl[q]), dot,
+                                                     false);
+                        dot = __builtin_amdgcn_sdot4(static_cast<int>((wv[q] >> 4) & 0x0F0F0F0Fu),
+                                                     static_cast<int>(xh[q]), dot, false);
+                    }
+                }
+                const float sx = reinterpret_cast<const float *>(cb + kA8ScaleOff)[gx];
+                const int sumc = reinterpret_cast<const int *>(cb + kA8SumOff)[gx];
+                acc += static_cast<double>(dot - 8 * sumc) * static_cast<double>(sx) *
+                       static_cast<double>(f16_to_f32(r.s[s]));
+                if (k + kRing < n) load_w4_tile(r, s, wq, ws, ng, t + kPkWaves * kRing);
+            }
+        }
+    }
+    if (cur >= 0) red[cur * kPkThreads + wave * 64 + lane] = acc;
+}
+
 // fp16 (lm_head) tile loop of one wave: fp32 accumulation per row block; the
 // normalised input is staged whole.  (Two or three tiles in flight per wave
 // instead of one measured the same, 1.495-1.497 ms per step: the phase
@@ -1140,6 +1282,9 @@ __device__ __forceinline__ void phase_reduce(const PKParams &p, const PhaseDesc 
     // work-group-wide barrier
 }
 
+// kA8: the int8-activation variant (every int4 GEMV's input quantised in
+// staging, integer dot products); the lm_head stays fp16.
+template <bool kA8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kPkThreads, kPkThreads), amdgpu_waves_per_eu(2)))
 void decode_persistent_kernel(const PKParams *__restrict__ pp) {
     // parameters live in device memory: functions below take their address,
@@ -1285,7 +1430,12 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             if (p.dbg_stage)
                 pk_dump_stage(p.dbg_stage + static_cast<size_t>(ph) * p.dbg_stride, s_stage,
                               g.stage == kStNorm ? p.d : (whole ? g.nk * g.V : 0), rg.b, rg.e, g.nk, g.V);
+            if constexpr (kA8) {
+                if (g.kind != kPhLM) stage_quant_a8(s_stage, whole ? g.nk : rg.e - rg.b);
+            }
             if (g.kind == kPhLM) f16_tiles(ring, p.lm, g.nk, rg, rb0, s_stage, s_red);
+            else if (kA8)
+                w4_tiles_a8(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
             else if (g.kind == kPhO || g.kind == kPhD)
                 w4_tiles<true>(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
             else

@@ -553,6 +553,8 @@ struct w4_model {
     hipStream_t cap_stream;
     hipGraphExec_t exec[2];   // persistent step: [0] no page boundary, [1] page boundary
     hipGraphExec_t exec_multi[2];   // kernel-per-op step, same variants
+    hipGraphExec_t exec_a8[2];      // persistent int8-activation step (captured on first use)
+    bool a8_ok;                     // the int8 variant's staged groups fit its registers
     int pos;                  // host mirror of the device position
     int n_prompt;
     int launches;
@@ -644,21 +646,25 @@ static hipError_t enqueue_step(w4_model *m, bool boundary, hipStream_t s) {
     return hipSuccess;
 }
 
-static hipError_t enqueue_persistent(w4_model *m, bool boundary, hipStream_t s) {
+static hipError_t enqueue_persistent(w4_model *m, bool boundary, hipStream_t s, bool a8 = false) {
     if (boundary) {
         hipLaunchKernelGGL(page_append_kernel, dim3(1), dim3(1), 0, s, m->state, m->page_table, m->free_list);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(decode_persistent_kernel, dim3(m->pk_grid), dim3(kPkThreads), 0, s,
-                       static_cast<const PKParams *>(m->pk_dev));
+    if (a8)
+        hipLaunchKernelGGL(decode_persistent_kernel<true>, dim3(m->pk_grid), dim3(kPkThreads), 0, s,
+                           static_cast<const PKParams *>(m->pk_dev));
+    else
+        hipLaunchKernelGGL(decode_persistent_kernel<false>, dim3(m->pk_grid), dim3(kPkThreads), 0, s,
+                           static_cast<const PKParams *>(m->pk_dev));
     return hipGetLastError();
 }
 
-static w4_status capture(w4_model *m, bool boundary, bool multi, hipGraphExec_t *out) {
+static w4_status capture(w4_model *m, bool boundary, bool multi, hipGraphExec_t *out, bool a8 = false) {
     hipGraph_t g = nullptr;
     W4_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-    hipError_t e = multi ? enqueue_step(m, boundary, m->cap_stream) : enqueue_persistent(m, boundary, m->cap_stream);
+    hipError_t e = multi ? enqueue_step(m, boundary, m->cap_stream) : enqueue_persistent(m, boundary, m->cap_stream, a8);
     hipError_t e2 = hipStreamEndCapture(m->cap_stream, &g);
     if (e != hipSuccess || e2 != hipSuccess) {
         if (g) (void)hipGraphDestroy(g);
@@ -675,6 +681,7 @@ static void model_free(w4_model *m) {
     for (int i = 0; i < 2; ++i) {
         if (m->exec[i]) (void)hipGraphExecDestroy(m->exec[i]);
         if (m->exec_multi[i]) (void)hipGraphExecDestroy(m->exec_multi[i]);
+        if (m->exec_a8[i]) (void)hipGraphExecDestroy(m->exec_a8[i]);
     }
     if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
     if (m->arena) (void)hipFree(m->arena);
@@ -765,7 +772,8 @@ static hipError_t enqueue_prefill(w4_model *m, int pos0, int M, hipStream_t s) {
 
 // Largest number of work-groups that split one row block, and the checks
 // that every work-group's range fits the kernel's LDS areas.
-static bool phase_geometry(int T, int nk, int V, int P, int wa, int wb, int &slots, std::string &why) {
+static bool phase_geometry(int T, int nk, int V, int P, int wa, int wb, int &slots, std::string &why,
+                           int *max_staged = nullptr) {
     slots = 1;
     const int n_rb = T / nk;
     const Part q = make_part(T, P, wa, wb);
@@ -786,6 +794,7 @@ static bool phase_geometry(int T, int nk, int V, int P, int wa, int wb, int &slo
         }
         if (e <= b) continue;
         const int staged = (e - b >= nk ? nk : e - b) * V;   // whole vector or the range's slices
+        if (max_staged) *max_staged = std::max(*max_staged, staged);
         if (staged * 2 > kStageBytes) { why = "staged input exceeds LDS"; return false; }
         if (staged > kStageMax * kPkThreads) { why = "staged input exceeds the per-thread batch"; return false; }
         if ((e - 1) / nk - b / nk + 1 > kMaxRbPerWg) { why = "range touches too many row blocks"; return false; }
@@ -798,7 +807,10 @@ static w4_status setup_persistent(w4_model *m) {
     int dev = 0, n_cu = 0, occ = 0;
     W4_HIP(hipGetDevice(&dev));
     W4_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
-    W4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_persistent_kernel, kPkThreads, 0));
+    int occ8 = 0;
+    W4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_persistent_kernel<false>, kPkThreads, 0));
+    W4_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ8, decode_persistent_kernel<true>, kPkThreads, 0));
+    occ = std::min(occ, occ8);   // one grid for both variants
     W4_CHECK(occ >= 1 && n_cu >= 1, W4_EHIP, "persistent kernel cannot be resident (occupancy %d)", occ);
     const int P = n_cu * std::min(occ, kPkWgPerCu);
     const int L = c.n_layers, d = c.d_model, f = c.d_ff;
@@ -822,11 +834,14 @@ static w4_status setup_persistent(w4_model *m) {
         pk.wa[k] = P == 2 * n_cu ? kPkWeights[k][0] : 1;
         pk.wb[k] = P == 2 * n_cu ? kPkWeights[k][1] : 1;
     }
-    const bool ok = phase_geometry(rb_q * nq, nq, kGroup, P, pk.wa[kPhQ], pk.wb[kPhQ], slots_unused, why) &&
-                    phase_geometry(rb_d * no, no, kGroup, P, pk.wa[kPhO], pk.wb[kPhO], slots_unused, why) &&
-                    phase_geometry(rb_gu * nq, nq, kGroup, P, pk.wa[kPhGU], pk.wb[kPhGU], slots_unused, why) &&
-                    phase_geometry(rb_d * nf, nf, kGroup, P, pk.wa[kPhD], pk.wb[kPhD], slots_unused, why) &&
-                    phase_geometry(rb_lm * nkc, nkc, 32, P, 1, 1, pk.slots_lm, why);
+    int staged_max = d;   // the norm phases stage the whole vector
+    const bool ok =
+        phase_geometry(rb_q * nq, nq, kGroup, P, pk.wa[kPhQ], pk.wb[kPhQ], slots_unused, why, &staged_max) &&
+        phase_geometry(rb_d * no, no, kGroup, P, pk.wa[kPhO], pk.wb[kPhO], slots_unused, why, &staged_max) &&
+        phase_geometry(rb_gu * nq, nq, kGroup, P, pk.wa[kPhGU], pk.wb[kPhGU], slots_unused, why, &staged_max) &&
+        phase_geometry(rb_d * nf, nf, kGroup, P, pk.wa[kPhD], pk.wb[kPhD], slots_unused, why, &staged_max) &&
+        phase_geometry(rb_lm * nkc, nkc, 32, P, 1, 1, pk.slots_lm, why);
+    m->a8_ok = staged_max <= kA8GroupsPerWave * kPkWaves * kGroup;
     W4_CHECK(ok, W4_EINVAL, "persistent schedule does not fit: %s (grid %d)", why.c_str(), P);
     // normalised inputs are staged whole, one element per thread and batch slot
     W4_CHECK(d <= kStageMax * kPkThreads && d * 2 <= kStageBytes && d <= kEmbChunks * 64 * 8, W4_EINVAL,
@@ -1107,14 +1122,21 @@ extern "C" w4_status decode_step(w4_model *m, int32_t pos, uint32_t flags, void 
     W4_CHECK(pos == m->pos, W4_ESTATE, "position %d out of sequence (model is at %d)", pos, m->pos);
     W4_CHECK(pos < m->cfg.max_pages * kPage, W4_ENOSPC, "position %d beyond the KV pool (%d tokens)", pos,
              m->cfg.max_pages * kPage);
-    W4_CHECK(flags <= (W4_EAGER | W4_MULTI), W4_EINVAL, "unknown flags %u", flags);
+    W4_CHECK(flags <= (W4_EAGER | W4_MULTI | W4_A8), W4_EINVAL, "unknown flags %u", flags);
     const bool boundary = (pos % kPage) == 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool eager = flags & W4_EAGER, multi = flags & W4_MULTI;
+    const bool eager = flags & W4_EAGER, multi = flags & W4_MULTI, a8 = flags & W4_A8;
+    W4_CHECK(!(a8 && multi), W4_EINVAL, "W4_A8 is a variant of the persistent step, not of W4_MULTI");
+    W4_CHECK(!a8 || m->a8_ok, W4_EINVAL, "this model's staged inputs are too long for the int8 variant");
+    if (a8 && !eager && !m->exec_a8[0]) {
+        w4_status st = capture(m, false, false, &m->exec_a8[0], true);
+        if (st == W4_OK) st = capture(m, true, false, &m->exec_a8[1], true);
+        if (st != W4_OK) return st;
+    }
     if (eager) {
-        W4_HIP(multi ? enqueue_step(m, boundary, s) : enqueue_persistent(m, boundary, s));
+        W4_HIP(multi ? enqueue_step(m, boundary, s) : enqueue_persistent(m, boundary, s, a8));
     } else {
-        W4_HIP(hipGraphLaunch((multi ? m->exec_multi : m->exec)[boundary ? 1 : 0], s));
+        W4_HIP(hipGraphLaunch((multi ? m->exec_multi : a8 ? m->exec_a8 : m->exec)[boundary ? 1 : 0], s));
     }
     m->pos = pos + 1;
     return W4_OK;

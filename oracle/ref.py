@@ -31,7 +31,7 @@ import numpy as np
 F64 = np.float64
 
 __all__ = [
-    "f16", "deq", "gemv", "quantize_int4", "quantize_act_int8", "gemv_w4a8", "rmsnorm", "rope", "silu", "swiglu", "softmax",
+    "f16", "deq", "gemv", "quantize_int4", "quantize_act_int8", "act_int8", "gemv_w4a8", "rmsnorm", "rope", "silu", "swiglu", "softmax",
     "paged_attention", "causal_attention", "mlp", "argmax_first",
     "KVCache", "layer_step", "decode_step", "forward_teacher_forced",
 ]
@@ -123,6 +123,26 @@ def quantize_act_int8(x: np.ndarray, group: int = 128) -> tuple:
         r = np.rint(xg[g] / scales[g]).astype(np.float32)     # float32 quotient, ties to even
         codes[g] = np.clip(r, -127, 127).astype(np.int8)
     return codes.reshape(k), scales
+
+
+def act_int8(x: np.ndarray, group: int = 128) -> np.ndarray:
+    """What an int8-activation GEMV multiplies: the fp16 input x (a vector [K]
+    or rows [T, K]) quantised per group as quantize_act_int8 does, returned
+    dequantised (codes times scale) in float64.  gemv(q, s, act_int8(x)) is
+    gemv_w4a8 of the quantised x.  Rows are quantised independently; the
+    arithmetic is quantize_act_int8's (float32 scale and quotient, ties to
+    even, clamp), written over all groups at once."""
+    x = np.asarray(x, dtype=np.float16)
+    lead, k = x.shape[:-1], x.shape[-1]
+    if k % group:
+        raise ValueError(f"K={k} is not a multiple of {group}")
+    xg = x.astype(np.float32).reshape(*lead, k // group, group)
+    scales = (np.max(np.abs(xg), axis=-1) / np.float32(127.0)).astype(np.float32)
+    nz = scales != 0
+    safe = np.where(nz, scales, np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.rint(xg / safe[..., None]).astype(np.float32), -127, 127)
+    codes = np.where(nz[..., None], codes, np.float32(0.0))
+    return (codes.astype(F64) * scales[..., None].astype(F64)).reshape(*lead, k)
 
 
 def gemv_w4a8(q: np.ndarray, s: np.ndarray, xq: np.ndarray, xs: np.ndarray, group: int = 128) -> np.ndarray:
@@ -288,15 +308,28 @@ def _split_qkv(dims, y):
     return q, k, v
 
 
+def _gemv_input(act: str):
+    """The four int4 GEMV inputs as the projections see them: the fp16 vector
+    itself (act="f16"), or its per-group int8 quantisation (act="int8", the
+    pages' integer-activation path, [TS] "Engineering Challenges" item 3)."""
+    if act == "f16":
+        return lambda v: v
+    if act == "int8":
+        return act_int8
+    raise ValueError(f"unknown activation mode {act!r}")
+
+
 def layer_step(dims, lw, x: np.ndarray, pos: int, cache: KVCache, layer: int,
-               trace: dict | None = None) -> np.ndarray:
+               trace: dict | None = None, act: str = "f16") -> np.ndarray:
     """One decoder layer for the token at position pos; returns the new residual.
 
     x is the float64 residual [d].  The layer's own k, v are appended to the
-    cache before attention, so the token attends to positions 0..pos.
+    cache before attention, so the token attends to positions 0..pos.  act
+    selects how the int4 GEMVs take their fp16 inputs (see _gemv_input).
     """
+    inp = _gemv_input(act)
     a = f16(rmsnorm(x, lw.ln1, dims.eps))
-    y = gemv(*lw.qkv, a) + lw.bqkv.astype(F64)
+    y = gemv(*lw.qkv, inp(a)) + lw.bqkv.astype(F64)
     q, k, v = _split_qkv(dims, y)
     q = f16(rope(q, pos, dims.theta))
     k = f16(rope(k, pos, dims.theta))
@@ -305,16 +338,17 @@ def layer_step(dims, lw, x: np.ndarray, pos: int, cache: KVCache, layer: int,
     o = paged_attention(q, cache.k[layer], cache.v[layer], cache.page_table,
                         pos + 1, 1.0 / np.sqrt(dims.head_dim), dims.page)
     o = f16(o).reshape(-1)
-    x = x + gemv(*lw.o, o)
-    a2 = f16(rmsnorm(x, lw.ln2, dims.eps))
-    h = f16(swiglu(gemv(*lw.gate, a2), gemv(*lw.up, a2)))
-    x = x + gemv(*lw.down, h)
+    x1 = x + gemv(*lw.o, inp(o))
+    a2 = f16(rmsnorm(x1, lw.ln2, dims.eps))
+    g, u = gemv(*lw.gate, inp(a2)), gemv(*lw.up, inp(a2))
+    h = f16(swiglu(g, u))
+    x2 = x1 + gemv(*lw.down, inp(h))
     if trace is not None:
-        trace.update(a=a, qkv=y, q=q, k=k, v=v, o=o, a2=a2, h=h, x=x)
-    return x
+        trace.update(a=a, qkv=y, q=q, k=k, v=v, o=o, x1=x1, a2=a2, g=g, u=u, h=h, x=x2)
+    return x2
 
 
-def decode_step(dims, layers, glob, cache: KVCache, token: int, pos: int) -> np.ndarray:
+def decode_step(dims, layers, glob, cache: KVCache, token: int, pos: int, act: str = "f16") -> np.ndarray:
     """Logits (float64 [vocab]) for the token at position pos, updating the cache.
 
     ``layers`` is a sequence of LayerWeights or a callable layer -> LayerWeights.
@@ -322,13 +356,13 @@ def decode_step(dims, layers, glob, cache: KVCache, token: int, pos: int) -> np.
     get = layers if callable(layers) else layers.__getitem__
     x = glob.embed[int(token)].astype(F64)
     for layer in range(dims.n_layers):
-        x = layer_step(dims, get(layer), x, pos, cache, layer)
+        x = layer_step(dims, get(layer), x, pos, cache, layer, act=act)
     xf = f16(rmsnorm(x, glob.lnf, dims.eps))
     return glob.lm_head.astype(F64) @ xf.astype(F64)
 
 
 def forward_teacher_forced(dims, layers, glob, tokens: np.ndarray, out_positions,
-                           progress=None) -> np.ndarray:
+                           progress=None, act: str = "f16") -> np.ndarray:
     """Logits at out_positions for the token sequence, all positions in one pass.
 
     Position p holds tokens[p] and attends to 0..p.  Per position this is the
@@ -337,6 +371,7 @@ def forward_teacher_forced(dims, layers, glob, tokens: np.ndarray, out_positions
     [len(out_positions), vocab].
     """
     get = layers if callable(layers) else layers.__getitem__
+    inp = _gemv_input(act)
     tokens = np.asarray(tokens)
     T = len(tokens)
     pos = np.arange(T)
@@ -345,16 +380,16 @@ def forward_teacher_forced(dims, layers, glob, tokens: np.ndarray, out_positions
     for layer in range(dims.n_layers):
         lw = get(layer)
         A = f16(rmsnorm(X, lw.ln1, dims.eps))
-        Y = gemv(*lw.qkv, A) + lw.bqkv.astype(F64)
+        Y = gemv(*lw.qkv, inp(A)) + lw.bqkv.astype(F64)
         Q, K, V = _split_qkv(dims, Y)
         Q = f16(rope(Q, pos, dims.theta))
         K = f16(rope(K, pos, dims.theta))
         V = f16(V)
         O = f16(causal_attention(Q, K, V, scale)).reshape(T, -1)
-        X = X + gemv(*lw.o, O)
+        X = X + gemv(*lw.o, inp(O))
         A2 = f16(rmsnorm(X, lw.ln2, dims.eps))
-        Hh = f16(swiglu(gemv(*lw.gate, A2), gemv(*lw.up, A2)))
-        X = X + gemv(*lw.down, Hh)
+        Hh = f16(swiglu(gemv(*lw.gate, inp(A2)), gemv(*lw.up, inp(A2))))
+        X = X + gemv(*lw.down, inp(Hh))
         del lw
         if progress is not None:
             progress(layer)

@@ -40,14 +40,15 @@ def run_model(model, prompt, n_steps, flags=L.W4_GRAPH):
 _ORACLE_CACHE = {}
 
 
-def compare_with_oracle(dims, layers, glob, logits, toks, n_prompt, positions, cache_key=None):
-    """Worst |logit error| at positions and the greedy-token mismatches.  With
-    cache_key, the oracle pass for the same key and token history is reused."""
-    key = None if cache_key is None else (cache_key, toks[: positions[-1] + 1].tobytes(), positions.tobytes())
+def compare_with_oracle(dims, layers, glob, logits, toks, n_prompt, positions, cache_key=None, act="f16"):
+    """Worst |logit error| at positions and the greedy-token mismatches against
+    the oracle in activation mode act.  With cache_key, the oracle pass for the
+    same key and token history is reused."""
+    key = None if cache_key is None else (cache_key, act, toks[: positions[-1] + 1].tobytes(), positions.tobytes())
     ref = _ORACLE_CACHE.get(key) if key is not None else None
     if ref is None:
         ref = oracle.forward_teacher_forced(dims, layers, glob, toks[: positions[-1] + 1], positions,
-                                            progress=lambda l: say(f"  oracle layer {l} done"))
+                                            progress=lambda l: say(f"  oracle layer {l} done"), act=act)
         if key is not None:
             _ORACLE_CACHE[key] = ref
     err = np.abs(logits[positions] - ref)
@@ -62,7 +63,7 @@ def compare_with_oracle(dims, layers, glob, logits, toks, n_prompt, positions, c
         if p + 1 >= n_prompt and toks[p + 1] != want:
             mism.append((int(p), int(toks[p + 1]), want, margin))
     gen = toks[positions + 1]
-    rec = {"positions": f"{int(positions[0])}-{int(positions[-1])}", "max_logit_err": worst,
+    rec = {"act": act, "positions": f"{int(positions[0])}-{int(positions[-1])}", "max_logit_err": worst,
            "min_top2_margin": float(min(margins)), "distinct_generated_tokens": int(len(np.unique(gen))),
            "token_mismatches": len(mism)}
     say(f"  parity record: {json.dumps(rec)}")
@@ -249,5 +250,74 @@ def test_full_model_prefill_512_then_128_steps():
     worst, mism = compare_with_oracle(dims, lambda l: synth.layer_weights(dims, l), glob, full, tk,
                                       512, positions, cache_key="qwen7b-512+128")
     say(f"prefill: max |logit err| over 129 positions {worst:.3e}; mismatches {mism} ({time.time() - t0:.0f}s)")
+    assert worst <= LOGIT_ATOL
+    assert not mism
+
+
+# ------------------------------------------------- int8 activations (W4_A8) --
+
+@pytest.mark.parametrize("dims_name", ["tiny", "gqa"])
+def test_a8_step_parity_graph_eager(dims_name):
+    """The int8-activation persistent step against the oracle's int8 mode
+    (same tolerance as the fp16 step: the quantisation is the same function
+    of the same fp16 inputs on both sides), graph == eager bitwise, and the
+    flag's refusals."""
+    if dims_name == "tiny":
+        dims, n_prompt, n, max_pages = synth.TINY, 20, 64, 4
+    else:
+        dims = synth.ModelDims(d_model=512, d_ff=1024, n_layers=2, n_q_heads=14, n_kv_heads=2,
+                               head_dim=128, vocab=1000)
+        n_prompt, n, max_pages = 150, 180, 12
+    layers = [synth.layer_weights(dims, l, cfg=150) for l in range(dims.n_layers)]
+    glob = synth.global_weights(dims, cfg=150)
+    free = synth.page_free_list(max_pages, cfg=150)
+    prompt = synth.prompt_ids(dims, n_prompt, cfg=150)
+    say(f"case: {dims_name} model, int8 activations, {n_prompt} prompt + {n - n_prompt} steps")
+    model = w4.DecodeModel(dims, lambda l: layers[l], glob, free, max_pages)
+    try:
+        lg, tk = run_model(model, prompt, n, L.W4_GRAPH | L.W4_A8)
+        assert model.device_error() == 0
+        le, te = run_model(model, prompt, n, L.W4_EAGER | L.W4_A8)
+        assert model.device_error() == 0
+        assert np.array_equal(tk, te)
+        assert np.array_equal(lg.view(np.uint32), le.view(np.uint32))
+        lf, _ = run_model(model, prompt, n, L.W4_GRAPH)
+        assert np.max(np.abs(lf - lg)) > 1e-4, "the int8 step differs from the fp16 step"
+        model.reset(prompt)
+        with pytest.raises(w4.W4Error) as e:
+            model.step(L.W4_GRAPH | L.W4_A8 | L.W4_MULTI)
+        assert e.value.status == L.W4_EINVAL
+    finally:
+        model.close()
+    positions = np.arange(n_prompt - 1, n)
+    worst, mism = compare_with_oracle(dims, layers, glob, lg, tk, n_prompt, positions, act="int8")
+    say(f"  a8 {dims_name}: max |logit err| {worst:.3e}; mismatches {mism}")
+    assert worst <= LOGIT_ATOL
+    assert not mism
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1500)
+def test_full_model_a8_64_plus_64():
+    """The 7B-shaped int8-activation step: a 64-token prompt, 64 greedy graph
+    steps (4 page boundaries), logits at positions 63..127 against the
+    oracle's int8 mode."""
+    dims = synth.QWEN7B
+    t0 = time.time()
+    say("case: full model 28 layers, int8 activations, prompt 64 + 64 generated, 8 shuffled pages")
+    glob = synth.global_weights(dims)
+    free = synth.page_free_list(8)
+    prompt = synth.prompt_ids(dims, 64)
+    model = w4.DecodeModel(dims, lambda l: synth.layer_weights(dims, l), glob, free, 8,
+                           progress=lambda l: say(f"  packed+uploaded layer {l} ({time.time() - t0:.0f}s)"))
+    try:
+        lg, tk = run_model(model, prompt, 128, L.W4_GRAPH | L.W4_A8)
+        assert model.device_error() == 0
+    finally:
+        model.close()
+    positions = np.arange(63, 128)
+    worst, mism = compare_with_oracle(dims, lambda l: synth.layer_weights(dims, l), glob, lg, tk, 64, positions,
+                                      cache_key="qwen7b-a8-64+64", act="int8")
+    say(f"a8 full: max |logit err| {worst:.3e}; mismatches {mism} ({time.time() - t0:.0f}s)")
     assert worst <= LOGIT_ATOL
     assert not mism

@@ -171,7 +171,7 @@ def _split(dims, y, mut):
 
 
 def _mutant_layer_step(mut):
-    def layer_step(dims, lw, x, pos, cache, layer, trace=None):
+    def layer_step(dims, lw, x, pos, cache, layer, trace=None, act="f16"):
         w1, w2 = (lw.ln2, lw.ln1) if mut == "ln_swap" else (lw.ln1, lw.ln2)
         a = ref.f16(ref.rmsnorm(x, w1, dims.eps))
         y = ref.gemv(*lw.qkv, a)
@@ -202,7 +202,7 @@ def _mutant_layer_step(mut):
 
 
 def _mutant_forward(mut):
-    def forward_teacher_forced(dims, layers, glob, tokens, out_positions, progress=None):
+    def forward_teacher_forced(dims, layers, glob, tokens, out_positions, progress=None, act="f16"):
         get = layers if callable(layers) else layers.__getitem__
         tokens = np.asarray(tokens)
         T = len(tokens)
