@@ -119,13 +119,18 @@ w4_status w4_pack_f16_matrix(const uint16_t *w, int64_t N, int64_t K,
  *   x                  : device, fp16 [K]
  *   y                  : device, fp16 [N] (written)
  *   workspace          : device, w4_gemv_ws_bytes(N, K) bytes of scratch
- *                        (partial sums of row blocks shared by work-groups,
- *                        and their arrival counters).  It must be all zero
- *                        before its first use (e.g. hipMemset once); every
- *                        call leaves it all zero again, whatever the shape,
- *                        so it can be reused across shapes without clearing.
- *                        Calls that share a workspace must be ordered on one
- *                        stream.
+ *                        (a mark word, then partial sums of row blocks
+ *                        shared by work-groups and their arrival counters).
+ *                        It must be all zero before its first use (e.g.
+ *                        hipMemset once); the first call sets the mark (the
+ *                        first 4 bytes) and every call leaves the rest all
+ *                        zero again, whatever the shape, so it can be reused
+ *                        across shapes without clearing.  A workspace whose
+ *                        mark is neither zero nor the library's (memory that
+ *                        was never zeroed) is left untouched and y is filled
+ *                        with NaN; corruption after the mark was set is not
+ *                        detected.  Calls that share a workspace must be
+ *                        ordered on one stream.
  * Errors: W4_EINVAL (N < 1, K not a positive multiple of 128, workspace too
  * small), W4_EALIGN, W4_EHIP (launch failure). */
 size_t w4_gemv_ws_bytes(int64_t N, int64_t K);
@@ -172,7 +177,7 @@ w4_status w4a16_gemv_noalloc(const uint8_t *packed_q, const uint16_t *packed_s,
  * w4a8_gemv: packed_q, packed_s as for w4a16_gemv; act from
  *   w4a8_quantize_act; y device fp16 [N] (packed row order); workspace
  *   w4_gemv_ws_bytes(N, K) bytes with the same contract as for w4a16_gemv
- *   (zero before first use, left zero).
+ *   (zero before first use, mark set and the rest left zero).
  * Errors: W4_EINVAL, W4_EALIGN, W4_EHIP. */
 size_t w4a8_act_bytes(int64_t K);
 w4_status w4a8_quantize_act(const uint16_t *x, int64_t K, void *act, void *stream);
@@ -188,8 +193,8 @@ w4_status w4a8_gemv(const uint8_t *packed_q, const uint16_t *packed_s, const voi
  *                    with the W4_PERM_GATE_UP row order (see below)
  *   down_q, down_s : device, Wd (D rows, K = F) packed in identity order
  *   x              : device, fp16 [D];  h : fp16 [F] and y : fp16 [D] (written)
- *   workspace      : device, w4_mlp_ws_bytes(D, F) bytes of scratch, zero
- *                    before first use and left zero (as for w4a16_gemv)
+ *   workspace      : device, w4_mlp_ws_bytes(D, F) bytes of scratch, with
+ *                    w4a16_gemv's contract (zero before first use)
  * The down GEMV sums as w4a16_gemv does.  The gate+up GEMV, whose input is
  * the block's normalised activation (O(1) entries), chains each group's
  * products in one fp32 accumulator (v_dot2 accumulation: about 40% less VALU

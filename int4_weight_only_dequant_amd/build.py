@@ -3,7 +3,7 @@
 Run ``python -m int4_weight_only_dequant_amd.build`` (or call ``build()``).
 The library is written next to this file, in-tree.  ``--trace`` builds
 libw4a16_trace.so instead: the same library with the persistent decode
-kernel's phase timestamps compiled in (read by ``pk_trace.py``).
+kernel's phase timestamps compiled in (loaded by ``bench.py --phase-trace``).
 """
 from __future__ import annotations
 

@@ -59,7 +59,17 @@ struct SgProblem {
     int key_by_rb;            // shared row blocks keyed by row block (else by first owner)
     double *slots;            // [n_keys][slot_stride][64], zero between calls
     unsigned *ctr;            // [n_keys][kSgCtrStride] arrival counters, zero between calls
+    unsigned *hdr;            // workspace mark: 0 (fresh) or kSgMark once used
 };
+
+// The workspace's first word: zero in a fresh workspace, set to kSgMark by
+// the first call.  Any other value means memory that was never zeroed: the
+// calls then write NaN outputs and leave the workspace alone instead of
+// reducing through stale counters (cheap: one load per work-group, waited
+// for only at the reduction).  Corruption of a zeroed workspace's counters
+// is not detected.
+constexpr unsigned kSgMark = 0x57344731u;
+constexpr size_t kSgHdrBytes = 256;
 
 // A row block shared by several work-groups is keyed by its index or by its
 // first owner, whichever set is smaller (a work-group is the first owner of
@@ -97,10 +107,10 @@ inline size_t sg_ctr_bytes(const SgGeom &g) {
     return (static_cast<size_t>(g.n_keys) * kSgCtrStride * 4 + 255) & ~size_t(255);
 }
 
-// Workspace: counters first, then the slots.
+// Workspace: the mark, the counters, then the slots.
 inline size_t sg_ws_bytes(int n_rb, int ng) {
     const SgGeom g = sg_geom(n_rb, ng);
-    return sg_ctr_bytes(g) + static_cast<size_t>(g.n_keys) * g.slot_stride * 64 * sizeof(double);
+    return kSgHdrBytes + sg_ctr_bytes(g) + static_cast<size_t>(g.n_keys) * g.slot_stride * 64 * sizeof(double);
 }
 
 __device__ __forceinline__ int sg_range_begin(int B, int T, int P) {
@@ -236,6 +246,8 @@ template <class Epi, bool kA8 = false, bool kExact = true>
 __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi) {
     __shared__ double red[kSgMaxRl * 256];
     const int B = blockIdx.x;
+    const unsigned mark = load_agent(p.hdr);   // used at the reduction
+    if (B == 0 && threadIdx.x == 0 && mark == 0u) store_agent(p.hdr, kSgMark);
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int t_begin = sg_range_begin(B, p.T, p.P), t_end = sg_range_begin(B + 1, p.T, p.P);
     const int rb0 = t_begin / p.ng;
@@ -284,12 +296,17 @@ __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi)
     __syncthreads();
 
     // one wave per row block of the range
+    const bool dirty = __builtin_amdgcn_readfirstlane(mark) != 0u && __builtin_amdgcn_readfirstlane(mark) != kSgMark;
     for (int rl = wave; rl < n_rl; rl += 4) {
         const double *rr = red + rl * 256 + lane;
         const double v = ((rr[0] + rr[64]) + rr[128]) + rr[192];
         const int rb = rb0 + rl;
         const int a = rb * p.ng;
         const int row = rb * 64 + lane;
+        if (dirty) {   // a workspace that was never zeroed: visible failure
+            epi(row, lane, __builtin_nan(""));
+            continue;
+        }
         if (a >= t_begin && a + p.ng <= t_end) {
             epi(row, lane, v);
             continue;

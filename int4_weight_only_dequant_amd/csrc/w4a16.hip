@@ -163,8 +163,9 @@ static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const void *x,
     p.P = g.P;
     p.slot_stride = g.slot_stride;
     p.key_by_rb = g.key_by_rb;
-    p.ctr = static_cast<unsigned *>(ws);
-    p.slots = reinterpret_cast<double *>(static_cast<char *>(ws) + sg_ctr_bytes(g));
+    p.hdr = static_cast<unsigned *>(ws);
+    p.ctr = reinterpret_cast<unsigned *>(static_cast<char *>(ws) + kSgHdrBytes);
+    p.slots = reinterpret_cast<double *>(static_cast<char *>(ws) + kSgHdrBytes + sg_ctr_bytes(g));
     hipLaunchKernelGGL((sg_gemv_kernel<Epi, kA8, kExact>), dim3(g.P), dim3(kThreads), 0, s, p, epi);
     return hipGetLastError();
 }

@@ -30,6 +30,15 @@ def _dev(a):
     return torch.from_numpy(a).to(DEV)
 
 
+WS_MARK = 0x57344731   # the streaming GEMV's workspace mark (first word)
+
+
+def assert_ws_clean(ws):
+    """After calls: the mark set, everything after the 256-byte header zero."""
+    assert int(ws[:4].cpu().numpy().view(np.uint32)[0]) == WS_MARK, "workspace mark not set"
+    assert int(torch.count_nonzero(ws[256:])) == 0, "workspace not left zero"
+
+
 def _gpu_gemv(q, s, x):
     n, k = q.shape
     pq, ps = w4.pack_int4_weights(q, s)
@@ -106,7 +115,7 @@ def test_gemv_shared_workspace_across_shapes_left_zero():
         L.check(lib.w4a16_gemv(dq.data_ptr(), ds.data_ptr(), dx.data_ptr(), y.data_ptr(), n, k,
                                ws.data_ptr(), ws.numel(), st))
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
+        assert_ws_clean(ws)
         fresh = w4.w4a16_gemv(dq, ds, dx, n, k).clone()
         torch.cuda.synchronize()
         assert torch.equal(y, fresh)
@@ -114,6 +123,32 @@ def test_gemv_shared_workspace_across_shapes_left_zero():
 
 
 # ------------------------------------------------------------------ MLP ----
+
+def test_gemv_workspace_never_zeroed_gives_nan():
+    """Memory that was never zeroed (its first word neither 0 nor the mark)
+    is refused visibly: y is all NaN and the workspace is left as it was;
+    once zeroed, the same call is correct."""
+    n, k = 3584, 3584
+    say(f"case: gemv N={n} K={k} on a workspace of 0xAB bytes")
+    q, s, x = synth.gemv_case(n, k, cfg=95)
+    pq, ps = w4.pack_int4_weights(q, s)
+    dq, ds, dx = _dev(pq), _dev(ps), _dev(x)
+    lib = L.lib()
+    ws = torch.full((lib.w4_gemv_ws_bytes(n, k),), 0xAB, dtype=torch.uint8, device=DEV)
+    y = torch.empty(n, dtype=torch.float16, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    L.check(lib.w4a16_gemv(dq.data_ptr(), ds.data_ptr(), dx.data_ptr(), y.data_ptr(), n, k, ws.data_ptr(),
+                           ws.numel(), st))
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(y.float()).all()), "a never-zeroed workspace must give NaN outputs"
+    assert bool((ws == 0xAB).all()), "a refused workspace is left untouched"
+    ws.zero_()
+    L.check(lib.w4a16_gemv(dq.data_ptr(), ds.data_ptr(), dx.data_ptr(), y.data_ptr(), n, k, ws.data_ptr(),
+                           ws.numel(), st))
+    torch.cuda.synchronize()
+    assert_gemv(y.cpu().numpy(), oracle.gemv(q, s, x), "after zeroing")
+    assert_ws_clean(ws)
+
 
 def test_mlp_cfg1():
     say("case: mlp cfg1 d=3584 f=18944")
@@ -180,7 +215,7 @@ def test_mlp_shapes_and_workspace_reuse(d, f):
         h, y = _mlp_raw(ops, d, f, ws)
         assert np.array_equal(h.view(np.uint16), h0.view(np.uint16)), f"call {i + 2}: h differs"
         assert np.array_equal(y.view(np.uint16), y0.view(np.uint16)), f"call {i + 2}: y differs"
-    assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero"
+    assert_ws_clean(ws)
 
 
 # ------------------------------------------------------------ attention ----
