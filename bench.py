@@ -55,11 +55,50 @@ TRAFFIC_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_traffic.md")
 STATS_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_persistent_kernel_stats.md")
 PREFILL_MD = os.path.join(HERE, "profiles", "prefill_qwen7b_512_kernel_stats.md")
 KERNEL = "decode_persistent_kernel"
+
+
+def _a8_kernel(name: str) -> bool:
+    """The int8-activation instantiation of the persistent kernel (kA8 = true)."""
+    return KERNEL in name and ("<true>" in name or "ILb1E" in name)
+
+
+def _f16_kernel(name: str) -> bool:
+    return KERNEL in name and not _a8_kernel(name)
 CALIB_BYTES = 256 << 20        # device-to-device copy used to calibrate the byte counters
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def _profile_open(path: str):
+    """Open a profiles/ summary for writing; a copy also lands in
+    gpurun_out/profiles/ when that folder exists (results written on a remote
+    machine come back only from there)."""
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+
+    class _Both:
+        def __init__(self):
+            self.fh = open(path, "w")
+            out = os.path.join(HERE, "gpurun_out")
+            self.copy = None
+            if os.path.isdir(out):
+                os.makedirs(os.path.join(out, "profiles"), exist_ok=True)
+                self.copy = open(os.path.join(out, "profiles", os.path.basename(path)), "w")
+
+        def write(self, text):
+            self.fh.write(text)
+            if self.copy:
+                self.copy.write(text)
+
+        def __enter__(self):
+            return self
+
+        def __exit__(self, *exc):
+            self.fh.close()
+            if self.copy:
+                self.copy.close()
+    return _Both()
 
 
 def source_hash() -> str:
@@ -273,25 +312,36 @@ def _pmc_rows(path):
     return rows
 
 
-def measure_traffic(out_dir: str):
-    """Two rocprofv3 --pmc runs of the traffic probe; writes TRAFFIC_MD."""
-    res = {}
-    cmds = []
-    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-        d = os.path.join(out_dir, f"pmc_{ctr.lower()}")
-        cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "pmc", "--",
+def _traffic_cmd(out_dir: str, ctr: str):
+    d = os.path.join(out_dir, f"pmc_{ctr.lower()}")
+    return d, ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "pmc", "--",
                sys.executable, "-u", os.path.join(HERE, "bench.py"), "--traffic-probe"]
-        cmds.append(" ".join(cmd[:-4] + ["python3", "-u", "bench.py", "--traffic-probe"]))
+
+
+def measure_traffic(out_dir: str):
+    """Two rocprofv3 --pmc runs of the traffic probe, then summarize_traffic."""
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        _, cmd = _traffic_cmd(out_dir, ctr)
         log("[bench] " + " ".join(cmd))
         env = dict(os.environ, TMPDIR="/tmp")
         r = subprocess.run(cmd, env=env, timeout=600)
         if r.returncode != 0:
             sys.exit(f"rocprofv3 {ctr} run failed ({r.returncode})")
+    summarize_traffic(out_dir)
+
+
+def summarize_traffic(out_dir: str):
+    """Counter files of measure_traffic's two runs -> TRAFFIC_MD."""
+    res = {}
+    cmds = []
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d, cmd = _traffic_cmd(out_dir, ctr)
+        cmds.append(" ".join(cmd[:-4] + ["python3", "-u", "bench.py", "--traffic-probe"]))
         files = glob.glob(os.path.join(d, "**", "pmc_counter_collection.csv"), recursive=True)
         if not files:
             sys.exit(f"no counter file under {d}")
         rows = _pmc_rows(files[0])
-        kern = [float(r["Counter_Value"]) for r in rows if KERNEL in r["Kernel_Name"] and r["Counter_Name"] == ctr]
+        kern = [float(r["Counter_Value"]) for r in rows if _f16_kernel(r["Kernel_Name"]) and r["Counter_Name"] == ctr]
         copy = [float(r["Counter_Value"]) for r in rows
                 if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
         if len(kern) < 16 or not copy:
@@ -328,7 +378,7 @@ def measure_traffic(out_dir: str):
         "still hash to `source_hash`.", "",
         "traffic-json: " + json.dumps(rec), ""]
     os.makedirs(os.path.dirname(TRAFFIC_MD), exist_ok=True)
-    with open(TRAFFIC_MD, "w") as fh:
+    with _profile_open(TRAFFIC_MD) as fh:
         fh.write("\n".join(lines))
     print(json.dumps(rec), flush=True)
 
@@ -342,9 +392,11 @@ def summarize_trace(d: str, steps: int, cmd: str):
     if not stats or not trace:
         sys.exit(f"no rocprofv3 csv files under {d}")
     rows = list(csv.DictReader(open(stats[0])))
-    tr = [r for r in csv.DictReader(open(trace[0])) if KERNEL in r["Kernel_Name"]]
-    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    all_tr = sorted(csv.DictReader(open(trace[0])), key=lambda r: int(r["Start_Timestamp"]))
+    tr = [r for r in all_tr if _f16_kernel(r["Kernel_Name"])]
+    tr8 = [r for r in all_tr if _a8_kernel(r["Kernel_Name"])]
     dur = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr], dtype=np.float64) / 1e3
+    dur8 = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr8], dtype=np.float64) / 1e3
     lines = ["# rocprofv3 kernel statistics: persistent decode step", "",
              "Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | total ms | % |", "|---|---:|---:|---:|---:|---:|---:|"]
@@ -359,8 +411,11 @@ def summarize_trace(d: str, steps: int, cmd: str):
               f"{dur[-steps:].mean():.1f} us (min {dur[-steps:].min():.1f}, max {dur[-steps:].max():.1f}).", "",
               "The earlier dispatches are the teacher-forced prompt (contexts 1-512, 16 of them eager",
               "launches) and the warmup; the kernel-per-op rows are the timing-hook replays of that variant.", ""]
+    if len(dur8):
+        lines += [f"The int8-activation instantiation (`W4_A8`, timed after the fp16 steps): {len(dur8)} dispatches, "
+                  f"mean {dur8.mean():.1f} us (min {dur8.min():.1f}, max {dur8.max():.1f}).", ""]
     os.makedirs(os.path.dirname(STATS_MD), exist_ok=True)
-    with open(STATS_MD, "w") as fh:
+    with _profile_open(STATS_MD) as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -406,7 +461,8 @@ def summarize_prefill_trace(d: str, cmd: str):
         tf = flops[k] / (m * 1e-6) / 1e12
         out.append(f"| {k} | {m:.1f} | {tf:.0f} | {tf / MFMA_F16_PEAK_TFLOPS:.3f} |")
     os.makedirs(os.path.dirname(PREFILL_MD), exist_ok=True)
-    open(PREFILL_MD, "w").write("\n".join(out) + "\n")
+    with _profile_open(PREFILL_MD) as fh:
+        fh.write("\n".join(out) + "\n")
     print("\n".join(out))
 
 
@@ -575,7 +631,7 @@ def phase_trace(write_md: bool = True):
     for ln in lines:
         log(ln)
     if write_md:
-        with open(TRACE_MD, "w") as fh:
+        with _profile_open(TRACE_MD) as fh:
             fh.write("# Phase timeline of the persistent decode kernel (Qwen2.5-7B shape, context 520)\n\n")
             fh.write("Command (from the repository root on one MI355X, after `python -m "
                      "int4_weight_only_dequant_amd.build --trace` on the build host):\n\n")
@@ -671,7 +727,7 @@ def launch_study(args):
                "kernel_per_op_graph_over_persistent_graph": round(fused, 2),
                "pages_eager_over_graph": round(PAGES_EAGER_MS / PAGES_GRAPH_MS, 2)}
     print(json.dumps({"launch_study": summary}), flush=True)
-    with open(LAUNCH_MD, "w") as fh:
+    with _profile_open(LAUNCH_MD) as fh:
         fh.write("# Eager launches vs graph replay of the decode step (Qwen2.5-7B shape)\n\n")
         fh.write("Command (from the repository root on one MI355X):\n\n")
         fh.write(f"```\npython3 -u bench.py --launch-study --steps {args.steps}\n```\n\n")
@@ -737,7 +793,7 @@ def summarize_standalone_trace(d: str, cmd: str):
                    else "paged_attn_decode ctx 8192"].append(t)
         elif "a8_quantize" in name:
             groups["w4a8_quantize_act"].append(t)
-        elif "true" in name:
+        elif "EpiStoreF16, true" in name:   # the int8-activation GEMV
             a8_grids.append((grid, t))
         elif "SwiGLU" in name:
             groups["w4a16_mlp: gate+up with SwiGLU"].append(t)
@@ -784,7 +840,7 @@ def summarize_standalone_trace(d: str, cmd: str):
                          f"{B[k] / m / 1e3:.0f} | {B[k] / m / 1e3 / HBM_PEAK_GBS:.3f} |")
         else:
             lines.append(f"| {k} | {len(v)} | {m:.2f} | {srt[len(srt) // 2]:.2f} | {srt[0]:.2f} | - | - | - |")
-    with open(SA_MD, "w") as fh:
+    with _profile_open(SA_MD) as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -1001,6 +1057,7 @@ def main():
                     help="phase timestamps of the persistent kernel (needs the trace build)")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--measure-traffic", metavar="OUT_DIR")
+    ap.add_argument("--summarize-traffic", metavar="OUT_DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--trace-command", default="")
     ap.add_argument("--summarize-prefill-trace", metavar="DIR")
@@ -1015,6 +1072,8 @@ def main():
         return traffic_probe()
     if args.measure_traffic:
         return measure_traffic(args.measure_traffic)
+    if args.summarize_traffic:
+        return summarize_traffic(args.summarize_traffic)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args.steps, args.trace_command)
     if args.summarize_prefill_trace:
