@@ -110,9 +110,9 @@ w4_status w4_pack_f16_matrix(const uint16_t *w, int64_t N, int64_t K,
  * W4A16 GEMV  ([TS] "Engineering Challenges" item 3, the fp16-activation
  * path: int4 weights unpacked on the fly, fp16 activations, no activation
  * quantisation).  y[r] = fp16( sum_k W[r][k] * x[k] ) for packed rows
- * r < N: every 8 consecutive products summed with correctly rounded fp32
- * operations (pair sums, then two adds), those 8-term sums and the groups
- * added in fp64.
+ * r < N: every 8 consecutive products summed in fp32 as two 4-term chains
+ * (each product exact; one fp32 addition per 4 terms may be off by up to one
+ * ulp), those 8-term sums and the groups added in fp64.
  *
  *   packed_q, packed_s : device, from pack_int4_weights (any row_perm; y is
  *                        in packed row order)

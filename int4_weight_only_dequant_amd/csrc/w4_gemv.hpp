@@ -88,27 +88,28 @@ __device__ __forceinline__ void dot8v(uint32_t w, const uint32_t (&xs)[4], float
 }
 
 // A pair sum a.x b.x + a.y b.y from a zero accumulator: correctly rounded
-// (the same measurement: every sum but 13 in 2^20 random ones).  The result
-// passes through an empty asm: otherwise the compiler folds an addition of two
-// such sums back into a chained accumulation.  Kept as the builtin, not an asm
-// dot: the compiler then spaces a dot's result from its reader by the wait
-// states the hardware needs, which it cannot do for an instruction hidden in
-// asm (an asm dot read one instruction later returned the previous contents of
-// its destination).
-__device__ __forceinline__ float dot2z(h2 a, h2 b) {
-    float r = __builtin_amdgcn_fdot2(a, b, 0.0f, false);
-    asm volatile("" : "+v"(r));
-    return r;
-}
+// (the same measurement: every sum but 13 in 2^20 random ones).  Kept as the
+// builtin, not an asm dot: the compiler then spaces a dot's result from its
+// reader by the wait states the hardware needs, which it cannot do for an
+// instruction hidden in asm (an asm dot read one instruction later returned
+// the previous contents of its destination).
+__device__ __forceinline__ float dot2z(h2 a, h2 b) { return __builtin_amdgcn_fdot2(a, b, 0.0f, false); }
 
-// The 8 products of dot8v summed without the chained-accumulator error: four
-// correctly rounded pair sums, added with IEEE fp32 adds; callers add these
-// 8-term sums in fp64.  A group's error then stays at the unbiased rounding of
-// 8-term sums.  Used where activations are large (attention output, SwiGLU
-// output of 10^2 and more), so that outputs near zero stay within the GEMV
-// tolerance: 18 VALU operations per 8 weights instead of 13.
-__device__ __forceinline__ float dot8v_exact(uint32_t w, const uint32_t (&xs)[4], uint32_t m_lo, uint32_t m_hi,
+// The 8 products of dot8v as one short sum for the caller to add in fp64: two
+// 4-term chains (a pair sum from zero, then one accumulating dot) added with
+// an IEEE fp32 add.  The accumulator's truncation then touches one addition
+// per 4 terms instead of a whole group's chain, so a group's error stays at
+// the rounding of 8-term sums, unbiased in practice.  Used where activations
+// are large (attention output, SwiGLU output of 10^2 and more), so that
+// outputs near zero stay within the GEMV tolerance: 18 VALU operations per 8
+// weights instead of 13 (each chain needs its zeroed accumulator; the fp64
+// conversion and add).  (Four correctly rounded pair sums added in fp32 were
+// as accurate on the layer tests and 2.4% slower per decode step.)
+// Contraction is off here: with it the compiler folds the final add into a
+// chained accumulation.
+__device__ __forceinline__ float dot8v_short(uint32_t w, const uint32_t (&xs)[4], uint32_t m_lo, uint32_t m_hi,
                                              uint32_t magic, uint32_t magic_hi) {
+#pragma clang fp contract(off)
     const h2 k1032 = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
     const h2 k72 = {static_cast<_Float16>(72.0f), static_cast<_Float16>(72.0f)};
     const uint32_t w8 = w >> 8;
@@ -116,9 +117,9 @@ __device__ __forceinline__ float dot8v_exact(uint32_t w, const uint32_t (&xs)[4]
     const h2 q23 = as_h2((w & m_hi) | magic_hi) - k72;
     const h2 q45 = as_h2((w8 & m_lo) | magic) - k1032;
     const h2 q67 = as_h2((w8 & m_hi) | magic_hi) - k72;
-    const float p0 = dot2z(q01, as_h2(xs[0])), p1 = dot2z(q23, as_h2(xs[1]));
-    const float p2 = dot2z(q45, as_h2(xs[2])), p3 = dot2z(q67, as_h2(xs[3]));
-    return (p0 + p1) + (p2 + p3);
+    const float pa = __builtin_amdgcn_fdot2(q45, as_h2(xs[2]), dot2z(q01, as_h2(xs[0])), false);
+    const float pb = __builtin_amdgcn_fdot2(q67, as_h2(xs[3]), dot2z(q23, as_h2(xs[1])), false);
+    return pa + pb;
 }
 
 // Sum over the work-group's 4 waves of one fp64 value per lane; result valid

@@ -143,12 +143,12 @@ __device__ __forceinline__ double sg_tile(const u32x4 (&w)[4], uint16_t s, const
     return static_cast<double>(acc1 + acc2) * static_cast<double>(f16_to_f32(s));
 }
 
-// One tile's scaled group sum from correctly rounded 8-term sums added in
-// fp64 (dot8v_exact), x from SGPRs.  The streaming GEMV's default: its x is
-// any caller's vector (the MLP's down projection reads h of magnitude 10^2 and
+// One tile's scaled group sum from short 8-term sums added in fp64
+// (dot8v_short), x from SGPRs.  The streaming GEMV's default: its x is any
+// caller's vector (the MLP's down projection reads h of magnitude 10^2 and
 // more), and the relative bound near outputs much smaller than their terms
-// needs the exact sums there (about 30% more VALU work per tile).
-__device__ __forceinline__ double sg_tile_exact(const u32x4 (&w)[4], uint16_t s, const_u32_ptr xg, uint32_t m_lo,
+// needs the short sums there (about 30% more VALU work per tile).
+__device__ __forceinline__ double sg_tile_short(const u32x4 (&w)[4], uint16_t s, const_u32_ptr xg, uint32_t m_lo,
                                                 uint32_t m_hi, uint32_t magic, uint32_t magic_hi) {
     double gs = 0.0;
 #pragma unroll
@@ -158,7 +158,7 @@ __device__ __forceinline__ double sg_tile_exact(const u32x4 (&w)[4], uint16_t s,
         for (int j = 0; j < 4; ++j) {
             const uint32_t xs[4] = {xg[c * 16 + j * 4 + 0], xg[c * 16 + j * 4 + 1], xg[c * 16 + j * 4 + 2],
                                     xg[c * 16 + j * 4 + 3]};
-            gs += static_cast<double>(dot8v_exact(ws4[j], xs, m_lo, m_hi, magic, magic_hi));
+            gs += static_cast<double>(dot8v_short(ws4[j], xs, m_lo, m_hi, magic, magic_hi));
         }
     }
     return gs * static_cast<double>(f16_to_f32(s));
@@ -240,9 +240,10 @@ __device__ __forceinline__ double sg_tile_a8(const u32x4 (&w)[4], uint16_t s, co
     return static_cast<double>(f16_to_f32(s)) * static_cast<double>(sx) * static_cast<double>(dot);
 }
 
-// kExact: exact 8-term sums (sg_tile_exact); off only where the activations
-// are O(1) by construction (the MLP's normalised gate/up input).
-template <class Epi, bool kA8 = false, bool kExact = true>
+// kShort: short 8-term sums added in fp64 (sg_tile_short); off only where
+// the activations are O(1) by construction (the MLP's normalised gate/up
+// input), which takes one fp32 chain per group.
+template <class Epi, bool kA8 = false, bool kShort = true>
 __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi) {
     __shared__ double red[kSgMaxRl * 256];
     const int B = blockIdx.x;
@@ -277,8 +278,8 @@ __global__ __launch_bounds__(kThreads) void sg_gemv_kernel(SgProblem p, Epi epi)
             acc += sg_tile_a8(w, s, xc + g * 32, __builtin_bit_cast(float, aux[p.a8_scales / 4 + g]),
                               static_cast<int>(aux[p.a8_sums / 4 + g]));
         } else {
-            if constexpr (kExact)
-                acc += sg_tile_exact(w, s, xc + g * 64, m_lo, m_hi, magic, magic_hi);
+            if constexpr (kShort)
+                acc += sg_tile_short(w, s, xc + g * 64, m_lo, m_hi, magic, magic_hi);
             else
                 acc += sg_tile(w, s, xc + g * 64, m_lo, m_hi, magic, magic_hi);
         }

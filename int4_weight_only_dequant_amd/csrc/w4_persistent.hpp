@@ -236,7 +236,7 @@ struct Part {
 #endif
 // weights (first half, second half) per phase kind: QKV, O, gate+up, down
 // (QKV and O have fewer than 4 tiles per work-group and use equal ranges).
-// Measured with the exact O/down arithmetic (us per step): gate+up 2:1 and
+// Measured with 8-term pair sums in O and down (us per step): gate+up 2:1 and
 // down 2:1 1572, 5:2 and 3:2 1581, 5:2 and 1:1 1600, 3:1 and 1:1 1628.
 constexpr int kPkWeights[4][2] = {{1, 1}, {1, 1}, {W4_PK_W_GU}, {W4_PK_W_D}};
 __host__ __device__ inline Part make_part(int T, int P, int wa, int wb) {
@@ -640,10 +640,10 @@ __device__ __forceinline__ bool pk_reduce(const PKParams &p, int rb, int nk, int
 
 // int4 tile loop of one wave: its tiles rg.b + wave + 4k, consuming the ring
 // (already holding the first tiles) and refilling it; per-row-block sums are
-// parked in red[rl][wave][lane].  kExact: the correctly rounded 8-term sums
+// parked in red[rl][wave][lane].  kShort: short 8-term sums added in fp64
 // (the O and down projections, whose inputs are large), else the chained
 // fp32 accumulation.
-template <bool kExact>
+template <bool kShort>
 __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_t *ws, int ng, Range rg,
                                          bool whole, int rb0, const uint16_t *lds, double *red) {
     const uint32_t m_lo = vreg_const(0x000F000Fu), m_hi = vreg_const(0x00F000F0u), magic = vreg_const(0x64006400u), magic_hi = vreg_const(0x54005400u);
@@ -666,7 +666,7 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
                 }
                 const u32x4 *xl = reinterpret_cast<const u32x4 *>(lds + (whole ? t % ng : i) * 128);
                 double gs;
-                if constexpr (kExact) {
+                if constexpr (kShort) {
                     gs = 0.0;
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
@@ -675,10 +675,10 @@ __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_
                         const uint32_t xb[4] = {x1.x, x1.y, x1.z, x1.w};
                         const uint32_t xc[4] = {x2.x, x2.y, x2.z, x2.w};
                         const uint32_t xd[4] = {x3.x, x3.y, x3.z, x3.w};
-                        gs += static_cast<double>(dot8v_exact(r.w[s][c].x, xa, m_lo, m_hi, magic, magic_hi));
-                        gs += static_cast<double>(dot8v_exact(r.w[s][c].y, xb, m_lo, m_hi, magic, magic_hi));
-                        gs += static_cast<double>(dot8v_exact(r.w[s][c].z, xc, m_lo, m_hi, magic, magic_hi));
-                        gs += static_cast<double>(dot8v_exact(r.w[s][c].w, xd, m_lo, m_hi, magic, magic_hi));
+                        gs += static_cast<double>(dot8v_short(r.w[s][c].x, xa, m_lo, m_hi, magic, magic_hi));
+                        gs += static_cast<double>(dot8v_short(r.w[s][c].y, xb, m_lo, m_hi, magic, magic_hi));
+                        gs += static_cast<double>(dot8v_short(r.w[s][c].z, xc, m_lo, m_hi, magic, magic_hi));
+                        gs += static_cast<double>(dot8v_short(r.w[s][c].w, xd, m_lo, m_hi, magic, magic_hi));
                     }
                 } else {
                     float a1 = 0.f, a2 = 0.f;

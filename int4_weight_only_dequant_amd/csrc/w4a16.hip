@@ -147,7 +147,7 @@ static bool sg_shape_ok(int64_t N, int64_t K) {
     return N >= 1 && K >= kGroup && K % kGroup == 0 && ((N + 63) / 64) * (K / kGroup) < (int64_t(1) << 31);
 }
 
-template <class Epi, bool kA8 = false, bool kExact = true>
+template <class Epi, bool kA8 = false, bool kShort = true>
 static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const void *x, int64_t N, int64_t K,
                             void *ws, const Epi &epi, hipStream_t s) {
     const int n_rb = static_cast<int>((N + 63) / 64), ng = static_cast<int>(K / kGroup);
@@ -166,7 +166,7 @@ static hipError_t launch_sg(const uint8_t *q, const uint16_t *sc, const void *x,
     p.hdr = static_cast<unsigned *>(ws);
     p.ctr = reinterpret_cast<unsigned *>(static_cast<char *>(ws) + kSgHdrBytes);
     p.slots = reinterpret_cast<double *>(static_cast<char *>(ws) + kSgHdrBytes + sg_ctr_bytes(g));
-    hipLaunchKernelGGL((sg_gemv_kernel<Epi, kA8, kExact>), dim3(g.P), dim3(kThreads), 0, s, p, epi);
+    hipLaunchKernelGGL((sg_gemv_kernel<Epi, kA8, kShort>), dim3(g.P), dim3(kThreads), 0, s, p, epi);
     return hipGetLastError();
 }
 
