@@ -118,7 +118,11 @@ def check_step(model, dims, layer_fn, glob, pos, layers, report):
     kc = model.k_cache.cpu().numpy().reshape(kv_shape)
     vc = model.v_cache.cpu().numpy().reshape(kv_shape)
     phys, slot = int(pt[pos // 16]), pos % 16
-    worst = {"gemv": 0.0, "attn": 0.0, "f16_off": 0}
+    worst = {"gemv": 0.0, "gemv_op": "", "attn": 0.0, "f16_off": 0}
+
+    def gemv_seen(e, what):
+        if e > worst["gemv"]:
+            worst["gemv"], worst["gemv_op"] = e, what
     for l in layers:
         lw = layer_fn(l)
         A = acc_all[l * lay.acc_layer:(l + 1) * lay.acc_layer].astype(np.float64) * scale_fix
@@ -129,8 +133,7 @@ def check_step(model, dims, layer_fn, glob, pos, layers, report):
         worst["f16_off"] += assert_f16_close(a, oracle.f16(oracle.rmsnorm(x_in, lw.ln1, dims.eps)), f"layer {l} norm1")
         # QKV GEMV (bias added by the consumers)
         qkv = unperm(perm_qkv, A[lay.acc_q:lay.acc_q + qkv_rows])
-        e = assert_gemv(qkv, oracle.gemv(*lw.qkv, a), f"layer {l} qkv")
-        worst["gemv"] = max(worst["gemv"], e)
+        gemv_seen(assert_gemv(qkv, oracle.gemv(*lw.qkv, a), f"layer {l} qkv"), f"layer {l} qkv")
         y = qkv + lw.bqkv.astype(np.float64)
         q = oracle.f16(oracle.rope(y[:qd].reshape(dims.n_q_heads, -1), pos, dims.theta))
         k = oracle.f16(oracle.rope(y[qd:qd + kd].reshape(dims.n_kv_heads, -1), pos, dims.theta))
@@ -149,18 +152,18 @@ def check_step(model, dims, layer_fn, glob, pos, layers, report):
         worst["attn_f16_off"] = worst.get("attn_f16_off", 0) + int(np.count_nonzero(f16_ulps(o_in, oracle.f16(o_ref))))
         # O GEMV and the residual add
         o_out = A[lay.acc_o:lay.acc_o + d]
-        worst["gemv"] = max(worst["gemv"], assert_gemv(o_out, oracle.gemv(*lw.o, o_in), f"layer {l} O"))
+        gemv_seen(assert_gemv(o_out, oracle.gemv(*lw.o, o_in), f"layer {l} O"), f"layer {l} O")
         want_xo = (x_in.astype(np.float64) + o_out).astype(np.float32)
         assert np.array_equal(xo.view(np.uint32), want_xo.view(np.uint32)), f"layer {l} residual after O"
         # pre-MLP RMSNorm, gate/up, SwiGLU, down, residual
         worst["f16_off"] += assert_f16_close(a2, oracle.f16(oracle.rmsnorm(xo, lw.ln2, dims.eps)), f"layer {l} norm2")
         gu = unperm(perm_gu, A[lay.acc_gu:lay.acc_gu + 2 * f])
         g, u = gu[:f], gu[f:]
-        worst["gemv"] = max(worst["gemv"], assert_gemv(g, oracle.gemv(*lw.gate, a2), f"layer {l} gate"))
-        worst["gemv"] = max(worst["gemv"], assert_gemv(u, oracle.gemv(*lw.up, a2), f"layer {l} up"))
+        gemv_seen(assert_gemv(g, oracle.gemv(*lw.gate, a2), f"layer {l} gate"), f"layer {l} gate")
+        gemv_seen(assert_gemv(u, oracle.gemv(*lw.up, a2), f"layer {l} up"), f"layer {l} up")
         worst["f16_off"] += assert_f16_close(h, oracle.f16(oracle.swiglu(g, u)), f"layer {l} swiglu")
         dn = A[lay.acc_d:lay.acc_d + d]
-        worst["gemv"] = max(worst["gemv"], assert_gemv(dn, oracle.gemv(*lw.down, h), f"layer {l} down"))
+        gemv_seen(assert_gemv(dn, oracle.gemv(*lw.down, h), f"layer {l} down"), f"layer {l} down")
         want_xd = (xo.astype(np.float64) + dn).astype(np.float32)
         assert np.array_equal(xd.view(np.uint32), want_xd.view(np.uint32)), f"layer {l} residual after down"
         del lw
