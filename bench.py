@@ -569,7 +569,7 @@ def phase_trace(write_md: bool = True):
     torch.cuda.synchronize()
     assert model.device_error() == 0
     P, n_ph = model.grid(), 4 * dims.n_layers + 1
-    tr = np.zeros((P, n_ph, 10), dtype=np.uint64)
+    tr = np.zeros((P, n_ph, 8), dtype=np.uint64)
     L.check(lib.w4_model_trace_copy(model._m, tr.ctypes.data, tr.nbytes))
     pos = model.pos - 1
     model.close()
@@ -611,9 +611,8 @@ def phase_trace(write_md: bool = True):
                 sig_last[ph] - prev,                # phase span (last signal to last signal)
             ])
             if kind == 1:
-                a0, a1, a2, a3 = us[:, ph, 5], us[:, ph, 6], us[:, ph, 7], us[:, ph, 8]
-                att.append([med(a1 - a0), mx(a1) - sig_last[ph - 1], mx(a1) - med(a1),
-                            med(a2) - sig_last[ph - 1], med(a3 - a2), med(a1 - a3)])
+                a0, a1 = us[:, ph, 5], us[:, ph, 6]
+                att.append([med(a1 - a0), mx(a1) - sig_last[ph - 1], mx(a1) - med(a1)])
     hdr = ("| phase | producer's last signal -> median wait passed (us) | staging (us) | wave 0 tiles (us) | "
            "reduce + signal (us) | median -> last signal (us) | span, last signal to last signal (us) |")
     lines = [hdr, "|---|---:|---:|---:|---:|---:|---:|"]
@@ -627,10 +626,7 @@ def phase_trace(write_md: bool = True):
     summary = {"position": pos, "grid": P, "kernel_us": round((t_end - t0) / 100.0, 1),
                "layer0_us": round(first, 2), "per_layer_us": round(per_layer, 2), "lm_head_us": round(lm, 2),
                "attention_unit_us": round(float(a[0]), 2),
-               "attention_last_publish_after_qkv_us": round(float(a[1]), 2),
-               "attention_staged_after_qkv_us": round(float(a[3]), 2),
-               "attention_pages_us": round(float(a[4]), 2),
-               "attention_merge_publish_us": round(float(a[5]), 2)}
+               "attention_last_publish_after_qkv_us": round(float(a[1]), 2)}
     log(f"[trace] {json.dumps(summary)}")
     for ln in lines:
         log(ln)

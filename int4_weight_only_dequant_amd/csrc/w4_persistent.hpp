@@ -138,9 +138,7 @@ enum {
     kTrSignal = 4,     // accumulators added and completion signalled
     kTrAttBegin = 5,   // attention work-groups: attention started
     kTrAttEnd = 6,     // attention work-groups: chunk published
-    kTrAttStaged = 7,  // attention work-groups: QKV wait passed, query staged
-    kTrAttDone = 8,    // attention work-groups: wave 0's pages done (before the merge)
-    kTraceSlots = 10
+    kTraceSlots = 8
 };
 #ifdef W4_PK_TRACE
 #define PK_STAMP(ph, k)                                                                                   \
@@ -1002,7 +1000,7 @@ __device__ __forceinline__ void att_load(const PKParams &p, const_layer_ptr L, i
 __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr L, const unsigned *q_done,
                                              const long long *acc_q, float *att_part, unsigned *head_cnt, int h,
                                              int c, int n_split, int ctx, int phys, float *s_att, uint16_t *s_qkv,
-                                             int code, int ph) {
+                                             int code) {
     const int lane = opaque_tid() & 63, wave = wave_id();
     const int ts = lane >> 4, dc = lane & 15;
     const int G = p.n_qh / p.n_kvh, j = h / G;
@@ -1021,7 +1019,6 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
     uint16_t *sq = s_qkv, *sk = s_qkv + 128, *sv = s_qkv + 256;
     qkv_to_lds(p, acc_q, L->qkv_b, h, j, pos, last_chunk, sq, sk, sv);
     __syncthreads();
-    PK_STAMP(ph, kTrAttStaged);
     const u32x4 qv = *reinterpret_cast<const u32x4 *>(sq + dc * 8);
     u32x4 knew{}, vnew{};
     if (has_cur) {
@@ -1089,7 +1086,6 @@ __device__ __forceinline__ bool pk_attention(const PKParams &p, const_layer_ptr 
             m = mn;
         }
     }
-    PK_STAMP(ph, kTrAttDone);
     // merge the 4 token rows of the wave (lanes 16 and 32 apart)
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
@@ -1404,7 +1400,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             PK_STAMP(ph, kTrAttBegin);
             ok = pk_attention(p, pk_layer(p, g.l), pk_grp_cnt(p, par, g.l, kPhQ), pk_acc(p, par, g.l, p.acc_q),
                               p.att_part + g.l * p.att_layer, pk_head_cnt(p, par, g.l), att_h, att_s, n_split, ctx,
-                              phys, reinterpret_cast<float *>(s_red), s_stage, 2000 + g.l, ph);
+                              phys, reinterpret_cast<float *>(s_red), s_stage, 2000 + g.l);
             PK_STAMP(ph, kTrAttEnd);
             if (!ok) break;
             prefetch_phase(ring, p, g);
