@@ -211,9 +211,10 @@ w4_status w4a16_mlp(const uint8_t *gu_q, const uint16_t *gu_s, const uint8_t *do
  * the pages time the first token of a 512-token prompt, [SP] "Technical
  * Specifications and Benchmarking Data", performance comparison table, and
  * [AI] "Summary", without describing the prefill).  Matrix cores
- * (MFMA 32x32x16 fp16), fp32 accumulation; within a group of 128 K the
- * integer codes meet the fp16 activations exactly and the group's scale is
- * applied in fp32, split-K partials are summed in fp64 in split order.
+ * (MFMA 32x32x16 fp16): within a group of 128 K the integer codes meet the
+ * fp16 activations exactly and the products are summed in fp32; each group
+ * sum times its fp16 scale is added in fp64; a split of the K groups stores
+ * its sum as fp32, and the splits are added in fp64 in split order.
  *   y[m][r] = sum_k x[m][k] * W[r][k]     for m < M, packed rows r < N
  *
  *   packed_q, packed_s : device, from pack_int4_weights (y is in packed row
