@@ -100,13 +100,13 @@ __device__ __forceinline__ float dot2z(h2 a, h2 b) { return __builtin_amdgcn_fdo
 // an IEEE fp32 add.  The accumulator's truncation then touches one addition
 // per 4 terms instead of a whole group's chain, so a group's error stays at
 // the rounding of 8-term sums, unbiased in practice.  Used where activations
-// are large (attention output, SwiGLU output of 10^2 and more), so that
-// outputs near zero stay within the GEMV tolerance: 18 VALU operations per 8
-// weights instead of 13 (each chain needs its zeroed accumulator; the fp64
-// conversion and add).  (Four correctly rounded pair sums added in fp32 were
-// as accurate on the layer tests and 2.4% slower per decode step.)
-// Contraction is off here: with it the compiler folds the final add into a
-// chained accumulation.
+// are large (SwiGLU output of 10^2 and more, any caller's vector in the
+// standalone GEMV), so that outputs near zero stay within the GEMV tolerance:
+// 18 VALU operations per 8 weights instead of 13 (each chain needs its zeroed
+// accumulator; the fp64 conversion and add).  Four correctly rounded pair
+// sums added in fp32 halved the worst layer-test error and cost 2.4% more per
+// decode step.  Contraction is off here: with it the compiler folds the final
+// add into a chained accumulation.
 __device__ __forceinline__ float dot8v_short(uint32_t w, const uint32_t (&xs)[4], uint32_t m_lo, uint32_t m_hi,
                                              uint32_t magic, uint32_t magic_hi) {
 #pragma clang fp contract(off)

@@ -236,7 +236,7 @@ struct Part {
 #endif
 // weights (first half, second half) per phase kind: QKV, O, gate+up, down
 // (QKV and O have fewer than 4 tiles per work-group and use equal ranges).
-// Measured with 8-term pair sums in O and down (us per step): gate+up 2:1 and
+// Measured with 8-term sums in O and down (us per step): gate+up 2:1 and
 // down 2:1 1572, 5:2 and 3:2 1581, 5:2 and 1:1 1600, 3:1 and 1:1 1628.
 constexpr int kPkWeights[4][2] = {{1, 1}, {1, 1}, {W4_PK_W_GU}, {W4_PK_W_D}};
 __host__ __device__ inline Part make_part(int T, int P, int wa, int wb) {
@@ -641,8 +641,10 @@ __device__ __forceinline__ bool pk_reduce(const PKParams &p, int rb, int nk, int
 // int4 tile loop of one wave: its tiles rg.b + wave + 4k, consuming the ring
 // (already holding the first tiles) and refilling it; per-row-block sums are
 // parked in red[rl][wave][lane].  kShort: short 8-term sums added in fp64
-// (the O and down projections, whose inputs are large), else the chained
-// fp32 accumulation.
+// (the down projection, whose inputs, SwiGLU outputs, reach 10^2 and more),
+// else one chained fp32 accumulation per group (QKV, O, gate+up: measured
+// within the GEMV tolerance on the layer tests; O's attention-output inputs
+// of up to about 30 gave 4.7e-4 at the 8192-token context against 2e-3).
 template <bool kShort>
 __device__ __forceinline__ void w4_tiles(Ring &r, const u32x4 *wq, const uint16_t *ws, int ng, Range rg,
                                          bool whole, int rb0, const uint16_t *lds, double *red) {
@@ -1436,7 +1438,7 @@ void decode_persistent_kernel(const PKParams *__restrict__ pp) {
             if (g.kind == kPhLM) f16_tiles(ring, p.lm, g.nk, rg, rb0, s_stage, s_red);
             else if (kA8)
                 w4_tiles_a8(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
-            else if (g.kind == kPhO || g.kind == kPhD)
+            else if (g.kind == kPhD)
                 w4_tiles<true>(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);
             else
                 w4_tiles<false>(ring, g.wq, g.ws, g.nk, rg, whole, rb0, s_stage, s_red);

@@ -123,6 +123,8 @@ def check_step(model, dims, layer_fn, glob, pos, layers, report):
     def gemv_seen(e, what):
         if e > worst["gemv"]:
             worst["gemv"], worst["gemv_op"] = e, what
+        kind = "gemv_" + what.split()[-1]          # worst per projection kind
+        worst[kind] = max(worst.get(kind, 0.0), e)
     for l in layers:
         lw = layer_fn(l)
         A = acc_all[l * lay.acc_layer:(l + 1) * lay.acc_layer].astype(np.float64) * scale_fix
