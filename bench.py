@@ -548,7 +548,7 @@ def long_context(args):
 TRACE_MD = os.path.join(HERE, "profiles", "decode_step_qwen7b_phase_trace.md")
 
 
-def phase_trace(write_md: bool = True):
+def phase_trace(write_md: bool = True, context: int = 512):
     import ctypes
     import torch
     import synth
@@ -561,11 +561,17 @@ def phase_trace(write_md: bool = True):
     lib.w4_model_trace_copy.restype = ctypes.c_int
     lib.w4_model_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     dims = synth.QWEN7B
-    n_prompt, n_extra = 512, 8
+    n_prompt, n_extra = context, 8
     model, _, _ = build_model(dims, n_prompt, n_extra)
     model.reset(synth.prompt_ids(dims, n_prompt))
-    for _ in range(n_prompt + n_extra):
-        model.step(L.W4_GRAPH)
+    if context == 512:
+        for _ in range(n_prompt + n_extra):
+            model.step(L.W4_GRAPH)
+    else:   # a long prompt goes through the prefill, as in the long-context workload
+        while model.pos < n_prompt - 1:
+            model.prefill(min(512, n_prompt - 1 - model.pos))
+        for _ in range(1 + n_extra):
+            model.step(L.W4_GRAPH)
     torch.cuda.synchronize()
     assert model.device_error() == 0
     P, n_ph = model.grid(), 4 * dims.n_layers + 1
@@ -631,11 +637,13 @@ def phase_trace(write_md: bool = True):
     for ln in lines:
         log(ln)
     if write_md:
-        with _profile_open(TRACE_MD) as fh:
-            fh.write("# Phase timeline of the persistent decode kernel (Qwen2.5-7B shape, context 520)\n\n")
+        md = TRACE_MD if context == 512 else TRACE_MD.replace(".md", f"_{context}.md")
+        with _profile_open(md) as fh:
+            fh.write(f"# Phase timeline of the persistent decode kernel (Qwen2.5-7B shape, context {pos + 1})\n\n")
             fh.write("Command (from the repository root on one MI355X, after `python -m "
                      "int4_weight_only_dequant_amd.build --trace` on the build host):\n\n")
-            fh.write("```\npython3 -u bench.py --phase-trace\n```\n\n")
+            fh.write("```\npython3 -u bench.py --phase-trace" + ("" if context == 512 else f" --context {context}")
+                     + "\n```\n\n")
             fh.write("The trace build records, in wave 0 of every work-group, the 100 MHz real-time counter "
                      "at the top of each phase, when its dependency wait passes, when its input is staged, "
                      "when wave 0's tiles are done and when the work-group's completion is signalled "
@@ -1085,7 +1093,7 @@ def main():
         launch_study(args)
         return None
     if args.phase_trace:
-        phase_trace()
+        phase_trace(context=args.context)
         return None
     if args.standalone_only:
         res = standalone_kernels()

@@ -536,9 +536,51 @@ __device__ __forceinline__ void stage_swiglu(uint16_t *lds, Range rg, int nk, in
     }
 }
 
+// Wave reductions by DPP within 16-lane rows, then lane reads across rows
+// (a fixed order: the results do not depend on timing).
+__device__ __forceinline__ int dpp_i32(int v, int ctrl_q) {
+    switch (ctrl_q) {   // the DPP control must be a constant
+        case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+        case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+        default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    }
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v = fmaxf(v, __builtin_bit_cast(float, dpp_i32(__builtin_bit_cast(int, v), c)));
+    const int b = __builtin_bit_cast(int, v);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v += dpp_i32(v, c);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v += __builtin_bit_cast(float, dpp_i32(__builtin_bit_cast(int, v), c));
+    const int b = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+
 // Attention output of the heads under the range's O-projection tiles (a
-// 128-element K group is one head): each wave merges one head's splits in
-// split order; lane holds dims 2 lane, 2 lane + 1.
+// 128-element K group is one head).  A wave per head: lane c holds chunk c's
+// (max, sum) (at most 64 chunks, host-checked), the wave takes the maximum
+// and each chunk's weight; every lane then adds the chunks' weighted sums for
+// its dims 2 lane, 2 lane + 1 in chunk order, kAttMergeBatch chunks' loads
+// in flight at once.  (Measured per step at context 520 and 8192: batches of
+// 24 1536/1780 us with 224 spilled SGPRs, 16 1480/1739, 8 1444/1720 with 59
+// and no spilled VGPRs; the former merge, every lane taking the weights of 16
+// chunks per batch itself, 1504/1863 with 20 spilled VGPRs.)
+constexpr int kAttMergeBatch = 8;
 __device__ __forceinline__ void stage_attn(uint16_t *lds, Range rg, int nk, const float *att_part, int att_smax,
                                            int n_split) {
     const bool whole = stage_whole(rg, nk);
@@ -547,36 +589,26 @@ __device__ __forceinline__ void stage_attn(uint16_t *lds, Range rg, int nk, cons
     for (int u = wave_id(); u < n_u; u += kPkWaves) {
         const int h = whole ? u : (rg.b + u) % nk;
         const float *hb = att_part + static_cast<size_t>(h) * att_smax * 132;
-        float M = -INFINITY, Ls = 0.f, A0 = 0.f, A1 = 0.f;
-        for (int s0 = 0; s0 < n_split; s0 += 16) {
-            float ms[16], ls[16], a0[16], a1[16];
+        float2 ml = make_float2(-INFINITY, 0.f);
+        if (lane < n_split) ml = *reinterpret_cast<const float2 *>(hb + lane * 132);
+        float A0 = 0.f, A1 = 0.f, w = 0.f, Ls = 0.f;
+        for (int s0 = 0; s0 < n_split; s0 += kAttMergeBatch) {
+            float2 aa[kAttMergeBatch];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                if (s0 + q < n_split) {
-                    const float *pp = hb + (s0 + q) * 132;
-                    const float2 ml = *reinterpret_cast<const float2 *>(pp);
-                    const float2 aa = *reinterpret_cast<const float2 *>(pp + 4 + 2 * lane);
-                    ms[q] = ml.x;
-                    ls[q] = ml.y;
-                    a0[q] = aa.x;
-                    a1[q] = aa.y;
-                }
+            for (int q = 0; q < kAttMergeBatch; ++q)
+                if (s0 + q < n_split) aa[q] = *reinterpret_cast<const float2 *>(hb + (s0 + q) * 132 + 4 + 2 * lane);
+            if (s0 == 0) {
+                const float M = wave_max_f32(ml.x);
+                w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+                Ls = wave_sum_f32(w * ml.y);
             }
-            // running rescale across batches (one batch at the usual contexts)
-            float Mb = M;
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-                if (s0 + q < n_split) Mb = fmaxf(Mb, ms[q]);
-            const float fr = M == -INFINITY ? 0.f : exp2f(M - Mb);
-            Ls *= fr; A0 *= fr; A1 *= fr;
-            M = Mb;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                if (s0 + q < n_split && ms[q] != -INFINITY) {
-                    const float f = exp2f(ms[q] - M);
-                    Ls += ls[q] * f;
-                    A0 += a0[q] * f;
-                    A1 += a1[q] * f;
+            for (int q = 0; q < kAttMergeBatch; ++q) {
+                if (s0 + q < n_split) {
+                    const float wq = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + q));
+                    A0 += wq * aa[q].x;
+                    A1 += wq * aa[q].y;
                 }
             }
         }
@@ -727,30 +759,6 @@ static_assert(kA8SumOff + kA8GroupsPerWave * kPkWaves * 4 <= kStageBytes, "int8 
 // Wave-wide max and sum: within each 16-lane row by DPP (as row16_sum),
 // then the four row results by readlane (a shuffle through LDS per step
 // measured about 4 us per phase on the step).
-__device__ __forceinline__ int dpp_i32(int v, int ctrl_q) {
-    switch (ctrl_q) {   // the DPP control must be a constant
-        case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
-        case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
-        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
-        default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
-    }
-}
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) v = fmaxf(v, __builtin_bit_cast(float, dpp_i32(__builtin_bit_cast(int, v), c)));
-    const int b = __builtin_bit_cast(int, v);
-    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
-                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
-                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
-                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
-}
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) v += dpp_i32(v, c);
-    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
-           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
-}
-
 // ng staged groups of 128 fp16 (group u at element 128 u), in place; wave w
 // takes groups w, w + 4, ...; lane holds elements 2 lane, 2 lane + 1.  All
 // reads finish before the barrier, all writes come after it (the codes of a

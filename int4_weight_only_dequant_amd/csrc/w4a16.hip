@@ -829,11 +829,13 @@ static w4_status setup_persistent(w4_model *m) {
     std::string why;
     int slots_unused = 0;
     // attention: a work-group per (head, chunk of kPkWaves x att_pps pages), wave
-    // v of it taking att_pps pages; at least 2 pages per wave, and enough
-    // that every (head, chunk) unit has a work-group of its own
-    pk.att_pps = std::max(2, (c.max_pages * c.n_q_heads + kPkWaves * P - 1) / (kPkWaves * P));
+    // v of it taking att_pps pages; at least 2 pages per wave, enough that
+    // every (head, chunk) unit has a work-group of its own, and at most 64
+    // chunks per head (the O staging merges them a chunk per lane)
+    pk.att_pps = std::max({2, (c.max_pages * c.n_q_heads + kPkWaves * P - 1) / (kPkWaves * P),
+                           (c.max_pages + kPkWaves * 64 - 1) / (kPkWaves * 64)});
     pk.att_smax = (c.max_pages + kPkWaves * pk.att_pps - 1) / (kPkWaves * pk.att_pps);
-    W4_CHECK(c.n_q_heads * pk.att_smax <= P, W4_EINVAL, "too many attention chunks for the grid");
+    W4_CHECK(c.n_q_heads * pk.att_smax <= P && pk.att_smax <= 64, W4_EINVAL, "too many attention chunks for the grid");
     // two work-groups per CU: the first-dispatched half of the grid gets the
     // larger share of every phase (measured: it gets through a phase faster)
     for (int k = 0; k < 4; ++k) {
