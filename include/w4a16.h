@@ -253,7 +253,10 @@ w4_status w4a16_gemm(const uint8_t *packed_q, const uint16_t *packed_s,
  *                 sharing it must be ordered on one stream
  * head_dim must be 128; 1 <= n_kvh <= 256; n_qh a multiple of n_kvh with
  * n_qh / n_kvh in {1, 2, 4, 7, 8}; 1 <= ctx_len <= 16 * n_pages_max.
- * Otherwise W4_EINVAL. */
+ * Otherwise W4_EINVAL.  Arithmetic: q.K on the matrix cores (fp16 operands,
+ * fp32 sums), softmax in fp32 (base 2), the weights entering the weighted sum
+ * of V as an fp16 pair hi + lo (about 22 bits of the fp32 weight), fp32 sums,
+ * fp16 output; splits merged in a fixed order (bitwise repeatable). */
 size_t w4_attn_ws_bytes(int32_t n_qh, int32_t n_kvh, int32_t n_pages_max);
 w4_status paged_attn_decode(const uint16_t *q, const uint16_t *k_pool,
                             const uint16_t *v_pool, const int32_t *page_table,
