@@ -52,7 +52,11 @@ struct AttnProblem {
 #ifndef W4_ATTN_MIN_PPS
 #define W4_ATTN_MIN_PPS 4
 #endif
-constexpr int kAttnWaves = kThreads / 64;
+#ifndef W4_ATTN_WAVES
+#define W4_ATTN_WAVES 4
+#endif
+constexpr int kAttnWaves = W4_ATTN_WAVES;      // waves per work-group
+constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kAttnTargetSplits = W4_ATTN_TARGET_SPLITS;
 constexpr int kAttnMinPps = W4_ATTN_MIN_PPS;
 static_assert(kAttnTargetSplits >= 1 && kAttnTargetSplits <= 256 && kAttnMinPps >= 1, "attention split bounds");
@@ -136,7 +140,7 @@ __device__ __forceinline__ void attn_load_batch(const AttnProblem &a, int j, int
 // merged through LDS in wave order, the work-group publishes its partial, and
 // the last work-group of the kv head merges all splits in split order.
 template <int G>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
+__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnProblem a) {
     static_assert(G >= 1 && G <= 8, "query heads per kv head");
     __shared__ __attribute__((aligned(16))) unsigned char s_slot[kAttnWaves][kAttnSlot];
     __shared__ int s_last;
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
     __syncthreads();
     // merge the waves in wave order; thread -> (head, dims 2 d2, 2 d2 + 1)
     const size_t pbase = (static_cast<size_t>(j) * a.n_split + sp) * G;
-    for (int idx = t; idx < G * 64; idx += kThreads) {
+    for (int idx = t; idx < G * 64; idx += kAttnThreads) {
         const int h = idx >> 6, d2 = idx & 63;
         float M = -INFINITY;
 #pragma unroll
@@ -317,14 +321,14 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnProblem a) {
 #pragma unroll
         for (int u = 0; u < kAttnMergeRound; ++u) r[u] = base[min(s0 + u, ns - 1) * stride];
     };
-    // the first 2 x 256 pairs go out first, then the first round of partials,
+    // the first two pairs per thread go out first, then the first round of partials,
     // so the LDS stores of the pairs (and the barrier) wait for the pairs only
-    const int ia = t, ib = kThreads + t;
+    const int ia = t, ib = kAttnThreads + t;
     const float2 va = mlp[min(ia, n_ml - 1)], vb = mlp[min(ib, n_ml - 1)];
     if (merger) load_round(ra, 0);
     if (ia < n_ml) { sml[2 * ia] = va.x; sml[2 * ia + 1] = va.y; }
     if (ib < n_ml) { sml[2 * ib] = vb.x; sml[2 * ib + 1] = vb.y; }
-    for (int i = 2 * kThreads + t; i < n_ml; i += kThreads) {   // more than 512 pairs
+    for (int i = 2 * kAttnThreads + t; i < n_ml; i += kAttnThreads) {   // more pairs than 2 per thread
         const float2 v = mlp[i];
         sml[2 * i] = v.x;
         sml[2 * i + 1] = v.y;

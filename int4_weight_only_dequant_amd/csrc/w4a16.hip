@@ -80,7 +80,7 @@ static hipError_t launch_w4(const W4Problem &p, const Epi &epi, hipStream_t s) {
 }
 
 static hipError_t launch_attn(int G, const AttnProblem &a, hipStream_t s) {
-    const dim3 grid(a.n_kvh * a.n_split), block(kThreads);
+    const dim3 grid(a.n_kvh * a.n_split), block(kAttnThreads);
     switch (G) {
         case 1: hipLaunchKernelGGL(attn_decode_kernel<1>, grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL(attn_decode_kernel<2>, grid, block, 0, s, a); break;
