@@ -22,8 +22,19 @@ Parity status of each function (what pins it):
 * ``rmsnorm``, ``rope``, ``silu``, ``swiglu``: closed forms and invariants — pinned;
 * ``paged_attention``, ``causal_attention``: one-token, two-token closed form,
   uniform-key mean, GQA mapping, page-shuffle invariance — pinned;
-* ``decode_step`` / ``forward_teacher_forced``: zero-weight special case against a
+* ``mlp``: identity and scaled-identity projections with a closed-form result —
+  pinned;
+* ``layer_step`` / ``decode_step`` / ``forward_teacher_forced``: a hand-built
+  one-layer model whose every intermediate has a closed form (distinct ln1, ln2
+  and final-norm weights, bias before RoPE at two positions, the QKV split
+  order, the MLP fed the second norm, both residual adds), planted wiring
+  mistakes that must fail it (``tests/test_oracle_layer_pins.py``,
+  ``tests/test_oracle_mutants.py``), the zero-weight special case against a
   single matmul, and sequential == batched on a tiny model — pinned;
+* ``act_int8`` and the ``act="int8"`` step mode: equal to ``quantize_act_int8``
+  dequantised, the layer's four quantised GEMV inputs checked against
+  ``gemv_w4a8`` with planted mistakes, sequential == batched
+  (``tests/test_oracle_int8_mode.py``) — pinned;
 * logits of the full 28-layer random model: parity unpinned beyond the
   component pins above (no external value exists for a random-init model).
 """
