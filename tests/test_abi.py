@@ -27,6 +27,22 @@ def test_every_declared_symbol_is_exported():
     assert not missing, missing
 
 
+def test_no_undefined_library_symbols():
+    """Every symbol of the library's own namespace is defined in it (a kernel
+    launched from host code whose launch stub was not emitted would otherwise
+    surface only when the library is loaded)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        import pytest
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", L.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    ours = [l.split()[-1] for l in out.splitlines() if "2w4" in l or "w4a16" in l or "w4_" in l]
+    assert not ours, ours
+
+
 def test_host_side_argument_errors():
     lib = w4.lib()
     buf = np.zeros(1 << 16, np.uint8)
