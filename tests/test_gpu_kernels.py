@@ -317,12 +317,24 @@ def test_attn_shuffled_equals_contiguous_bitwise():
 
 
 def test_attn_gqa_and_scale_variants():
-    for n_qh, n_kvh in [(28, 4), (8, 4), (16, 4), (8, 1), (32, 4)]:
+    for n_qh, n_kvh in [(28, 4), (8, 4), (16, 4), (8, 1), (32, 4), (4, 4), (8, 8)]:
         say(f"case: attention GQA {n_qh}/{n_kvh}")
         q, kp, vp, table = synth.attn_case(77, n_qh=n_qh, n_kvh=n_kvh, n_pages=6, cfg=100)
         o = _gpu_attn(q, kp, vp, table, 77, scale=0.05)
         ref = oracle.paged_attention(q, kp, vp, table, 77, 0.05)
         assert_attn(o, ref, f"gqa {n_qh}/{n_kvh}")
+
+
+@pytest.mark.parametrize("scale", [1.0, 4.0])
+def test_attn_peaked_softmax(scale):
+    """Scores spread over tens of units (base-2 exponents past -100): most
+    weights underflow, one or a few tokens carry the output; the weights' fp16
+    hi + lo pair and the split merge must still match the oracle."""
+    say(f"case: attention ctx 1000, scale {scale}")
+    q, kp, vp, table = synth.attn_case(1000, n_pages=70, cfg=111)
+    o = _gpu_attn(q, kp, vp, table, 1000, scale=scale, n_pages_max=70)
+    ref = oracle.paged_attention(q, kp, vp, table, 1000, scale)
+    say(f"  abs err {assert_attn(o, ref, f'scale={scale}'):.3e}")
 
 
 def test_attn_repeat_bit_identical():
