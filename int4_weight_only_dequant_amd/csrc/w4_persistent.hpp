@@ -818,7 +818,11 @@ __device__ __forceinline__ void stage_quant_a8(uint16_t *lds, int ng) {
 // 8 x the group's code sum, times the activation and weight scales in fp64.
 __device__ __forceinline__ void w4_tiles_a8(Ring &r, const u32x4 *wq, const uint16_t *ws, int ng, Range rg,
                                             bool whole, int rb0, const uint16_t *lds, double *red) {
-    const int wave = wave_id(), lane = lane_id();
+    // lane index and nibble mask produced here behind empty asm rather than
+    // as plain expressions the compiler may hoist out of the phase loop: with
+    // the plain forms this kernel spilled 40 VGPRs (8 of them the weight ring)
+    const int wave = wave_id(), lane = opaque_tid() & 63;
+    const uint32_t m4 = vreg_const(0x0F0F0F0Fu);
     const int n = rg.e - rg.b > wave ? (rg.e - rg.b - wave + kPkWaves - 1) / kPkWaves : 0;
     const unsigned char *cb = reinterpret_cast<const unsigned char *>(lds);
     int cur = -1;
@@ -846,9 +850,9 @@ __device__ __forceinline__ void w4_tiles_a8(Ring &r, const u32x4 *wq, const uint
                     const uint32_t xl[4] = {xa.x, xa.z, xb.x, xb.z}, xh[4] = {xa.y, xa.w, xb.y, xb.w};
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        dot = __builtin_amdgcn_sdot4(static_cast<int>(wv[q] & 0x0F0F0F0Fu), static_cast<int>(xl[q]), dot,
+                        dot = __builtin_amdgcn_sdot4(static_cast<int>(wv[q] & m4), static_cast<int>(xl[q]), dot,
                                                      false);
-                        dot = __builtin_amdgcn_sdot4(static_cast<int>((wv[q] >> 4) & 0x0F0F0F0Fu),
+                        dot = __builtin_amdgcn_sdot4(static_cast<int>((wv[q] >> 4) & m4),
                                                      static_cast<int>(xh[q]), dot, false);
                     }
                 }
